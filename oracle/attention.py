@@ -1,0 +1,98 @@
+"""Dense fp64 masked softmax attention (oracle; test-only).
+
+Splash and flash attention compute the same masked softmax attention and
+differ only in which work they skip (splash page, "What is splash attention
+and how is it different from flash attention?").  So this oracle is the
+plain definition, in float64, with no tiling and no online softmax:
+
+  s_ij  = scale * <q_i, k_j>           scale defaults to head_dim ** -0.5
+                                       (EasyDeL BlockSparseAttn.forward_native)
+  s_ij <- c * tanh(s_ij / c)           only if a logits soft cap c is given;
+                                       the pages name the parameter but not the
+                                       formula -- the usual tanh cap on the
+                                       scaled logits, before masking, is taken
+  over allowed j:  M_i = max s_ij,  lse_i = M_i + ln sum_j exp(s_ij - M_i),
+                   o_i = sum_j exp(s_ij - lse_i) v_j
+  no allowed j:    o_i = 0, lse_i = -inf
+
+lse is the natural-log residual the flash kernel keeps for its backward pass
+(pallas-flash-attention-tpu page, "What does the TPU flash attention kernel
+save for the backward pass?": the running max and the running sum; here
+combined as max + log(sum)).
+
+GQA/MQA: query head h reads key/value head h // (Hq // Hkv).
+Mask heads: Hm == 1 is shared by every query head; Hm == Hq is per head.
+"""
+import numpy as np
+
+
+def attention_rows(q, k, v, allowed, scale=None, soft_cap=None):
+    """One (batch, head): q [n, D], k [Skv, D], v [Skv, Dv], allowed [n, Skv] bool.
+
+    Returns (o [n, Dv] float64, lse [n] float64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    s = scale * (q @ k.T)
+    if soft_cap is not None:
+        s = soft_cap * np.tanh(s / soft_cap)
+    s = np.where(allowed, s, -np.inf)
+    m = s.max(axis=1)
+    has = np.isfinite(m)
+    m_safe = np.where(has, m, 0.0)
+    e = np.exp(s - m_safe[:, None])            # exp(-inf) = 0 at masked entries
+    total = e.sum(axis=1)
+    lse = np.where(has, m_safe + np.log(np.where(has, total, 1.0)), -np.inf)
+    w = np.where(has[:, None], e / np.where(has, total, 1.0)[:, None], 0.0)
+    o = w @ v
+    return o, lse
+
+
+def attention(q, k, v, mask_rows, scale=None, soft_cap=None, row_chunk=512):
+    """Full attention.
+
+    q [B, Hq, Sq, D], k [B, Hkv, Skv, D], v [B, Hkv, Skv, Dv] (any float type,
+    upcast to float64); mask_rows(head, rows) -> bool [len(rows), Skv] gives
+    the allowed keys for the query positions `rows` of mask head `head`
+    (callers pass head = 0 for a shared mask).
+
+    Returns (o [B, Hq, Sq, Dv], lse [B, Hq, Sq]) in float64.  Rows are done
+    in chunks so no Sq x Skv float64 slab is held whole.
+    """
+    b_, hq, sq, _ = q.shape
+    hkv = k.shape[1]
+    if hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = hq // hkv
+    o = np.zeros((b_, hq, sq, v.shape[-1]), dtype=np.float64)
+    lse = np.zeros((b_, hq, sq), dtype=np.float64)
+    for b in range(b_):
+        for h in range(hq):
+            kk = np.asarray(k[b, h // group], dtype=np.float64)
+            vv = np.asarray(v[b, h // group], dtype=np.float64)
+            for i0 in range(0, sq, row_chunk):
+                rows = np.arange(i0, min(sq, i0 + row_chunk))
+                ob, lb = attention_rows(q[b, h, rows], kk, vv, mask_rows(h, rows), scale, soft_cap)
+                o[b, h, rows] = ob
+                lse[b, h, rows] = lb
+    return o, lse
+
+
+def attention_sampled(q, k, v, mask_rows, samples, scale=None, soft_cap=None):
+    """Selected output rows only: samples = iterable of (b, h, i).
+
+    Returns (o [n, Dv], lse [n]) in the order given.  Used at full workload
+    sizes, where the whole output is too costly to compute in float64.
+    """
+    hq, hkv = q.shape[1], k.shape[1]
+    group = hq // hkv
+    outs, lses = [], []
+    for b, h, i in samples:
+        ob, lb = attention_rows(q[b, h, [i]], k[b, h // group], v[b, h // group],
+                                mask_rows(h, np.array([i])), scale, soft_cap)
+        outs.append(ob[0])
+        lses.append(lb[0])
+    return np.stack(outs), np.array(lses)

@@ -1,0 +1,194 @@
+"""Pins for the oracle attention (CPU only).
+
+Closed forms, a library routine (torch scaled_dot_product_attention in
+float64), invariants and an independent tiled online-softmax derivation --
+each chosen so that a dropped term, a wrong sign or index, or a transposed
+operand in the oracle fails at least one check.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from oracle import masks as omasks
+
+
+def _rows_fn(mask):
+    return lambda h, rows: mask[0 if mask.shape[0] == 1 else h][rows]
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+@pytest.mark.parametrize("kind,kw", [
+    ("causal", {}), ("local", {"left": 5, "right": 2}), ("local", {"left": 0, "right": 0}),
+    ("chunked", {"chunk": 7}),
+])
+def test_zero_query_gives_mean_of_allowed_values(kind, kw):
+    """q = 0 makes every allowed score equal, so o_i is the plain mean of the
+    allowed v_j and lse_i = ln(#allowed) -- counted here from the interval form
+    of each mask, not from the oracle's predicate."""
+    rng = np.random.default_rng(0)
+    sq = skv = 23
+    q = np.zeros((1, 1, sq, 8))
+    k, v = _rand(rng, 1, 1, skv, 8), _rand(rng, 1, 1, skv, 5)
+    m = omasks.materialize(kind, sq, skv, **kw)
+    o, lse = oatt.attention(q, k, v, _rows_fn(m))
+    for i in range(sq):
+        if kind == "causal":
+            lo, hi = 0, i
+        elif kind == "local":
+            lo, hi = max(0, i - kw["left"]), min(skv - 1, i + kw["right"])
+        else:
+            lo, hi = (i // kw["chunk"]) * kw["chunk"], i
+        n = hi - lo + 1
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, lo:hi + 1].mean(axis=0), rtol=0, atol=1e-13)
+        assert abs(lse[0, 0, i] - math.log(n)) < 1e-13
+
+
+def test_causal_first_row_is_first_value():
+    rng = np.random.default_rng(1)
+    q, k, v = _rand(rng, 1, 2, 9, 4), _rand(rng, 1, 2, 9, 4), _rand(rng, 1, 2, 9, 3)
+    m = omasks.materialize("causal", 9, 9)
+    o, lse = oatt.attention(q, k, v, _rows_fn(m))
+    for h in range(2):
+        np.testing.assert_array_equal(o[0, h, 0], v[0, h, 0])
+        assert abs(lse[0, h, 0] - 0.5 * float(q[0, h, 0] @ k[0, h, 0])) < 1e-14
+
+
+def test_unmasked_equals_torch_sdpa_float64():
+    rng = np.random.default_rng(2)
+    q, k, v = _rand(rng, 2, 3, 17, 16), _rand(rng, 2, 3, 29, 16), _rand(rng, 2, 3, 29, 12)
+    full = np.ones((1, 17, 29), dtype=bool)
+    o, lse = oatt.attention(q, k, v, _rows_fn(full), row_chunk=5)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    # lse against torch.logsumexp of the scaled scores
+    s = torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2) / 4.0
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_causal_equals_torch_sdpa_is_causal():
+    rng = np.random.default_rng(3)
+    q, k, v = _rand(rng, 1, 2, 33, 8), _rand(rng, 1, 2, 33, 8), _rand(rng, 1, 2, 33, 8)
+    m = omasks.materialize("causal", 33, 33)
+    o, _ = oatt.attention(q, k, v, _rows_fn(m), scale=0.3)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True, scale=0.3).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_dense_mask_equals_torch_sdpa_bool_mask():
+    rng = np.random.default_rng(4)
+    q, k, v = _rand(rng, 1, 2, 16, 8), _rand(rng, 1, 2, 24, 8), _rand(rng, 1, 2, 24, 8)
+    m = rng.random((2, 16, 24)) < 0.4
+    m[:, :, 0] = True                          # no empty rows for SDPA
+    o, _ = oatt.attention(q, k, v, _rows_fn(m))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(m)[None]).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    rng = np.random.default_rng(5)
+    q, k, v = _rand(rng, 2, 6, 10, 8), _rand(rng, 2, 2, 10, 8), _rand(rng, 2, 2, 10, 8)
+    m = omasks.materialize("causal", 10, 10)
+    o, lse = oatt.attention(q, k, v, _rows_fn(m))
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)   # head h -> kv head h // 3
+    o2, lse2 = oatt.attention(q, kr, vr, _rows_fn(m))
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    # and head 4 really reads kv head 1 (a swapped mapping would differ)
+    o3, _ = oatt.attention(q[:, 4:5], k[:, 1:2], v[:, 1:2], _rows_fn(m))
+    np.testing.assert_array_equal(o[:, 4:5], o3)
+
+
+def test_soft_cap_closed_form():
+    """Scores built as c*atanh(+-1/2)/scale make the capped logits exactly
+    +-c/2, so the weights are 1/(1+e^-c) and 1/(1+e^c) and lse has a closed
+    form -- with no tanh in the expectation."""
+    c, scale = 3.0, 0.25
+    x = c * math.atanh(0.5)
+    q = np.array([[[[x / scale, 0.0]]]])           # one query
+    k = np.array([[[[1.0, 0.0], [-1.0, 0.0]]]])      # scores +x, -x
+    v = np.array([[[[1.0, 2.0], [5.0, -1.0]]]])
+    o, lse = oatt.attention(q, k, v, lambda h, r: np.ones((1, 2), dtype=bool), scale=scale, soft_cap=c)
+    w0 = 1.0 / (1.0 + math.exp(-c))
+    np.testing.assert_allclose(o[0, 0, 0], w0 * v[0, 0, 0] + (1 - w0) * v[0, 0, 1], rtol=0, atol=1e-14)
+    assert abs(lse[0, 0, 0] - (c / 2 + math.log(1 + math.exp(-c)))) < 1e-14
+
+
+def test_soft_cap_large_equals_uncapped():
+    rng = np.random.default_rng(6)
+    q, k, v = _rand(rng, 1, 1, 12, 8), _rand(rng, 1, 1, 12, 8), _rand(rng, 1, 1, 12, 8)
+    m = omasks.materialize("causal", 12, 12)
+    o1, l1 = oatt.attention(q, k, v, _rows_fn(m), soft_cap=1e7)
+    o2, l2 = oatt.attention(q, k, v, _rows_fn(m))
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-11)
+
+
+def test_fully_masked_row_is_zero_with_neg_inf_lse():
+    rng = np.random.default_rng(7)
+    q, k, v = _rand(rng, 1, 1, 4, 4), _rand(rng, 1, 1, 6, 4), _rand(rng, 1, 1, 6, 4)
+    m = np.ones((1, 4, 6), dtype=bool)
+    m[0, 2] = False
+    o, lse = oatt.attention(q, k, v, _rows_fn(m))
+    assert np.all(o[0, 0, 2] == 0.0) and lse[0, 0, 2] == -np.inf
+    assert np.all(np.isfinite(lse[0, 0, [0, 1, 3]]))
+
+
+def test_default_scale_is_inverse_sqrt_head_dim():
+    rng = np.random.default_rng(8)
+    q, k, v = _rand(rng, 1, 1, 5, 16), _rand(rng, 1, 1, 5, 16), _rand(rng, 1, 1, 5, 16)
+    full = np.ones((1, 5, 5), dtype=bool)
+    a = oatt.attention(q, k, v, _rows_fn(full))
+    b = oatt.attention(q, k, v, _rows_fn(full), scale=0.25)
+    np.testing.assert_array_equal(a[0], b[0])
+
+
+def test_tiled_online_softmax_rederivation():
+    """Flash-style running max / normaliser over key tiles (the rescaling the
+    splash page describes for combining steps) must reproduce the dense oracle."""
+    rng = np.random.default_rng(9)
+    sq, skv, d = 19, 53, 8
+    q, k, v = _rand(rng, sq, d), _rand(rng, skv, d), _rand(rng, skv, 6)
+    allowed = omasks.allowed_block("local", np.arange(sq), np.arange(skv), left=9, right=20)
+    scale, cap = 0.4, 2.5
+    m = np.full(sq, -np.inf)
+    l = np.zeros(sq)
+    acc = np.zeros((sq, 6))
+    for j0 in range(0, skv, 8):
+        sl = slice(j0, min(skv, j0 + 8))
+        s = cap * np.tanh(scale * (q @ k[sl].T) / cap)
+        s = np.where(allowed[:, sl], s, -np.inf)
+        m_new = np.maximum(m, s.max(axis=1))
+        base = np.where(np.isfinite(m_new), m_new, 0.0)
+        alpha = np.exp(m - base)
+        p = np.exp(s - base[:, None])
+        l = alpha * l + p.sum(axis=1)
+        acc = alpha[:, None] * acc + p @ v[sl]
+        m = m_new
+    o_ref = acc / l[:, None]
+    lse_ref = m + np.log(l)
+    o, lse = oatt.attention_rows(q, k, v, allowed, scale=scale, soft_cap=cap)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def test_sampled_rows_equal_full():
+    rng = np.random.default_rng(10)
+    q, k, v = _rand(rng, 2, 4, 16, 8), _rand(rng, 2, 2, 16, 8), _rand(rng, 2, 2, 16, 8)
+    m = omasks.materialize("chunked", 16, 16, chunk=5)
+    o, lse = oatt.attention(q, k, v, _rows_fn(m), soft_cap=1.5)
+    samples = [(1, 3, 15), (0, 0, 0), (1, 2, 7)]
+    os_, ls_ = oatt.attention_sampled(q, k, v, _rows_fn(m), samples, soft_cap=1.5)
+    for n, (b, h, i) in enumerate(samples):
+        # one row vs a block of rows: only the BLAS summation order differs
+        np.testing.assert_allclose(os_[n], o[b, h, i], rtol=0, atol=1e-14)
+        assert abs(ls_[n] - lse[b, h, i]) < 1e-14
