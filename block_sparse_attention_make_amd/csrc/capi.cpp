@@ -1,0 +1,211 @@
+// C-ABI layer: errors, device copies of a MaskInfo, validation and launch of
+// the forward kernel.  Declarations and contracts are in include/splash.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "mask_info.h"
+#include "splash_kernel.h"
+
+namespace splash {
+
+namespace {
+thread_local std::string g_last_error;
+
+size_t array_bytes(const HostArray &a) { return a.bytes.size(); }
+}  // namespace
+
+splash_status fail(splash_status st, const std::string &msg) {
+  g_last_error = msg;
+  return st;
+}
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+splash_status hip_fail(hipError_t e, const char *what) {
+  return fail(e == hipErrorOutOfMemory ? SPLASH_ENOMEM : SPLASH_EHIP,
+              std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void free_copy(DeviceCopy &dc) {
+  if (dc.device < 0) return;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(dc.device);
+  for (void *&ptr : dc.ptr) {
+    if (ptr) (void)hipFree(ptr);
+    ptr = nullptr;
+  }
+  if (dc.row_order) (void)hipFree(dc.row_order);
+  dc.row_order = nullptr;
+  dc.device = -1;
+  if (prev >= 0) (void)hipSetDevice(prev);
+}
+
+// Device copy for the current device, uploading it if needed.
+splash_status ensure_device_copy(splash_mask_info *mi, DeviceCopy **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SPLASH_EUNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(mi->mu);
+  DeviceCopy &dc = mi->dev[dev];
+  if (dc.device == dev) {
+    *out = &dc;
+    return SPLASH_OK;
+  }
+  DeviceCopy fresh;
+  fresh.device = dev;
+  for (int i = 0; i < kNumArrays; ++i) {
+    const HostArray &a = mi->arr[i];
+    if (!a.present || a.bytes.empty()) continue;
+    e = hipMalloc(&fresh.ptr[i], array_bytes(a));
+    if (e == hipSuccess) e = hipMemcpy(fresh.ptr[i], a.bytes.data(), array_bytes(a), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      free_copy(fresh);
+      return hip_fail(e, "uploading MaskInfo");
+    }
+  }
+  if (!mi->row_order.empty()) {
+    const size_t nb = mi->row_order.size() * sizeof(int32_t);
+    e = hipMalloc(reinterpret_cast<void **>(&fresh.row_order), nb);
+    if (e == hipSuccess) e = hipMemcpy(fresh.row_order, mi->row_order.data(), nb, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      free_copy(fresh);
+      return hip_fail(e, "uploading MaskInfo row order");
+    }
+  }
+  dc = fresh;
+  *out = &dc;
+  return SPLASH_OK;
+}
+
+}  // namespace
+}  // namespace splash
+
+using namespace splash;
+
+extern "C" SPLASH_API const char *splash_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" SPLASH_API void splash_mask_info_destroy(splash_mask_info *mi) {
+  if (!mi) return;
+  for (DeviceCopy &dc : mi->dev) free_copy(dc);
+  delete mi;
+}
+
+extern "C" SPLASH_API splash_status splash_mask_info_upload(splash_mask_info *mi) {
+  clear_error();
+  if (!mi) return fail(SPLASH_EINVAL, "MaskInfo is NULL");
+  DeviceCopy *dc = nullptr;
+  return ensure_device_copy(mi, &dc);
+}
+
+extern "C" SPLASH_API splash_status splash_mask_info_read_device(const splash_mask_info *mi,
+                                                                 int32_t which, void *dst,
+                                                                 size_t nbytes) {
+  clear_error();
+  if (!mi || !dst) return fail(SPLASH_EINVAL, "NULL argument");
+  if (which < 0 || which >= kNumArrays) return fail(SPLASH_EINVAL, "unknown MaskInfo array id");
+  const HostArray &a = mi->arr[which];
+  if (!a.present) return fail(SPLASH_EINVAL, "array is None");
+  if (nbytes != a.bytes.size()) return fail(SPLASH_EINVAL, "nbytes does not match the array size");
+  if (nbytes == 0) return SPLASH_OK;
+  bool any_copy = false;
+  for (const DeviceCopy &dc : mi->dev) any_copy = any_copy || dc.device >= 0;
+  if (!any_copy) return fail(SPLASH_EINVAL, "MaskInfo has not been uploaded to any device");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices || mi->dev[dev].device != dev || !mi->dev[dev].ptr[which])
+    return fail(SPLASH_EINVAL, "MaskInfo is not uploaded to the current device");
+  e = hipMemcpy(dst, mi->dev[dev].ptr[which], nbytes, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the device MaskInfo");
+  return SPLASH_OK;
+}
+
+extern "C" SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void *q, const void *k,
+                                               const void *v, void *out, float *lse, int64_t B,
+                                               int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                                               int64_t D, int64_t Dv, int32_t dtype,
+                                               float softmax_scale, float logits_soft_cap,
+                                               void *hip_stream) {
+  clear_error();
+  // ---- validation: nothing below launches or allocates until all passes ----
+  if (!mi) return fail(SPLASH_EINVAL, "MaskInfo is NULL");
+  if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || D <= 0 || Dv <= 0)
+    return fail(SPLASH_EINVAL, "negative size or non-positive head dim");
+  if (dtype != SPLASH_BF16 && dtype != SPLASH_F32) return fail(SPLASH_EINVAL, "unknown dtype");
+  if (Sq != mi->q_len || Skv != mi->kv_len)
+    return fail(SPLASH_EINVAL, "Sq / Skv do not match the MaskInfo's q_len / kv_len");
+  if (Hkv == 0 && Hq > 0) return fail(SPLASH_EINVAL, "Hkv must be positive");
+  if (Hkv > 0 && Hq % Hkv != 0) return fail(SPLASH_EINVAL, "Hq must be a multiple of Hkv");
+  if (mi->num_heads != 1 && mi->num_heads != Hq)
+    return fail(SPLASH_EINVAL, "MaskInfo head count must be 1 or Hq");
+  if (!(std::isnan(softmax_scale) || (std::isfinite(softmax_scale) && softmax_scale > 0.f)))
+    return fail(SPLASH_EINVAL, "softmax_scale must be NaN (default) or finite and > 0");
+  if (mi->block_q != 128 || mi->block_kv != 128)
+    return fail(SPLASH_EUNSUPPORTED, "the forward kernel runs 128 x 128 MaskInfo blocks");
+  if (D != Dv || (D != 64 && D != 128))
+    return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
+  if (B == 0 || Hq == 0 || Sq == 0) return SPLASH_OK;
+  if (!q || !out || (Skv > 0 && (!k || !v)))
+    return fail(SPLASH_EINVAL, "NULL tensor pointer");
+  const int64_t n_wg = B * Hq * mi->nq;
+  if (n_wg > 0x7fffffffLL || B * Hq > 0x7fffffffLL)
+    return fail(SPLASH_EUNSUPPORTED, "grid too large");
+  const size_t elt = dtype == SPLASH_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+       reinterpret_cast<uintptr_t>(out)) % 16 != 0)
+    return fail(SPLASH_EINVAL, "q, k, v and out must be 16-byte aligned");
+  (void)elt;
+
+  DeviceCopy *dc = nullptr;
+  splash_status st = ensure_device_copy(mi, &dc);
+  if (st != SPLASH_OK) return st;
+
+  FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Skv = Skv;
+  p.D = static_cast<int32_t>(D);
+  p.group = static_cast<int32_t>(Hq / Hkv);
+  p.nq = static_cast<int32_t>(mi->nq);
+  p.width = static_cast<int32_t>(mi->width);
+  p.hm = mi->num_heads;
+  p.bm = dc->ptr[SPLASH_MI_BLOCK_MASK];
+  p.dn = dc->ptr[SPLASH_MI_DATA_NEXT];
+  p.mn = dc->ptr[SPLASH_MI_MASK_NEXT];
+  p.pmb = static_cast<const uint8_t *>(dc->ptr[SPLASH_MI_PARTIAL_BLOCKS]);
+  p.q_seq = static_cast<const int32_t *>(dc->ptr[SPLASH_MI_Q_SEQUENCE]);
+  p.row_order = dc->row_order;
+  p.bm_bytes = mi->arr[SPLASH_MI_BLOCK_MASK].elem_bits / 8;
+  p.dn_bytes = mi->arr[SPLASH_MI_DATA_NEXT].elem_bits / 8;
+  p.mn_bytes = mi->arr[SPLASH_MI_MASK_NEXT].present ? mi->arr[SPLASH_MI_MASK_NEXT].elem_bits / 8 : 4;
+  p.mask_kind = mi->kind;
+  p.left = mi->left;
+  p.right = mi->right;
+  p.chunk = mi->chunk;
+  p.dense = mi->kind == SPLASH_MASK_DENSE;
+  const float scale = std::isnan(softmax_scale) ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D)))
+                                                : softmax_scale;
+  const bool cap = std::isfinite(logits_soft_cap) && logits_soft_cap > 0.f;
+  p.cap = cap;
+  const double log2e = 1.4426950408889634;
+  p.c2 = cap ? static_cast<float>(static_cast<double>(scale) / logits_soft_cap)
+             : static_cast<float>(scale * log2e);
+  p.cap_out = cap ? static_cast<float>(logits_soft_cap * log2e) : 0.f;
+
+  hipError_t e = launch_fwd(p, dtype, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return SPLASH_OK;
+}

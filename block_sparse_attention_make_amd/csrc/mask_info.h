@@ -1,0 +1,59 @@
+// Internal layout of a compiled MaskInfo (host side plus cached device
+// copies).  Shared by the host mask compiler and the C-ABI / launch code.
+#pragma once
+
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "splash.h"
+
+namespace splash {
+
+struct HostArray {
+  bool present = false;     // false <=> None
+  int32_t elem_bits = 32;   // 8 / 16 / 32
+  bool is_signed = true;
+  int32_t ndim = 0;
+  int64_t shape[3] = {0, 0, 0};
+  std::vector<uint8_t> bytes;
+  int64_t numel() const {
+    int64_t n = 1;
+    for (int i = 0; i < ndim; ++i) n *= shape[i];
+    return ndim ? n : 0;
+  }
+};
+
+constexpr int kNumArrays = 5;
+constexpr int kMaxDevices = 64;
+
+struct DeviceCopy {
+  int device = -1;
+  void *ptr[kNumArrays] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  int32_t *row_order = nullptr;
+};
+
+}  // namespace splash
+
+struct splash_mask_info {
+  int32_t kind = 0;
+  int32_t num_heads = 1;  // Hm
+  int64_t q_len = 0, kv_len = 0;
+  int64_t left = -1, right = -1, chunk = 0;
+  int32_t block_q = 0, block_kv = 0;
+  int64_t nq = 0, nk = 0, width = 0;
+  uint32_t flags = 0;
+  splash::HostArray arr[splash::kNumArrays];
+  // Block rows ordered by descending non-empty block count (summed over mask
+  // heads), ties by row index: the launch hands the longest rows out first.
+  std::vector<int32_t> row_order;
+  std::mutex mu;
+  splash::DeviceCopy dev[splash::kMaxDevices];
+};
+
+namespace splash {
+// Thread-local error message helpers (capi.cpp).
+splash_status fail(splash_status st, const std::string &msg);
+void clear_error();
+}  // namespace splash

@@ -1,0 +1,34 @@
+// Launch parameters shared by the C-ABI layer and the forward kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace splash {
+
+struct FwdParams {
+  const void *q, *k, *v;
+  void *out;
+  float *lse;             // may be null
+  int64_t B, Hq, Hkv, Sq, Skv;
+  int32_t D;              // == Dv
+  int32_t group;          // Hq / Hkv
+  int32_t nq, width, hm;  // MaskInfo grid: block rows, grid width W, mask heads
+  const void *bm, *dn, *mn;           // device MaskInfo index arrays (downcast types)
+  const uint8_t *pmb;                 // device partial blocks (dense masks)
+  const int32_t *q_seq;               // device q_sequence (computable masks)
+  const int32_t *row_order;           // device launch order of block rows
+  int32_t bm_bytes, dn_bytes, mn_bytes;
+  int32_t mask_kind;                  // 0 causal, 1 local, 2 chunked causal, 3 dense
+  int64_t left, right, chunk;
+  float c2;       // no cap: softmax_scale * log2(e); cap: softmax_scale / cap
+  float cap_out;  // cap * log2(e)
+  int32_t cap;    // soft cap on
+  int32_t dense;  // dense mask
+};
+
+// dtype: 0 = bf16, 1 = f32.  D in {64, 128}.  Returns hipGetLastError().
+hipError_t launch_fwd(const FwdParams &p, int dtype, hipStream_t stream);
+
+}  // namespace splash

@@ -1,0 +1,224 @@
+"""Python binding of libsplash (ctypes).  Argument marshalling only: every
+step of the path -- mask compilation and the attention kernel -- runs in the
+native library.  torch is used for device memory and streams.
+
+The library must have been built (block_sparse_attention_make_amd.build);
+there is no fallback: a missing library raises.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libsplash.so")
+
+OK, EINVAL, ENOMEM, EHIP, EUNSUPPORTED = 0, 1, 2, 3, 4
+MASK_KINDS = {"causal": 0, "local": 1, "chunked": 2, "dense": 3}
+BF16, F32 = 0, 1
+BLOCK_MASK, DATA_NEXT, MASK_NEXT, PARTIAL_BLOCKS, Q_SEQUENCE = range(5)
+ARRAY_NAMES = ("block_mask", "data_next", "mask_next", "partial_mask_blocks", "q_sequence")
+FLAG_SHRINK, FLAG_DOWNCAST = 1, 2
+
+
+class SplashError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"splash status {status}: {msg}")
+        self.status = status
+
+
+class _MaskDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
+                ("left", ctypes.c_int64), ("right", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("dense", ctypes.c_void_p)]
+
+
+class _ArrayView(ctypes.Structure):
+    _fields_ = [("elem_bits", ctypes.c_int32), ("is_signed", ctypes.c_int32),
+                ("ndim", ctypes.c_int32), ("_pad", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 3), ("data", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path=None):
+    """Load libsplash.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m block_sparse_attention_make_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.splash_make_mask_info.argtypes = [ctypes.POINTER(_MaskDesc), i32, i32, ctypes.c_uint32, ctypes.POINTER(vp)]
+    lib.splash_make_mask_info.restype = ctypes.c_int
+    lib.splash_mask_info_view.argtypes = [vp, i32, ctypes.POINTER(_ArrayView)]
+    lib.splash_mask_info_view.restype = ctypes.c_int
+    lib.splash_mask_info_upload.argtypes = [vp]
+    lib.splash_mask_info_upload.restype = ctypes.c_int
+    lib.splash_mask_info_read_device.argtypes = [vp, i32, vp, ctypes.c_size_t]
+    lib.splash_mask_info_read_device.restype = ctypes.c_int
+    lib.splash_mask_info_destroy.argtypes = [vp]
+    lib.splash_mask_info_destroy.restype = None
+    lib.splash_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32,
+                               ctypes.c_float, ctypes.c_float, vp]
+    lib.splash_fwd.restype = ctypes.c_int
+    lib.splash_last_error.argtypes = []
+    lib.splash_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status):
+    if status != OK:
+        raise SplashError(status, lib.splash_last_error().decode())
+
+
+_NP_INT = {(8, 1): np.int8, (16, 1): np.int16, (32, 1): np.int32, (8, 0): np.uint8}
+
+
+class MaskInfo:
+    """A compiled mask owned by the native library."""
+
+    def __init__(self, handle, lib, kind, q_len, kv_len, block_q, block_kv, num_heads):
+        self._h = handle
+        self._lib = lib
+        self.kind, self.q_len, self.kv_len = kind, q_len, kv_len
+        self.block_q, self.block_kv, self.num_heads = block_q, block_kv, num_heads
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.splash_mask_info_destroy(h)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def _view(self, which):
+        v = _ArrayView()
+        _check(self._lib, self._lib.splash_mask_info_view(self._h, which, ctypes.byref(v)))
+        return v
+
+    def array(self, which):
+        """Host copy of one MaskInfo array as numpy, or None."""
+        v = self._view(which)
+        if not v.data:
+            return None
+        dt = _NP_INT[(v.elem_bits, v.is_signed)]
+        shape = tuple(v.shape[i] for i in range(v.ndim))
+        n = int(np.prod(shape)) if shape else 0
+        buf = (ctypes.c_char * (n * np.dtype(dt).itemsize)).from_address(v.data) if n else b""
+        return np.frombuffer(bytes(buf), dtype=dt).reshape(shape).copy()
+
+    def array_nbytes(self, which):
+        v = self._view(which)
+        if not v.data:
+            return 0
+        return int(np.prod([v.shape[i] for i in range(v.ndim)])) * v.elem_bits // 8
+
+    @property
+    def block_mask(self):
+        return self.array(BLOCK_MASK)
+
+    @property
+    def data_next(self):
+        return self.array(DATA_NEXT)
+
+    @property
+    def mask_next(self):
+        return self.array(MASK_NEXT)
+
+    @property
+    def partial_mask_blocks(self):
+        return self.array(PARTIAL_BLOCKS)
+
+    @property
+    def q_sequence(self):
+        return self.array(Q_SEQUENCE)
+
+    def upload(self):
+        _check(self._lib, self._lib.splash_mask_info_upload(self._h))
+
+    def read_device(self, which):
+        """The device copy (current device) of one array, copied back to host."""
+        host = self.array(which)
+        if host is None:
+            return None
+        out = np.empty_like(host)
+        _check(self._lib, self._lib.splash_mask_info_read_device(
+            self._h, which, out.ctypes.data_as(ctypes.c_void_p), out.nbytes))
+        return out
+
+
+def make_mask_info(kind, q_len, kv_len, left=None, right=None, chunk=None, dense=None,
+                   block_q=128, block_kv=128, shrink=True, downcast=True):
+    """Compile a mask.  kind: "causal" | "local" | "chunked" | "dense".
+    dense: host array [Hm, q_len, kv_len] (or [q_len, kv_len]), nonzero = allowed."""
+    lib = load_library()
+    if kind not in MASK_KINDS:
+        raise ValueError(f"unknown mask kind {kind!r}")
+    d = _MaskDesc()
+    d.kind = MASK_KINDS[kind]
+    d.num_heads = 1
+    d.q_len, d.kv_len = int(q_len), int(kv_len)
+    d.left = -1 if left is None else int(left)
+    d.right = -1 if right is None else int(right)
+    d.chunk = 0 if chunk is None else int(chunk)
+    keep = None
+    if kind == "dense":
+        arr = dense.detach().cpu().numpy() if hasattr(dense, "detach") else np.asarray(dense)
+        if arr.ndim == 2:
+            arr = arr[None]
+        keep = np.ascontiguousarray(arr.astype(np.uint8, copy=False))
+        if keep.shape[1:] != (q_len, kv_len):
+            raise ValueError("dense mask shape does not match (q_len, kv_len)")
+        d.num_heads = keep.shape[0]
+        d.dense = keep.ctypes.data
+    flags = (FLAG_SHRINK if shrink else 0) | (FLAG_DOWNCAST if downcast else 0)
+    h = ctypes.c_void_p()
+    _check(lib, lib.splash_make_mask_info(ctypes.byref(d), int(block_q), int(block_kv), flags, ctypes.byref(h)))
+    del keep
+    return MaskInfo(h.value, lib, kind, int(q_len), int(kv_len), int(block_q), int(block_kv), d.num_heads)
+
+
+def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
+               out=None, lse=None, return_lse=True, stream=None):
+    """Splash-attention forward on GPU torch tensors (contiguous BHSD).
+
+    Returns (out, lse); lse is float32 [B, Hq, Sq] or None if return_lse is False.
+    Launches asynchronously on `stream` (default: torch's current stream).
+    """
+    import torch
+    lib = load_library()
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-d tensor [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if k.shape[0] != B or v.shape[:3] != k.shape[:3] or k.shape[3] != D:
+        raise ValueError("k / v shapes do not match q")
+    if out is None:
+        out = torch.empty((B, Hq, Sq, Dv), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    scale = math.nan if softmax_scale is None else float(softmax_scale)
+    cap = 0.0 if logits_soft_cap is None else float(logits_soft_cap)
+    with torch.cuda.device(q.device):
+        st = lib.splash_fwd(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr() if lse is not None else None,
+                            B, Hq, Hkv, Sq, Skv, D, Dv, BF16 if q.dtype == torch.bfloat16 else F32,
+                            scale, cap, ctypes.c_void_p(stream.cuda_stream))
+    _check(lib, st)
+    return out, lse

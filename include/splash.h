@@ -1,0 +1,197 @@
+/*
+ * splash.h -- C ABI of the MI355X (gfx950) splash-attention forward library.
+ *
+ * Two operations, as the splash-attention explainer page
+ * (explainers.rudrite.com/splash-attention) describes them:
+ *
+ *  1. A mask compiler (FAQ "What is MaskInfo in splash attention?", "Does
+ *     splash attention make every sparse mask faster?", "What does grid
+ *     shrinking do in splash attention?"): cut a mask into grid-step blocks,
+ *     label each 0 / 1 / 2 (empty / partial / full), build data_next,
+ *     mask_next, the deduplicated partial_mask_blocks and q_sequence, shrink
+ *     the grid to the longest non-empty block row and downcast the integer
+ *     arrays.  A single computable mask (causal, local, chunked causal)
+ *     stores no mask data; the kernel recomputes it.
+ *
+ *  2. The forward kernel (FAQ "What is splash attention and how is it
+ *     different from flash attention?"): block-sparse online-softmax
+ *     attention whose loop over key/value blocks is read from the MaskInfo.
+ *     Label 0 runs nothing and fetches nothing, label 2 skips masking,
+ *     label 1 computes and masks.  It also returns the per-row
+ *     log-sum-exp residual (the running max and sum that the flash kernel
+ *     keeps for its backward pass, pallas-flash-attention-tpu page, FAQ
+ *     "What does the TPU flash attention kernel save for the backward
+ *     pass?"), and takes the softmax scale and optional logits soft cap of
+ *     the EasyDeL BlockSparseAttn.forward_native signature.
+ *
+ * Conventions
+ *  - Every entry point returns a splash_status; on failure a message is
+ *    available from splash_last_error() on the same thread.  No C++
+ *    exception crosses this boundary.
+ *  - Argument errors are reported before anything is launched or allocated.
+ *  - Tensors are contiguous row-major, BHSD: q [B, Hq, Sq, D],
+ *    k [B, Hkv, Skv, D], v [B, Hkv, Skv, Dv], out [B, Hq, Sq, Dv],
+ *    lse [B, Hq, Sq] float32.
+ *  - Query head h reads key/value head h / (Hq / Hkv)  (GQA / MQA).
+ */
+#ifndef SPLASH_H
+#define SPLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPLASH_API __attribute__((visibility("default")))
+
+typedef enum splash_status {
+  SPLASH_OK = 0,
+  SPLASH_EINVAL = 1,       /* bad argument: nothing was launched or allocated      */
+  SPLASH_ENOMEM = 2,       /* host or device allocation failed                    */
+  SPLASH_EHIP = 3,         /* a HIP runtime call or kernel launch failed          */
+  SPLASH_EUNSUPPORTED = 4  /* valid request outside what the kernel is built for  */
+} splash_status;
+
+typedef enum splash_mask_kind {
+  SPLASH_MASK_CAUSAL = 0,         /* key j allowed for query i iff j <= i                   */
+  SPLASH_MASK_LOCAL = 1,          /* i - left <= j <= i + right; a side < 0 is unbounded     */
+  SPLASH_MASK_CHUNKED_CAUSAL = 2, /* i / chunk == j / chunk and j <= i                       */
+  SPLASH_MASK_DENSE = 3           /* explicit 0/1 bytes, [num_heads, q_len, kv_len]          */
+} splash_mask_kind;
+
+typedef enum splash_dtype {
+  SPLASH_BF16 = 0, /* q, k, v, out are bfloat16; products in bf16 MFMA, fp32 accumulate  */
+  SPLASH_F32 = 1   /* q, k, v, out are float32; fp32 MFMA, no rounding through bf16       */
+} splash_dtype;
+
+/* A mask, as the caller describes it.  Positions are plain indices
+ * 0..q_len-1 and 0..kv_len-1 (top-left alignment). */
+typedef struct splash_mask_desc {
+  int32_t kind;          /* a splash_mask_kind                                              */
+  int32_t num_heads;     /* DENSE: Hm, 1 (shared by every query head) or Hq; else must be 1 */
+  int64_t q_len;         /* Sq >= 0                                                         */
+  int64_t kv_len;        /* Skv >= 0                                                        */
+  int64_t left;          /* LOCAL: left window, < 0 = unbounded                             */
+  int64_t right;         /* LOCAL: right window, < 0 = unbounded                            */
+  int64_t chunk;         /* CHUNKED_CAUSAL: chunk length > 0                                */
+  const uint8_t *dense;  /* DENSE: HOST bytes [num_heads, q_len, kv_len], nonzero = allowed;
+                            borrowed for the duration of the call only                      */
+} splash_mask_desc;
+
+/* The compiled mask.  Opaque; owned by the library. */
+typedef struct splash_mask_info splash_mask_info;
+
+/* Which array of a MaskInfo a view refers to. */
+typedef enum splash_mi_array {
+  SPLASH_MI_BLOCK_MASK = 0,     /* [Hm, nq, W] labels 0/1/2                               */
+  SPLASH_MI_DATA_NEXT = 1,      /* [Hm, nq, W] key/value block column to fetch            */
+  SPLASH_MI_MASK_NEXT = 2,      /* [Hm, nq, W] index into partial blocks (DENSE), or None */
+  SPLASH_MI_PARTIAL_BLOCKS = 3, /* [P, bq, bk] uint8 deduplicated mixed blocks, or None   */
+  SPLASH_MI_Q_SEQUENCE = 4      /* [Sq] int32 query positions (computable), or None       */
+} splash_mi_array;
+
+/* A read-only host view of one MaskInfo array. */
+typedef struct splash_array_view {
+  int32_t elem_bits;   /* 8, 16 or 32                                                  */
+  int32_t is_signed;   /* 1 for the index arrays, 0 for the uint8 partial blocks        */
+  int32_t ndim;        /* 1 or 3                                                       */
+  int32_t _pad;
+  int64_t shape[3];
+  const void *data;    /* NULL <=> the array is None                                    */
+} splash_array_view;
+
+/* Flags of splash_make_mask_info. */
+enum {
+  SPLASH_FLAG_SHRINK = 1,   /* shrink the grid to the longest non-empty block row       */
+  SPLASH_FLAG_DOWNCAST = 2, /* store each index array as int8/int16 when its max fits   */
+  SPLASH_FLAG_DEFAULT = 3
+};
+
+/* Compile a mask into a MaskInfo (host work only; nothing touches the GPU).
+ *
+ * block_q, block_kv: grid-step block (>0, must divide q_len / kv_len).  The
+ * forward kernel runs 128 x 128 blocks; other sizes are for inspection.
+ * Labels follow any/all per block.  Mixed blocks of a DENSE mask are stored
+ * once each, in first-appearance order over (head, row, column) of the
+ * unshrunk grid.  Shrink keeps each block row's non-empty columns ascending
+ * and pads with label-0 slots at the row end to W = max(1, longest row).
+ * data_next at an empty slot holds the next non-empty slot's column in the
+ * row, else the previous one's, else 0; mask_next at a non-partial slot holds
+ * the next partial slot's index, else the previous one's, else 0.  With
+ * SPLASH_FLAG_DOWNCAST each index array is int8 if its max <= 127, else int16
+ * if <= 32767, else int32.  q_sequence is int32 arange(q_len) for computable
+ * masks.
+ *
+ * On success *out owns a new MaskInfo; release it with
+ * splash_mask_info_destroy().  Errors: SPLASH_EINVAL (NULL pointers, unknown
+ * kind, non-dividing blocks, bad window / chunk / head count), SPLASH_ENOMEM. */
+SPLASH_API splash_status splash_make_mask_info(const splash_mask_desc *mask, int32_t block_q,
+                                               int32_t block_kv, uint32_t flags,
+                                               splash_mask_info **out);
+
+/* Host view of one array of a MaskInfo (valid until the MaskInfo is
+ * destroyed).  A None array gives data == NULL and ndim == 0.
+ * Errors: SPLASH_EINVAL for NULL arguments or an unknown array id. */
+SPLASH_API splash_status splash_mask_info_view(const splash_mask_info *mi, int32_t which,
+                                               splash_array_view *view);
+
+/* Copy the MaskInfo to the current HIP device (once per device; later calls
+ * return at once).  splash_fwd does this itself on first use; calling it
+ * ahead keeps the copy out of the first forward call.  Allocates device
+ * memory owned by the MaskInfo.  Errors: SPLASH_EINVAL, SPLASH_ENOMEM,
+ * SPLASH_EHIP. */
+SPLASH_API splash_status splash_mask_info_upload(splash_mask_info *mi);
+
+/* Copy one array of the device copy on the current device back to host
+ * memory `dst` of `nbytes` bytes (must equal the array's byte size), so the
+ * device MaskInfo can be compared bit for bit with the host one.
+ * Synchronous.  Errors: SPLASH_EINVAL (not uploaded to this device, None
+ * array, size mismatch), SPLASH_EHIP. */
+SPLASH_API splash_status splash_mask_info_read_device(const splash_mask_info *mi, int32_t which,
+                                                      void *dst, size_t nbytes);
+
+/* Free a MaskInfo and its device copies.  NULL-safe.  The caller must make
+ * sure no kernel that reads it is still running. */
+SPLASH_API void splash_mask_info_destroy(splash_mask_info *mi);
+
+/* Splash-attention forward on the current HIP device, asynchronous on
+ * hip_stream (a hipStream_t; NULL = the default stream).
+ *
+ * q, k, v, out: DEVICE pointers, contiguous BHSD in `dtype`.  lse: DEVICE
+ * float32 [B, Hq, Sq], or NULL to skip it.  All are owned by the caller and
+ * must stay valid until the stream reaches the kernel's end.
+ *
+ * For every (b, h, i): over the keys j the MaskInfo allows for query i
+ * (mask head h if Hm == Hq, else 0),
+ *   s_ij = softmax_scale * <q_i, k_j>, capped to c * tanh(s_ij / c) when a
+ *   soft cap c is given; out_i = sum_j softmax(s_i)_j v_j and
+ *   lse_i = log sum_j exp(s_ij) (natural log).
+ * A row with no allowed key gets out_i = 0 and lse_i = -inf.
+ * softmax_scale: NaN selects D ** -0.5; otherwise must be finite and > 0.
+ * logits_soft_cap: a finite value > 0 turns the cap on; 0, a negative value,
+ * NaN or +inf turn it off.
+ *
+ * Requirements: mi built with 128 x 128 blocks for q_len == Sq and
+ * kv_len == Skv; Hm in {1, Hq}; Hq % Hkv == 0; D == Dv in {64, 128}.
+ * B, Hq or Sq equal to 0 is a no-op.  Validation failures return
+ * SPLASH_EINVAL (or SPLASH_EUNSUPPORTED for a head dim / block size the
+ * kernel is not built for) before anything runs.  The first call on a device
+ * uploads the MaskInfo (see splash_mask_info_upload); later calls allocate
+ * nothing.  A launch failure returns SPLASH_EHIP. */
+SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void *q, const void *k,
+                                    const void *v, void *out, float *lse, int64_t B, int64_t Hq,
+                                    int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D, int64_t Dv,
+                                    int32_t dtype, float softmax_scale, float logits_soft_cap,
+                                    void *hip_stream);
+
+/* Message of the last failed call on this thread ("" if none).  The string
+ * stays valid until the next library call on this thread. */
+SPLASH_API const char *splash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLASH_H */

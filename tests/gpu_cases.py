@@ -1,0 +1,51 @@
+"""Shared helpers for the GPU parity tests: run the HIP path and the oracle
+on the same seeded inputs."""
+import numpy as np
+import torch
+
+from block_sparse_attention_make_amd import make_mask_info, splash_fwd
+from oracle import attention as oatt
+from oracle import masks as omasks
+
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-5}
+
+
+def mask_rows_fn(kind, skv, left=None, right=None, chunk=None, dense=None):
+    if kind == "dense":
+        return lambda h, rows: dense[0 if dense.shape[0] == 1 else h][rows]
+    cols = np.arange(skv)
+    return lambda h, rows: omasks.allowed_block(kind, rows, cols, left=left, right=right, chunk=chunk)
+
+
+def run_gpu(q, k, v, kind, left=None, right=None, chunk=None, dense=None, cap=None, scale=None,
+            nan_fill=True):
+    dev = torch.device("cuda:0")
+    Sq, Skv = q.shape[2], k.shape[2]
+    mi = make_mask_info(kind, Sq, Skv, left=left, right=right, chunk=chunk, dense=dense)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = lse = None
+    if nan_fill:   # rows the kernel fails to write stay NaN and fail the comparison
+        out = torch.full((q.shape[0], q.shape[1], Sq, v.shape[3]), float("nan"), dtype=q.dtype, device=dev)
+        lse = torch.full((q.shape[0], q.shape[1], Sq), float("nan"), dtype=torch.float32, device=dev)
+    out, lse = splash_fwd(qd, kd, vd, mi, softmax_scale=scale, logits_soft_cap=cap, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy(), mi
+
+
+def oracle_full(q, k, v, kind, left=None, right=None, chunk=None, dense=None, cap=None, scale=None):
+    fn = mask_rows_fn(kind, k.shape[2], left, right, chunk, dense)
+    return oatt.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), fn,
+                          scale=scale, soft_cap=cap)
+
+
+def compare(o, l, o_ref, l_ref, tol, what=""):
+    """Max-abs error on out and lse; -inf lse rows must match exactly."""
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    inf_ref = ~np.isfinite(l_ref)
+    assert np.array_equal(inf_ref, ~np.isfinite(l)), f"{what}: -inf lse rows differ"
+    assert (l[inf_ref] == -np.inf).all() and (l_ref[inf_ref] == -np.inf).all()
+    err_o = float(np.abs(o - o_ref).max()) if o.size else 0.0
+    err_l = float(np.abs(l[~inf_ref] - l_ref[~inf_ref]).max()) if (~inf_ref).any() else 0.0
+    print(f"{what}: max|dO|={err_o:.3e} max|dlse|={err_l:.3e} tol={tol}", flush=True)
+    assert err_o <= tol and err_l <= tol, (what, err_o, err_l)
+    return err_o, err_l

@@ -1,0 +1,101 @@
+"""The C ABI: every symbol include/splash.h declares is exported, and
+argument errors come back as status codes before anything runs (CPU; no
+GPU compute is called here)."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_make_amd import splash
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "splash.h")).read()
+    return sorted(set(re.findall(r"SPLASH_API\s+[\w\s\*]+?\b(splash_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted([
+        "splash_fwd", "splash_last_error", "splash_make_mask_info", "splash_mask_info_destroy",
+        "splash_mask_info_read_device", "splash_mask_info_upload", "splash_mask_info_view"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = splash.load_library()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    # nothing else with C linkage leaks out under the splash_ prefix
+    out = os.popen(f"nm -D --defined-only {splash.LIB_PATH}").read()
+    exported = sorted(set(re.findall(r"\b(splash_\w+)\b", out)))
+    assert exported == declared_symbols()
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(splash._MaskDesc) == 56
+    assert ctypes.sizeof(splash._ArrayView) == 48
+
+
+def _fwd_args(info, **over):
+    mi = info
+    a = dict(mi=mi.handle, q=16, k=16, v=16, out=16, lse=None, B=1, Hq=2, Hkv=2, Sq=mi.q_len,
+             Skv=mi.kv_len, D=128, Dv=128, dtype=splash.BF16, scale=math.nan, cap=0.0, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Sq=256), splash.EINVAL),                 # does not match the MaskInfo
+    (dict(Hq=3, Hkv=2), splash.EINVAL),            # head ratio
+    (dict(D=96, Dv=96), splash.EUNSUPPORTED),      # head dim not built
+    (dict(D=128, Dv=64), splash.EUNSUPPORTED),
+    (dict(dtype=7), splash.EINVAL),
+    (dict(scale=-1.0), splash.EINVAL),
+    (dict(scale=math.inf), splash.EINVAL),
+    (dict(q=0), splash.EINVAL),                    # NULL tensor
+    (dict(q=8), splash.EINVAL),                    # misaligned
+    (dict(mi=None), splash.EINVAL),
+])
+def test_fwd_validation_errors_before_launch(over, status):
+    lib = splash.load_library()
+    mi = splash.make_mask_info("causal", 512, 512)
+    st = lib.splash_fwd(*_fwd_args(mi, **over))
+    assert st == status, lib.splash_last_error()
+    assert lib.splash_last_error()
+
+
+def test_fwd_rejects_non_128_blocks():
+    lib = splash.load_library()
+    mi = splash.make_mask_info("causal", 512, 512, block_q=64, block_kv=64)
+    assert lib.splash_fwd(*_fwd_args(mi)) == splash.EUNSUPPORTED
+
+
+def test_fwd_rejects_mask_head_mismatch():
+    lib = splash.load_library()
+    m = np.ones((3, 128, 128), dtype=bool)
+    mi = splash.make_mask_info("dense", 128, 128, dense=m)
+    assert lib.splash_fwd(*_fwd_args(mi, Hq=2, Hkv=2)) == splash.EINVAL
+
+
+def test_fwd_empty_batch_is_noop():
+    lib = splash.load_library()
+    mi = splash.make_mask_info("causal", 512, 512)
+    assert lib.splash_fwd(*_fwd_args(mi, B=0, q=0, k=0, v=0, out=0)) == splash.OK
+
+
+def test_null_arguments():
+    lib = splash.load_library()
+    assert lib.splash_make_mask_info(None, 128, 128, 3, None) == splash.EINVAL
+    assert lib.splash_mask_info_view(None, 0, None) == splash.EINVAL
+    assert lib.splash_mask_info_upload(None) == splash.EINVAL
+    lib.splash_mask_info_destroy(None)
+    mi = splash.make_mask_info("causal", 256, 256)
+    v = splash._ArrayView()
+    assert lib.splash_mask_info_view(mi.handle, 9, ctypes.byref(v)) == splash.EINVAL
+    # not uploaded -> read_device refuses
+    buf = np.zeros(4, dtype=np.int8)
+    assert lib.splash_mask_info_read_device(mi.handle, 0, buf.ctypes.data, 4) == splash.EINVAL

@@ -1,0 +1,110 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element.
+
+Small cases span several 128-blocks with odd block counts, every mask kind,
+GQA / MQA, the soft cap, both dtypes and head dims, Sq != Skv, per-head dense
+masks and fully masked rows.  Tolerances: max-abs 2e-2 (bf16) and 1e-5
+(float32) on out and lse.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_make_amd import synthetic
+from tests.gpu_cases import TOL, compare, oracle_full, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+SMALL = [
+    # name, seed, B, Hq, Hkv, Sq, Skv, D, dtype, mask kwargs, cap
+    ("causal_5blk_gqa", 11, 2, 4, 2, 640, 640, 128, torch.bfloat16, dict(kind="causal"), None),
+    ("causal_mqa", 12, 1, 3, 1, 384, 384, 128, torch.bfloat16, dict(kind="causal"), None),
+    ("local_200_50", 13, 1, 4, 4, 768, 768, 128, torch.bfloat16, dict(kind="local", left=200, right=50), None),
+    ("local_right_only", 14, 1, 2, 2, 512, 512, 128, torch.bfloat16, dict(kind="local", left=None, right=100), None),
+    ("chunked_300_cap", 15, 1, 4, 2, 1024, 1024, 128, torch.bfloat16, dict(kind="chunked", chunk=300), 5.0),
+    ("chunked_256", 16, 2, 2, 2, 896, 896, 128, torch.bfloat16, dict(kind="chunked", chunk=256), None),
+    ("causal_rect_sq_lt_skv", 17, 1, 2, 2, 256, 640, 128, torch.bfloat16, dict(kind="causal"), None),
+    ("causal_rect_sq_gt_skv", 18, 1, 2, 2, 640, 256, 128, torch.bfloat16, dict(kind="causal"), None),
+    ("causal_d64_bf16", 19, 1, 4, 2, 512, 512, 64, torch.bfloat16, dict(kind="causal"), None),
+    ("causal_d128_f32", 20, 1, 2, 1, 384, 384, 128, torch.float32, dict(kind="causal"), None),
+    ("local_d64_f32_cap", 21, 1, 2, 2, 512, 512, 64, torch.float32, dict(kind="local", left=130, right=3), 4.0),
+    ("one_block", 22, 1, 1, 1, 128, 128, 128, torch.bfloat16, dict(kind="causal"), None),
+    ("cap_only_full", 23, 1, 2, 2, 256, 256, 128, torch.bfloat16, dict(kind="local", left=None, right=None), 2.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(case):
+    name, seed, B, Hq, Hkv, Sq, Skv, D, dt, mk, cap = case
+    q, k, v = synthetic.make_qkv(seed, B, Hq, Hkv, Sq, Skv, D, D, dtype=dt)
+    o, l, _ = run_gpu(q, k, v, cap=cap, **mk)
+    o_ref, l_ref = oracle_full(q, k, v, cap=cap, **mk)
+    compare(o, l, o_ref, l_ref, TOL[dt], name)
+
+
+@pytest.mark.parametrize("hm", [1, 4])
+def test_dense_random_small(hm):
+    rng = np.random.default_rng(30 + hm)
+    q, k, v = synthetic.make_qkv(31, 1, 4, 2, 512, 640, 128, 128)
+    dense = synthetic.random_dense_mask(rng, hm, 512, 640, 0.2, force_diagonal=True)
+    # plant an all-ones block, an all-zeros block and a repeated block
+    dense[:, 0:128, 128:256] = True
+    dense[:, 128:256, 0:128] = False
+    dense[:, 384:512, 512:640] = dense[:, 256:384, 384:512]
+    o, l, mi = run_gpu(q, k, v, "dense", dense=dense)
+    o_ref, l_ref = oracle_full(q, k, v, "dense", dense=dense)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], f"dense_hm{hm}")
+
+
+def test_fully_masked_rows_give_zero_and_neg_inf():
+    q, k, v = synthetic.make_qkv(40, 1, 2, 2, 256, 384, 128, 128)
+    dense = np.ones((1, 256, 384), dtype=bool)
+    dense[0, 5] = False                    # one empty row inside a partial block
+    dense[0, 128:256, :] = False           # a whole empty block row (label 0 everywhere)
+    o, l, _ = run_gpu(q, k, v, "dense", dense=dense)
+    o_ref, l_ref = oracle_full(q, k, v, "dense", dense=dense)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], "masked_rows")
+    assert (o[:, :, 128:256] == 0).all() and (l[:, :, 128:256] == -np.inf).all()
+    assert (o[:, :, 5] == 0).all() and (l[:, :, 5] == -np.inf).all()
+
+
+def test_tiny_causal_f32_workload_full():
+    w = synthetic.WORKLOADS["tiny_causal_f32"]
+    q, k, v, _ = synthetic.make_inputs(w)
+    o, l, mi = run_gpu(q, k, v, "causal")
+    o_ref, l_ref = oracle_full(q, k, v, "causal")
+    compare(o, l, o_ref, l_ref, TOL[torch.float32], w.name)
+    assert int((mi.block_mask == 0).sum()) == 6
+
+
+def test_random_dense_workload_full():
+    w = synthetic.WORKLOADS["random_dense_2k"]
+    q, k, v, dense = synthetic.make_inputs(w)
+    o, l, _ = run_gpu(q, k, v, "dense", dense=dense)
+    o_ref, l_ref = oracle_full(q, k, v, "dense", dense=dense)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], w.name)
+
+
+def test_explicit_scale_and_no_lse():
+    from block_sparse_attention_make_amd import make_mask_info, splash_fwd
+    q, k, v = synthetic.make_qkv(50, 1, 2, 2, 256, 256, 128, 128)
+    dev = torch.device("cuda:0")
+    mi = make_mask_info("causal", 256, 256)
+    out, lse = splash_fwd(q.to(dev), k.to(dev), v.to(dev), mi, softmax_scale=0.05, return_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    o_ref, _ = oracle_full(q, k, v, "causal", scale=0.05)
+    assert float(np.abs(out.float().cpu().numpy() - o_ref).max()) <= 2e-2
+
+
+def test_repeat_calls_are_bitwise_identical():
+    q, k, v = synthetic.make_qkv(60, 1, 4, 4, 512, 512, 128, 128)
+    a = run_gpu(q, k, v, "local", left=300, right=0)
+    b = run_gpu(q, k, v, "local", left=300, right=0)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
