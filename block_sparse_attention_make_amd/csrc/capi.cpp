@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "mask_info.h"
 #include "splash_kernel.h"
@@ -41,8 +42,28 @@ void free_copy(DeviceCopy &dc) {
   }
   if (dc.row_order) (void)hipFree(dc.row_order);
   dc.row_order = nullptr;
+  if (dc.mask_bits) (void)hipFree(dc.mask_bits);
+  dc.mask_bits = nullptr;
+  dc.mask_bits_bytes = 0;
   dc.device = -1;
   if (prev >= 0) (void)hipSetDevice(prev);
+}
+
+// Partial blocks [P, bq, bk] (one byte per element) packed to 32-key words:
+// word [(p * (bk / 32) + j) * bq + i], bit c <=> element (i, 32 j + c) != 0.
+std::vector<uint32_t> pack_mask_bits(const HostArray &pm) {
+  const int64_t P = pm.shape[0], bq = pm.shape[1], bk = pm.shape[2], groups = bk / 32;
+  std::vector<uint32_t> bits(static_cast<size_t>(P * groups * bq), 0u);
+  for (int64_t b = 0; b < P; ++b)
+    for (int64_t i = 0; i < bq; ++i) {
+      const uint8_t *row = pm.bytes.data() + (b * bq + i) * bk;
+      for (int64_t j = 0; j < groups; ++j) {
+        uint32_t w = 0;
+        for (int c = 0; c < 32; ++c) w |= (row[32 * j + c] != 0 ? 1u : 0u) << c;
+        bits[static_cast<size_t>((b * groups + j) * bq + i)] = w;
+      }
+    }
+  return bits;
 }
 
 // Device copy for the current device, uploading it if needed.
@@ -77,6 +98,18 @@ splash_status ensure_device_copy(splash_mask_info *mi, DeviceCopy **out) {
       free_copy(fresh);
       return hip_fail(e, "uploading MaskInfo row order");
     }
+  }
+  const HostArray &pm = mi->arr[SPLASH_MI_PARTIAL_BLOCKS];
+  if (pm.present && pm.ndim == 3 && pm.shape[0] > 0 && pm.shape[2] % 32 == 0) {
+    const std::vector<uint32_t> bits = pack_mask_bits(pm);
+    const size_t nb = bits.size() * sizeof(uint32_t);
+    e = hipMalloc(reinterpret_cast<void **>(&fresh.mask_bits), nb);
+    if (e == hipSuccess) e = hipMemcpy(fresh.mask_bits, bits.data(), nb, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      free_copy(fresh);
+      return hip_fail(e, "uploading packed mask blocks");
+    }
+    fresh.mask_bits_bytes = static_cast<int64_t>(nb);
   }
   dc = fresh;
   *out = &dc;
@@ -186,6 +219,8 @@ extern "C" SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void 
   p.dn = dc->ptr[SPLASH_MI_DATA_NEXT];
   p.mn = dc->ptr[SPLASH_MI_MASK_NEXT];
   p.pmb = static_cast<const uint8_t *>(dc->ptr[SPLASH_MI_PARTIAL_BLOCKS]);
+  p.pmb_bits = dc->mask_bits;
+  p.pmb_bits_bytes = dc->mask_bits_bytes;
   p.q_seq = static_cast<const int32_t *>(dc->ptr[SPLASH_MI_Q_SEQUENCE]);
   p.row_order = dc->row_order;
   p.bm_bytes = mi->arr[SPLASH_MI_BLOCK_MASK].elem_bits / 8;

@@ -32,6 +32,12 @@ struct DeviceCopy {
   int device = -1;
   void *ptr[kNumArrays] = {nullptr, nullptr, nullptr, nullptr, nullptr};
   int32_t *row_order = nullptr;
+  // Partial mask blocks packed to bits for the bf16 kernel: for block p,
+  // 32-key group j and block row i, word [(p * (bk / 32) + j) * bq + i] holds
+  // in bit c whether key 32 j + c is allowed.  Null when there are none or
+  // the block width is not a multiple of 32.
+  uint32_t *mask_bits = nullptr;
+  int64_t mask_bits_bytes = 0;
 };
 
 }  // namespace splash

@@ -428,6 +428,739 @@ void splash_fwd_kernel(const FwdParams p) {
   }
 }
 
+// ===========================================================================
+// bf16 kernel with 64 query rows per wave ("wide" rows).
+//
+// Why: with 32 rows per wave every wave reads the whole K and V tile from LDS
+// for only 32 rows of work, which puts LDS read time at or above the MFMA
+// time.  Here each wave owns 64 query rows -- two 32-row halves (qs = 0, 1)
+// that share every K and V operand read -- so LDS reads per flop halve.  The
+// price is registers (Q and O for 64 rows), so one wave runs per SIMD and the
+// overlap of softmax (VALU) with matrix work (MFMA) comes from software
+// pipelining inside the wave instead of from a second wave: pipeline step u
+// (32 keys, a quarter of a 128-key block) runs
+//     QK(u+1)  ||  softmax(u)  ||  PV(u-1)
+// with independent register sets, so the exponentials of one step issue
+// between the matrix instructions of its neighbours.
+//
+// Workgroup: two waves = 128 query rows = one mask block row; two workgroups
+// share a CU.  K and V arrive in LDS through direct-to-LDS loads (no VGPRs),
+// 32 keys per stage, four stages each.  The loads of K(u+4) and V(u+2) are
+// issued at the top of iteration u into the stages iteration u-1 finished
+// reading; step u+1's K and step u-1's V must have landed by the top of
+// iteration u, so each load has three iterations to arrive.
+constexpr int kWWaves = 2;
+constexpr int kWThreads = 64 * kWWaves;
+constexpr int kSK = 32;            // keys per pipeline step
+constexpr int kSteps = kBK / kSK;  // steps per mask block
+constexpr int kStages = 4;         // LDS stages for K and for V
+constexpr int kWMeta = 256;        // grid positions compacted at a time
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource over `bytes` bytes at `base` (gfx9 data-format word 3).
+// Uniform by construction; readfirstlane keeps it in SGPRs.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, int64_t bytes) {
+  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+  i32x4 v;
+  __builtin_memcpy(&v, &r, sizeof(v));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  return v;
+}
+
+// Barrier that waits only for this wave's LDS operations; global->LDS loads
+// are awaited explicitly with wait_vmcnt, so a prefetch may stay in flight
+// across it.  The asm is also a compiler memory barrier for LDS accesses.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One 32-key stage of K or V: 32 rows of D bf16, 16-byte chunks XOR-swizzled
+// per row (the swizzles of the 128-row tiles above).
+template <int D>
+struct Stage {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kBytes = kSK * kRowBytes;
+  static constexpr int kInsts = kBytes / 1024 / kWWaves;  // 1 KiB loads per wave per stage
+  __device__ static int swz_k(int row) {
+    if constexpr (kChunks >= 16) return row & 15;
+    else return (row >> 1) & 7;
+  }
+  __device__ static int swz_v(int row) {
+    if constexpr (kChunks >= 16) return (row & 3) << 2;
+    else return ((row >> 1) & 1) << 2;
+  }
+};
+
+// Issue the direct-to-LDS loads (buffer_load_dwordx4 ... lds) of one stage:
+// rows [row0, row0 + 32) of a (batch, kv-head) K or V array described by
+// `res`.  Wave w moves the stage's 1 KiB segments w*kInsts .. w*kInsts+kInsts-1.
+// Each instruction writes 64 lanes x 16 bytes to consecutive LDS bytes
+// (M0 + instruction offset + 16 lane); the instruction offset is added to
+// the global address too, so one M0 value serves all of a wave's segments.
+// The swizzle is applied on the global side: the lane that lands on chunk pc
+// of a row fetches logical chunk pc ^ swz(row).  Reads past the resource's
+// end return zeros instead of faulting.
+//
+// Issued from inline assembly so the compiler does not track them: it cannot
+// tell that a load into one stage does not alias LDS reads of another and
+// would otherwise drain every prefetch before each LDS read.  Completion is
+// awaited with wait_vmcnt before the barrier that publishes a stage; waits the
+// compiler computes for its own loads stay correct (loads retire in order, so
+// extra loads in flight only make them more conservative).  M0 is written in
+// the same statement as the loads that read it.
+template <int D, bool IS_V>
+__device__ __forceinline__ uint32_t stage_voff(int wave, int lane, int i) {
+  using SG = Stage<D>;
+  constexpr int kRowsPerSeg = 1024 / SG::kRowBytes;
+  constexpr int kLanesPerRow = SG::kChunks;
+  const int seg = wave * SG::kInsts + i;
+  const int row = seg * kRowsPerSeg + lane / kLanesPerRow;
+  const int pc = lane % kLanesPerRow;
+  const int c = pc ^ (IS_V ? SG::swz_v(row) : SG::swz_k(row));
+  return static_cast<uint32_t>((lane / kLanesPerRow) * SG::kRowBytes + c * 16);
+}
+
+template <int D, bool IS_V>
+__device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, int wave, int lane) {
+  using SG = Stage<D>;
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) char *)(lds + wave * SG::kInsts * 1024)));
+  const uint32_t soff = static_cast<uint32_t>(row0 * SG::kRowBytes) + wave * SG::kInsts * 1024;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (SG::kInsts == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
+        :: "s"(m0), "v"(stage_voff<D, IS_V>(wave, lane, 0)), "v"(stage_voff<D, IS_V>(wave, lane, 1)),
+           "v"(stage_voff<D, IS_V>(wave, lane, 2)), "v"(stage_voff<D, IS_V>(wave, lane, 3)), "s"(res), "s"(soff)
+        : "memory", "m0");
+  } else {
+    static_assert(SG::kInsts == 2, "stage loads per wave");
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
+        :: "s"(m0), "v"(stage_voff<D, IS_V>(wave, lane, 0)), "v"(stage_voff<D, IS_V>(wave, lane, 1)), "s"(res),
+           "s"(soff)
+        : "memory", "m0");
+  }
+#pragma clang diagnostic pop
+}
+
+// S^T for one 32-key step: sc[qs] holds, for this lane's row of half qs, keys
+// 8(v/4) + 4 half + v%4 of the step.
+template <int D>
+__device__ __forceinline__ void wide_qk(const char *ks_lds, const bf16x8 (*qf)[D / 16], int lane, int half,
+                                        f32x16 *sc) {
+  using SG = Stage<D>;
+  const f32x16 zero16 = {};
+  const int row = lane & 31;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+        ks_lds + row * SG::kRowBytes + (((2 * ks + half) ^ SG::swz_k(row)) * 16));
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+      sc[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qs][ks], ks == 0 ? zero16 : sc[qs], 0, 0, 0);
+  }
+}
+
+// Per-row softmax state of the wide kernel.  The exponent base of a row is
+// fixed by its first step with an allowed key and never moves afterwards, so
+// the accumulator is never rescaled inside the loop: exponentials of later,
+// larger scores simply exceed 1.  That is exact as long as they stay far
+// from the float range.  A step whose exponentials of one row sum to more
+// than 2^64 (so some exceeded 2^59) raises `over`, and the whole row is then
+// computed again with its exact max as the base (found by a QK-only pass),
+// where every exponential is at most 1.
+constexpr float kOverflowSum = 18446744073709551616.f;   // 2^64
+
+struct RowState {
+  float base[2];   // exponent base, base-2 units (-inf until the first allowed key)
+  float l[2];      // this lane's share of the running sum
+  bool over;       // some step's sum exceeded kOverflowSum
+};
+
+// Scores of one step -> capped (base-2 units), masked.  MASK: label-1 step.
+// Computable masks use the row's key interval; dense masks the packed word
+// of the row (bit c <=> key c of the step).
+template <bool CAP, bool DENSE, bool MASK>
+__device__ __forceinline__ void wide_cap_mask(const FwdParams &p, f32x16 *sc, int key0, int half, const int *lo,
+                                              const int *hi, const unsigned *mword) {
+  if constexpr (CAP) {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        // a key masked before the cap stays at -inf (tanh alone would map it to -cap)
+        const float x = sc[qs][v] * p.c2;  // c2 = scale / cap here
+        const float e = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(x));
+        const float th = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+        sc[qs][v] = x == -INFINITY ? -INFINITY : copysignf(th, x) * p.cap_out;
+      }
+  }
+  if constexpr (MASK) {
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const unsigned w = mword[qs] >> (4 * half);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 8 * (v / 4) + (v % 4);
+          sc[qs][v] = ((w >> c) & 1u) ? sc[qs][v] : -INFINITY;
+        }
+      }
+    } else {
+      const int kb = key0 + 4 * half;
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) {
+        const int rlo = min(max(lo[qs] - kb, -1), kSK);
+        const int rhi = min(max(hi[qs] - kb, -1), kSK);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 8 * (v / 4) + (v % 4);
+          sc[qs][v] = (c >= rlo && c <= rhi) ? sc[qs][v] : -INFINITY;
+        }
+      }
+    }
+  }
+}
+
+// O^T += V^T P^T for one step.  The lane supplies V[key][dv] for
+// dv = 32 dt + lane%32 and the keys 16h + 4 half + {0..3, 8..11} -- the order
+// in which pf holds them -- with two transposing reads.
+template <int D>
+__device__ __forceinline__ void wide_pv(const char *vs_lds, const bf16x8 (*pf)[2], int lane, int half,
+                                        f32x16 (*o)[2]) {
+  using SG = Stage<D>;
+  const int trow = 4 * half + ((lane & 15) >> 2);
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int row0 = 16 * h + trow;
+      const int col = 32 * dt + tcol;
+      const int c = col >> 3, within = (col & 7) * 2;
+      const char *a0 = vs_lds + row0 * SG::kRowBytes + ((c ^ SG::swz_v(row0)) * 16) + within;
+      const char *a1 = vs_lds + (row0 + 8) * SG::kRowBytes + ((c ^ SG::swz_v(row0 + 8)) * 16) + within;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a0));
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a1));
+      const s16x4 both[2] = {lo4, hi4};
+      bf16x8 a;
+      __builtin_memcpy(&a, both, 16);
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+        o[dt][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qs][h], o[dt][qs], 0, 0, 0);
+    }
+}
+
+// Wait until at most n vector-memory loads of this wave are in flight
+// (n <= N; s_waitcnt takes an immediate, so walk down from N).
+template <int N>
+__device__ __forceinline__ void wait_at_most(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) wait_vmcnt<N>();
+    else wait_at_most<N - 1>(n);
+  }
+}
+
+template <int D, bool CAP, bool DENSE>
+__global__ __launch_bounds__(kWThreads, 1)
+void splash_fwd_wide(const FwdParams p) {
+  using SG = Stage<D>;
+  constexpr int kDT = D / 32;
+  constexpr int kKS = D / 16;
+  constexpr int kMaskBytes = kBQ * 4;            // one packed word per block row per step
+  constexpr int kMaxInFlight = 5 * SG::kInsts + 3;
+
+  __shared__ __attribute__((aligned(1024))) char k_st[kStages][SG::kBytes];
+  __shared__ __attribute__((aligned(1024))) char v_st[kStages][SG::kBytes];
+  __shared__ __attribute__((aligned(16))) char m_st[DENSE ? kStages : 1][kMaskBytes];
+  __shared__ int c_kvb[kWMeta], c_lab[kWMeta], c_mn[kWMeta];
+  __shared__ int wave_count[kWWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+
+  // Same (batch, head, row) mapping as the 32-row kernel: XCD x gets a
+  // contiguous range of (batch, head) pairs, rows go out longest first.
+  const int nbh = static_cast<int>(p.B * p.Hq);
+  const int pid = blockIdx.x;
+  int bh, rank;
+  if ((nbh & 7) == 0) {
+    const int per = nbh >> 3, x = pid & 7, j = pid >> 3;
+    bh = x * per + j % per;
+    rank = j / per;
+  } else {
+    bh = pid % nbh;
+    rank = pid / nbh;
+  }
+  const int r = p.row_order[rank];
+  const int b = bh / static_cast<int>(p.Hq);
+  const int hq = bh % static_cast<int>(p.Hq);
+  const int hkv = hq / p.group;
+  const int hm = p.hm == 1 ? 0 : hq;
+  const int row_in_block0 = 64 * wave + (lane & 31);      // qs = 0; qs = 1 adds 32
+  const int64_t q_row0 = static_cast<int64_t>(r) * kBQ + row_in_block0;
+
+  // V stages start as zeros: the first step's PV(-1) reads the last stage
+  // with zero P, and 0 * (uninitialised LDS) could be NaN.
+#pragma unroll
+  for (int i = 0; i < kStages * SG::kBytes / (16 * kWThreads); ++i)
+    reinterpret_cast<u32x4 *>(&v_st[0][0])[tid + kWThreads * i] = u32x4{0u, 0u, 0u, 0u};
+
+  const __bf16 *kg = static_cast<const __bf16 *>(p.k) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
+  const __bf16 *vg = static_cast<const __bf16 *>(p.v) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
+  const i32x4 k_res = make_rsrc(kg, p.Skv * D * 2);
+  const i32x4 v_res = make_rsrc(vg, p.Skv * D * 2);
+  const bool has_bits = DENSE && p.pmb_bits != nullptr;
+  const i32x4 m_res = make_rsrc(has_bits ? static_cast<const void *>(p.pmb_bits) : p.k,
+                                has_bits ? p.pmb_bits_bytes : 0);
+  const int64_t meta_base = (static_cast<int64_t>(hm) * p.nq + r) * p.width;
+
+  bf16x8 qf[2][kKS];       // Q (B operand of S^T = K Q^T), rows of both halves
+  int lo[2], hi[2];        // computable masks: allowed key interval, clamped to [-1, Skv]
+  {
+    const __bf16 *qg = static_cast<const __bf16 *>(p.q) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row0) * D;
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+        qf[qs][ks] = *reinterpret_cast<const bf16x8 *>(qg + static_cast<int64_t>(32 * qs) * D + 16 * ks + 8 * half);
+  }
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    lo[qs] = hi[qs] = 0;
+    if constexpr (!DENSE) {
+      // Every computable mask admits, for query position i, one key interval:
+      // causal (-inf, i]; local [i - left, i + right]; chunked [chunk start, i].
+      const int64_t qpos = p.q_seq[q_row0 + 32 * qs];
+      int64_t l64, h64;
+      if (p.mask_kind == 0) { l64 = -1; h64 = qpos; }
+      else if (p.mask_kind == 1) { l64 = p.left < 0 ? -1 : qpos - p.left; h64 = p.right < 0 ? p.Skv : qpos + p.right; }
+      else { l64 = (qpos / p.chunk) * p.chunk; h64 = qpos; }
+      lo[qs] = static_cast<int>(clamp64(l64, -1, p.Skv));
+      hi[qs] = static_cast<int>(clamp64(h64, -1, p.Skv));
+    }
+  }
+  const float c2e = CAP ? 1.f : p.c2;
+
+  // Compact one chunk of the block row's grid positions: keep label > 0.
+  // Entry j + 1 is the block data_next points the pipeline at after entry j.
+  // Returns the number kept (uniform).
+  auto compact = [&](int s0) -> int {
+    const int n_meta = min(kWMeta, p.width - s0);
+    __syncthreads();
+    int lab[kWMeta / kWThreads], kv_t[kWMeta / kWThreads], mn_t[kWMeta / kWThreads];
+    int tot = 0;
+#pragma unroll
+    for (int i = 0; i < kWMeta / kWThreads; ++i) {
+      const int s = tid + kWThreads * i;
+      lab[i] = 0; kv_t[i] = 0; mn_t[i] = 0;
+      if (s < n_meta) {
+        lab[i] = load_index(p.bm, p.bm_bytes, meta_base + s0 + s);
+        kv_t[i] = load_index(p.dn, p.dn_bytes, meta_base + s0 + s);
+        if constexpr (DENSE) mn_t[i] = load_index(p.mn, p.mn_bytes, meta_base + s0 + s);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kWMeta / kWThreads; ++i) {
+      const uint64_t keep = __builtin_amdgcn_ballot_w64(lab[i] > 0);
+      if (lane == 0) wave_count[wave] = __builtin_popcountll(keep);
+      __syncthreads();
+      int off = tot;
+#pragma unroll
+      for (int w = 0; w < kWWaves; ++w) {
+        off += w < wave ? wave_count[w] : 0;
+        tot += wave_count[w];
+      }
+      if (lab[i] > 0) {
+        const int at = off + __builtin_popcountll(keep & ((uint64_t(1) << lane) - 1));
+        c_kvb[at] = kv_t[i];
+        c_lab[at] = lab[i];
+        if constexpr (DENSE) c_mn[at] = mn_t[i];
+      }
+      __syncthreads();
+    }
+    return __builtin_amdgcn_readfirstlane(tot);
+  };
+  auto key0 = [&](int u) -> int {
+    return __builtin_amdgcn_readfirstlane(c_kvb[u / kSteps]) * kBK + kSK * (u % kSteps);
+  };
+  auto label = [&](int u) -> int { return __builtin_amdgcn_readfirstlane(c_lab[u / kSteps]); };
+  // Packed mask words of step u (dense): this wave's 64 block rows.
+  auto issue_mask = [&](int pb, int t, int stage) {   // partial block pb, key group t
+    const uint32_t soff = static_cast<uint32_t>(((pb * kSteps + t) * kBQ + 64 * wave) * 4);
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) char *)(m_st[stage] + 256 * wave)));
+    const uint32_t voff = static_cast<uint32_t>(4 * lane);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(m_res), "s"(soff) : "memory", "m0");
+#pragma clang diagnostic pop
+  };
+  auto mask_words = [&](int stage, unsigned *mw) {
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+        mw[qs] = *reinterpret_cast<const unsigned *>(m_st[stage] + 4 * (row_in_block0 + 32 * qs));
+    }
+  };
+
+  f32x16 o[kDT][2];        // O^T accumulators
+  RowState rs;
+  float base_init[2] = {-INFINITY, -INFINITY};
+
+  // Exponent base of rows that have none yet: the step's max (after cap and
+  // mask; the cap is monotonic, so capping the max gives the max of the
+  // capped scores).  Rows whose keys are all masked so far keep -inf.
+  auto set_base = [&](const f32x16 *sc) {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[qs][v]);
+      mx = pair_max(mx);
+      float mx2 = mx * c2e;
+      if constexpr (CAP) {
+        const float x = mx * p.c2;
+        const float e = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(x));
+        const float th = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+        mx2 = x == -INFINITY ? -INFINITY : copysignf(th, x) * p.cap_out;
+      }
+      rs.base[qs] = rs.base[qs] == -INFINITY ? mx2 : rs.base[qs];
+    }
+  };
+
+  // One step: QK(u+1) || softmax(u) || PV(u-1) as straight-line code cut
+  // into nine slices by scheduling barriers.  Slice i holds the QK MFMAs of
+  // k-step i-1, the PV MFMAs of operand i-1, the LDS reads two slices ahead
+  // of their MFMAs and an eighth of the softmax (four exponentials per row
+  // half), so every matrix instruction has a little VALU work to hide under
+  // and no operand lives longer than a few slices.  The softmax runs against
+  // the row's fixed base; the step's row sums come from dot products of the
+  // bf16 exponentials with ones (the same rounded values PV multiplies) and
+  // double as the overflow test.
+  auto body = [&](int u, f32x16 *sc_cur, f32x16 *sc_nxt, bf16x8 (*pf_cur)[2], bf16x8 (*pf_prv)[2]) {
+    constexpr int kPVOps = 2 * kDT;       // PV A operands per step: (h, dt)
+    const char *kst = k_st[(u + 1) % kStages];
+    const char *vst = v_st[(u + kStages - 1) % kStages];
+    const int krow = lane & 31;
+    const int trow = 4 * half + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto read_k = [&](int ks) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8 *>(kst + krow * SG::kRowBytes +
+                                               (((2 * ks + half) ^ SG::swz_k(krow)) * 16));
+    };
+    auto read_v = [&](int i) -> bf16x8 {
+      const int h = i / kDT, dt = i % kDT;
+      const int row0 = 16 * h + trow;
+      const int col = 32 * dt + tcol;
+      const int c = col >> 3, within = (col & 7) * 2;
+      const char *a0 = vst + row0 * SG::kRowBytes + ((c ^ SG::swz_v(row0)) * 16) + within;
+      const char *a1 = vst + (row0 + 8) * SG::kRowBytes + ((c ^ SG::swz_v(row0 + 8)) * 16) + within;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a0));
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a1));
+      const s16x4 both[2] = {lo4, hi4};
+      bf16x8 r;
+      __builtin_memcpy(&r, both, 16);
+      return r;
+    };
+    const f32x16 zero16 = {};
+    bf16x8 ka[kKS], va[kPVOps];
+    auto mfma_slice = [&](int i) {   // QK k-step i, PV operand i
+      if (i < kKS) {
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+          sc_nxt[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[qs][i], i == 0 ? zero16 : sc_nxt[qs], 0, 0, 0);
+      }
+      if (i < kPVOps) {
+        const int h = i / kDT, dt = i % kDT;
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+          o[dt][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pf_prv[qs][h], o[dt][qs], 0, 0, 0);
+      }
+    };
+    auto reads_slice = [&](int i) {
+      if (i < kKS) ka[i] = read_k(i);
+      if (i < kPVOps) va[i] = read_v(i);
+    };
+    float b2[2], sum[2] = {0.f, 0.f};
+    const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    auto exps = [&](int i) {   // elements 4(i%4) .. +3 of row half i/4
+      const int qs = i / 4, v0 = 4 * (i % 4);
+      float e[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float x = sc_cur[qs][v0 + k];
+        if constexpr (CAP) {
+          // capped logit in base-2 units; a masked key stays at -inf
+          const float xs = x * p.c2;
+          const float t2 = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(xs));
+          const float th = (1.f - t2) * __builtin_amdgcn_rcpf(1.f + t2);
+          x = xs == -INFINITY ? -INFINITY : copysignf(th, xs) * p.cap_out;
+        }
+        e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2e, -b2[qs]));
+      }
+      bf16x2 p01 = {static_cast<__bf16>(e[0]), static_cast<__bf16>(e[1])};
+      bf16x2 p23 = {static_cast<__bf16>(e[2]), static_cast<__bf16>(e[3])};
+      const int h = v0 / 8, e0 = v0 % 8;
+      pf_cur[qs][h][e0 + 0] = p01[0];
+      pf_cur[qs][h][e0 + 1] = p01[1];
+      pf_cur[qs][h][e0 + 2] = p23[0];
+      pf_cur[qs][h][e0 + 3] = p23[1];
+      sum[qs] = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, sum[qs], false);
+      sum[qs] = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, sum[qs], false);
+    };
+
+    // slice 0: operands of MFMA slices 0 and 1
+    reads_slice(0);
+    reads_slice(1);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) b2[qs] = rs.base[qs] == -INFINITY ? 0.f : rs.base[qs];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i + 2 < 8) reads_slice(i + 2);
+      mfma_slice(i);
+      exps(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    static_assert(kKS <= 8 && kPVOps <= 8, "slice plan assumes at most 8 operands");
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      rs.l[qs] += sum[qs];
+      rs.over |= sum[qs] > kOverflowSum;
+    }
+    // Keep this step's softmax results here: without a use in this block
+    // the compiler sinks the exponentials into the next step, after its
+    // branches, where they no longer overlap these MFMAs.
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pf_cur[qs][h]));
+      asm volatile("" : "+v"(rs.l[qs]));
+    }
+  };
+
+  for (int attempt = 0; attempt < 2; ++attempt) {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      rs.base[qs] = base_init[qs];
+      rs.l[qs] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][qs][v] = 0.f;
+    }
+    rs.over = false;
+
+    for (int s0 = 0; s0 < p.width; s0 += kWMeta) {
+      const int nb = compact(s0);
+      if (nb == 0) continue;
+      const int N = kSteps * nb;   // pipeline steps
+
+      // Loads of (virtual) iteration w: K(w+4), V(w+2) and, for dense masks,
+      // the mask words of step w+4 -- those that exist.  Counted per wave.
+      auto count = [&](int w) -> int {
+        return (w + 4 >= 0 && w + 4 < N ? SG::kInsts + (has_bits ? 1 : 0) : 0) +
+               (w + 2 >= 0 && w + 2 < N ? SG::kInsts : 0);
+      };
+      auto load_k = [&](int stage, int kv, int t) {
+        issue_stage<D, false>(k_st[stage], k_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane);
+      };
+      auto load_v = [&](int stage, int kv, int t) {
+        issue_stage<D, true>(v_st[stage], v_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane);
+      };
+      auto load_m = [&](int stage, int mn, int t) {
+        if (has_bits) issue_mask(mn, t, stage);
+      };
+
+      f32x16 sc_a[2], sc_b[2];         // scores: step being exponentiated / step being formed
+      bf16x8 pf_a[2][2], pf_b[2][2];   // P of the step being exponentiated / being multiplied
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pf_b[qs][h] = bf16x8{};   // PV(-1) adds exact zeros
+
+      // Cap-free finishing of freshly formed scores S(u) (in sc): the mask of
+      // a label-1 step, and the exponent base of rows that have none.  Runs
+      // right after the QK that formed them, so the scores move from the
+      // accumulators to VGPRs once and stay there for the softmax.
+      // (The empty volatile asm statements keep the compiler from running the
+      // masking unconditionally and selecting the result.)
+      auto finish = [&](f32x16 *sc, int lab, int stage, int key0) {
+        if (lab == 1) {
+          asm volatile("");
+          unsigned mw[2] = {0u, 0u};
+          mask_words(stage, mw);
+          wide_cap_mask<false, DENSE, true>(p, sc, key0, half, lo, hi, mw);
+        }
+        if (__builtin_amdgcn_ballot_w64(rs.base[0] == -INFINITY || rs.base[1] == -INFINITY) != 0) {
+          asm volatile("");
+          set_base(sc);
+        }
+      };
+
+      // prologue: loads of virtual iterations -4..-1 (K(0..3), mask words of
+      // steps 0..3, V(0..1), all in block 0), then S(0)
+      int kv0 = __builtin_amdgcn_readfirstlane(c_kvb[0]);
+      int mn0 = DENSE ? __builtin_amdgcn_readfirstlane(c_mn[0]) : 0;
+      int kv1 = __builtin_amdgcn_readfirstlane(c_kvb[min(1, nb - 1)]);
+      int mn1 = DENSE ? __builtin_amdgcn_readfirstlane(c_mn[min(1, nb - 1)]) : 0;
+      int lab0 = __builtin_amdgcn_readfirstlane(c_lab[0]);
+      int lab1 = __builtin_amdgcn_readfirstlane(c_lab[min(1, nb - 1)]);
+      load_k(0, kv0, 0); load_m(0, mn0, 0);
+      load_k(1, kv0, 1); load_m(1, mn0, 1);
+      load_k(2, kv0, 2); load_m(2, mn0, 2); load_v(0, kv0, 0);
+      load_k(3, kv0, 3); load_m(3, mn0, 3); load_v(1, kv0, 1);
+      wait_at_most<kMaxInFlight>(count(-3) + count(-2) + count(-1));
+      lds_barrier();
+      wide_qk<D>(k_st[0], qf, lane, half, sc_a);
+      finish(sc_a, lab0, 0, kv0 * kBK);
+
+      // Trip j runs the four steps u = 4j + t of block j.  Step u:
+      //   top     wait for step u+1's K and mask words and step u-1's V
+      //           (issued three iterations ago), barrier, refill the stages
+      //           iteration u-1 finished with: K(u+4), mask(u+4), V(u+2);
+      //   body    QK(u+1) || softmax(u) || PV(u-1), straight-line;
+      //   finish  mask and base of S(u+1).
+      // Step 0's PV(-1) multiplies zero P, and step N-1's QK(N) reads a stale
+      // stage whose result is dropped, so all steps share one body.
+      for (int j = 0; j < nb; ++j) {
+        const bool more = j + 1 < nb;
+        // metadata of block j+2 / label of block j+2, for the next trip
+        const int kv2_v = c_kvb[min(j + 2, nb - 1)];
+        const int mn2_v = DENSE ? c_mn[min(j + 2, nb - 1)] : 0;
+        const int lab2_v = c_lab[min(j + 2, nb - 1)];
+#pragma unroll
+        for (int t = 0; t < kSteps; ++t) {
+          const int u = kSteps * j + t;
+          f32x16 *sc_cur = (t & 1) ? sc_b : sc_a;
+          f32x16 *sc_nxt = (t & 1) ? sc_a : sc_b;
+          bf16x8 (*pf_cur)[2] = (t & 1) ? pf_b : pf_a;
+          bf16x8 (*pf_prv)[2] = (t & 1) ? pf_a : pf_b;
+          // top
+          wait_at_most<kMaxInFlight>(count(u - 2) + count(u - 1));
+          lds_barrier();
+          if (more) {
+            load_k(t, kv1, t);
+            load_m(t, mn1, t);
+          }
+          if (t < 2) load_v(t + 2, kv0, t + 2);
+          else if (more) load_v(t - 2, kv1, t - 2);
+          // body, then the finish of S(u+1)
+          body(u, sc_cur, sc_nxt, pf_cur, pf_prv);
+          if (t < kSteps - 1) finish(sc_nxt, lab0, t + 1, kv0 * kBK + kSK * (t + 1));
+          else if (more) finish(sc_nxt, lab1, 0, kv1 * kBK);
+        }
+        kv0 = kv1;
+        mn0 = mn1;
+        lab0 = lab1;
+        kv1 = __builtin_amdgcn_readfirstlane(kv2_v);
+        mn1 = DENSE ? __builtin_amdgcn_readfirstlane(mn2_v) : 0;
+        lab1 = __builtin_amdgcn_readfirstlane(lab2_v);
+      }
+      // drain: PV(N-1); step N-1 = 4(nb-1) + 3 exponentiated into pf_b
+      wait_vmcnt<0>();
+      lds_barrier();
+      wide_pv<D>(v_st[(N - 1) % kStages], pf_b, lane, half, o);
+    }
+
+    // Workgroup-uniform decision: both waves run the same barriers below.
+    const int any_over = __syncthreads_or(rs.over ? 1 : 0);
+    if (attempt == 1 || any_over == 0) break;
+
+    // Rare: some row's scores outgrew its base.  Find every row's exact max
+    // (QK only, one stage at a time) and run the row again with it as base.
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) base_init[qs] = -INFINITY;
+    for (int s0 = 0; s0 < p.width; s0 += kWMeta) {
+      const int nb = compact(s0);
+      for (int u = 0; u < kSteps * nb; ++u) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        issue_stage<D, false>(k_st[0], k_res, key0(u), wave, lane);
+        if (has_bits) issue_mask(__builtin_amdgcn_readfirstlane(c_mn[u / kSteps]), u % kSteps, 0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        f32x16 sc[2];
+        wide_qk<D>(k_st[0], qf, lane, half, sc);
+        unsigned mw[2] = {0u, 0u};
+        if (label(u) == 1) {
+          if (has_bits) mask_words(0, mw);
+          wide_cap_mask<CAP, DENSE, true>(p, sc, key0(u), half, lo, hi, mw);
+        } else {
+          wide_cap_mask<CAP, DENSE, false>(p, sc, key0(u), half, lo, hi, mw);
+        }
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[qs][v]);
+          base_init[qs] = fmaxf(base_init[qs], pair_max(mx) * c2e);
+        }
+      }
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
+
+  // ---- epilogue: O / l, lse
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs) {
+    const int64_t q_row = q_row0 + 32 * qs;
+    const float l_tot = pair_sum(rs.l[qs]);
+    const bool has = l_tot > 0.f;
+    const float inv = has ? 1.f / l_tot : 0.f;
+    __bf16 *og = static_cast<__bf16 *>(p.out) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * dt + 8 * g + 4 * half;
+        union { __bf16 h[4]; u32x2 u; } pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk.h[e] = static_cast<__bf16>(o[dt][qs][4 * g + e] * inv);
+        *reinterpret_cast<u32x2 *>(og + col) = pk.u;
+      }
+    if (p.lse && half == 0) {
+      const float base = rs.base[qs] == -INFINITY ? 0.f : rs.base[qs];
+      p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] =
+          has ? (base + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int D, bool CAP, bool DENSE>
+hipError_t launch_wide(const FwdParams &p, hipStream_t stream) {
+  const int64_t blocks = p.B * p.Hq * p.nq;
+  hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE>), dim3(static_cast<unsigned>(blocks)), dim3(kWThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool CAP, bool DENSE>
 hipError_t launch_one(const FwdParams &p, hipStream_t stream) {
   const int64_t blocks = p.B * p.Hq * p.nq;
@@ -438,8 +1171,13 @@ hipError_t launch_one(const FwdParams &p, hipStream_t stream) {
 
 template <typename T, int D>
 hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
-  if (p.cap) return p.dense ? launch_one<T, D, true, true>(p, stream) : launch_one<T, D, true, false>(p, stream);
-  return p.dense ? launch_one<T, D, false, true>(p, stream) : launch_one<T, D, false, false>(p, stream);
+  if constexpr (sizeof(T) == 2) {
+    if (p.cap) return p.dense ? launch_wide<D, true, true>(p, stream) : launch_wide<D, true, false>(p, stream);
+    return p.dense ? launch_wide<D, false, true>(p, stream) : launch_wide<D, false, false>(p, stream);
+  } else {
+    if (p.cap) return p.dense ? launch_one<T, D, true, true>(p, stream) : launch_one<T, D, true, false>(p, stream);
+    return p.dense ? launch_one<T, D, false, true>(p, stream) : launch_one<T, D, false, false>(p, stream);
+  }
 }
 
 }  // namespace

@@ -16,7 +16,9 @@ struct FwdParams {
   int32_t group;          // Hq / Hkv
   int32_t nq, width, hm;  // MaskInfo grid: block rows, grid width W, mask heads
   const void *bm, *dn, *mn;           // device MaskInfo index arrays (downcast types)
-  const uint8_t *pmb;                 // device partial blocks (dense masks)
+  const uint8_t *pmb;                 // device partial blocks (dense masks), one byte per element
+  const uint32_t *pmb_bits;           // the same packed to 32-key words (see DeviceCopy), or null
+  int64_t pmb_bits_bytes;
   const int32_t *q_seq;               // device q_sequence (computable masks)
   const int32_t *row_order;           // device launch order of block rows
   int32_t bm_bytes, dn_bytes, mn_bytes;

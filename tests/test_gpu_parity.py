@@ -108,3 +108,39 @@ def test_repeat_calls_are_bitwise_identical():
     a = run_gpu(q, k, v, "local", left=300, right=0)
     b = run_gpu(q, k, v, "local", left=300, right=0)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _growing_scores(seed, B, H, S, D, a=31.0, b=31.0):
+    """q_i = a e0 (+ small noise), k_j = b (j / S) e0 (+ small noise): every
+    row's scores grow along the keys, so late rows end up more than 2^64 above
+    the max of their first allowed keys -- the kernel must fall back to its
+    exact-max recompute for them, while early rows stay on the fast path with
+    exponentials far above 1."""
+    q, k, v = synthetic.make_qkv(seed, B, H, H, S, S, D, D)
+    t = torch.arange(S, dtype=torch.float32) / S
+    q = (0.05 * q.float()).clone()
+    k = (0.05 * k.float()).clone()
+    q[..., 0] += a
+    k[..., 0] += b * t
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v
+
+
+@pytest.mark.parametrize("kind,kw,cap", [
+    ("causal", {}, None),
+    ("local", dict(left=300, right=40), None),
+    ("chunked", dict(chunk=384), 30.0),
+])
+def test_scores_outgrowing_first_block_base(kind, kw, cap):
+    q, k, v = _growing_scores(70, 1, 2, 768, 128)
+    o, l, _ = run_gpu(q, k, v, kind, cap=cap, **kw)
+    o_ref, l_ref = oracle_full(q, k, v, kind, cap=cap, **kw)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], f"growing_{kind}")
+
+
+def test_scores_outgrowing_base_dense_mask():
+    q, k, v = _growing_scores(71, 1, 2, 512, 128)
+    rng = np.random.default_rng(72)
+    dense = synthetic.random_dense_mask(rng, 1, 512, 512, 0.3, force_diagonal=True)
+    o, l, _ = run_gpu(q, k, v, "dense", dense=dense)
+    o_ref, l_ref = oracle_full(q, k, v, "dense", dense=dense)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], "growing_dense")
