@@ -589,6 +589,7 @@ __device__ __forceinline__ void wide_qk(const char *ks_lds, const bf16x8 (*qf)[D
 // computed again with its exact max as the base (found by a QK-only pass),
 // where every exponential is at most 1.
 constexpr float kOverflowSum = 18446744073709551616.f;   // 2^64
+constexpr float kUnderflowSum = 5.421010862427522e-20f;   // 2^-64
 
 struct RowState {
   float base[2];   // exponent base, base-2 units (-inf until the first allowed key)
@@ -832,9 +833,11 @@ void splash_fwd_wide(const FwdParams p) {
   RowState rs;
   float base_init[2] = {-INFINITY, -INFINITY};
 
-  // Exponent base of rows that have none yet: the step's max (after cap and
-  // mask; the cap is monotonic, so capping the max gives the max of the
-  // capped scores).  Rows whose keys are all masked so far keep -inf.
+  // Exponent base of rows that have none yet: the max of the chunk's first
+  // step (after cap and mask; the cap is monotonic, so capping the max gives
+  // the max of the capped scores), or 0 for a row whose keys in that step
+  // are all masked.  A base far from the row's true max only matters at the
+  // float range's ends, which the overflow and underflow tests catch.
   auto set_base = [&](const f32x16 *sc) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
@@ -849,7 +852,7 @@ void splash_fwd_wide(const FwdParams p) {
         const float th = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
         mx2 = x == -INFINITY ? -INFINITY : copysignf(th, x) * p.cap_out;
       }
-      rs.base[qs] = rs.base[qs] == -INFINITY ? mx2 : rs.base[qs];
+      rs.base[qs] = rs.base[qs] == -INFINITY ? (mx2 == -INFINITY ? 0.f : mx2) : rs.base[qs];
     }
   };
 
@@ -1004,22 +1007,15 @@ void splash_fwd_wide(const FwdParams p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) pf_b[qs][h] = bf16x8{};   // PV(-1) adds exact zeros
 
-      // Cap-free finishing of freshly formed scores S(u) (in sc): the mask of
-      // a label-1 step, and the exponent base of rows that have none.  Runs
-      // right after the QK that formed them, so the scores move from the
-      // accumulators to VGPRs once and stay there for the softmax.
-      // (The empty volatile asm statements keep the compiler from running the
-      // masking unconditionally and selecting the result.)
+      // Mask of freshly formed scores S(u) of a label-1 step, right after the
+      // QK that formed them.  (The empty volatile asm keeps the compiler from
+      // running the masking unconditionally and selecting the result.)
       auto finish = [&](f32x16 *sc, int lab, int stage, int key0) {
         if (lab == 1) {
           asm volatile("");
           unsigned mw[2] = {0u, 0u};
           mask_words(stage, mw);
           wide_cap_mask<false, DENSE, true>(p, sc, key0, half, lo, hi, mw);
-        }
-        if (__builtin_amdgcn_ballot_w64(rs.base[0] == -INFINITY || rs.base[1] == -INFINITY) != 0) {
-          asm volatile("");
-          set_base(sc);
         }
       };
 
@@ -1039,6 +1035,7 @@ void splash_fwd_wide(const FwdParams p) {
       lds_barrier();
       wide_qk<D>(k_st[0], qf, lane, half, sc_a);
       finish(sc_a, lab0, 0, kv0 * kBK);
+      if (__builtin_amdgcn_ballot_w64(rs.base[0] == -INFINITY || rs.base[1] == -INFINITY) != 0) set_base(sc_a);
 
       // Trip j runs the four steps u = 4j + t of block j.  Step u:
       //   top     wait for step u+1's K and mask words and step u-1's V
@@ -1088,7 +1085,11 @@ void splash_fwd_wide(const FwdParams p) {
       wide_pv<D>(v_st[(N - 1) % kStages], pf_b, lane, half, o);
     }
 
-    // Workgroup-uniform decision: both waves run the same barriers below.
+    // Rows whose sum is tiny had a base far above their max (or no allowed
+    // key at all); they join the recompute too, where the exact max is the
+    // base.  Workgroup-uniform decision: both waves run the same barriers.
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) rs.over |= attempt == 0 && pair_sum(rs.l[qs]) < kUnderflowSum;
     const int any_over = __syncthreads_or(rs.over ? 1 : 0);
     if (attempt == 1 || any_over == 0) break;
 
