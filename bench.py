@@ -213,7 +213,8 @@ def main():
         "mask_compile_ms": round(mask_ms, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "splash_fwd_kernel", "flops_per_launch": flops,
+                     "kernel": "splash_fwd_wide" if w.dtype == "bf16" else "splash_fwd_kernel",
+                     "flops_per_launch": flops,
                      "kernel_ms_avg": round(kern_avg, 5)},
         "cpu_baseline": None,
     }
