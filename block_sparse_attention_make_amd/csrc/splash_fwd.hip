@@ -562,6 +562,28 @@ __device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, 
 #pragma clang diagnostic pop
 }
 
+// One QK matrix instruction of the pipelined body, issued from inline
+// assembly so its accumulator lives in VGPRs (where the softmax reads it) and
+// its Q operand in AGPRs: left to itself the compiler keeps every MFMA
+// accumulator in AGPRs and moves each score to VGPRs before the softmax.
+// The compiler does not see this instruction's latency, so a VALU read of
+// the accumulator must come at least kQkMfmaDrain cycles later (see
+// qk_drain); the pipeline only reads it a whole step later, or after
+// qk_drain.  A k-step that starts a tile writes the accumulator without
+// reading it (C = 0) and must not share registers with its inputs.
+__device__ __forceinline__ void qk_mfma(f32x16 &acc, const bf16x8 &a, const bf16x8 &q, bool first) {
+  if (first)
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(q));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(q));
+}
+
+// Wait states covering the result latency of the last qk_mfma before its
+// accumulator is read by VALU instructions (16 passes, generously).
+__device__ __forceinline__ void qk_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+}
+
 // S^T for one 32-key step: sc[qs] holds, for this lane's row of half qs, keys
 // 8(v/4) + 4 half + v%4 of the step.
 template <int D>
@@ -746,8 +768,12 @@ void splash_fwd_wide(const FwdParams p) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks)
-        qf[qs][ks] = *reinterpret_cast<const bf16x8 *>(qg + static_cast<int64_t>(32 * qs) * D + 16 * ks + 8 * half);
+      for (int ks = 0; ks < kKS; ++ks) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(qg + static_cast<int64_t>(32 * qs) * D + 16 * ks + 8 * half);
+        // Q lives in AGPRs for the whole kernel: the QK instructions read it
+        // from there, which leaves the VGPRs to the scores and P.
+        asm volatile("" : "=a"(qf[qs][ks]) : "0"(x));
+      }
   }
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
@@ -890,13 +916,11 @@ void splash_fwd_wide(const FwdParams p) {
       __builtin_memcpy(&r, both, 16);
       return r;
     };
-    const f32x16 zero16 = {};
     bf16x8 ka[kKS], va[kPVOps];
     auto mfma_slice = [&](int i) {   // QK k-step i, PV operand i
       if (i < kKS) {
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-          sc_nxt[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[qs][i], i == 0 ? zero16 : sc_nxt[qs], 0, 0, 0);
+        for (int qs = 0; qs < 2; ++qs) qk_mfma(sc_nxt[qs], ka[i], qf[qs][i], i == 0);
       }
       if (i < kPVOps) {
         const int h = i / kDT, dt = i % kDT;
@@ -1012,7 +1036,7 @@ void splash_fwd_wide(const FwdParams p) {
       // running the masking unconditionally and selecting the result.)
       auto finish = [&](f32x16 *sc, int lab, int stage, int key0) {
         if (lab == 1) {
-          asm volatile("");
+          qk_drain();   // the scores were formed by the step that just ended
           unsigned mw[2] = {0u, 0u};
           mask_words(stage, mw);
           wide_cap_mask<false, DENSE, true>(p, sc, key0, half, lo, hi, mw);
