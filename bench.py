@@ -110,7 +110,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU's clock settles only after ~100 ms of sustained load, so the default warm-up is long.
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="causal_mha_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
