@@ -562,6 +562,25 @@ __device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, 
 #pragma clang diagnostic pop
 }
 
+// One segment (1 KiB, segment I of this wave's share) of a stage, for
+// spreading a stage's loads over several slices of a step.
+template <int D, bool IS_V, int I>
+__device__ __forceinline__ void issue_seg(char *lds, i32x4 res, int64_t row0, int wave, int lane) {
+  using SG = Stage<D>;
+  static_assert(I < SG::kInsts, "segment index");
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) char *)(lds + wave * SG::kInsts * 1024)));
+  const uint32_t soff = static_cast<uint32_t>(row0 * SG::kRowBytes) + wave * SG::kInsts * 1024;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds"
+      :: "s"(m0), "v"(stage_voff<D, IS_V>(wave, lane, I)), "s"(res), "s"(soff), "n"(I * 1024)
+      : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // One QK matrix instruction of the pipelined body, issued from inline
 // assembly so its accumulator lives in VGPRs (where the softmax reads it) and
 // its Q operand in AGPRs: left to itself the compiler keeps every MFMA
@@ -590,24 +609,24 @@ template <int D>
 __device__ __forceinline__ void wide_qk(const char *ks_lds, const bf16x8 (*qf)[D / 16], int lane, int half,
                                         f32x16 *sc) {
   using SG = Stage<D>;
-  const f32x16 zero16 = {};
   const int row = lane & 31;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
         ks_lds + row * SG::kRowBytes + (((2 * ks + half) ^ SG::swz_k(row)) * 16));
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-      sc[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qs][ks], ks == 0 ? zero16 : sc[qs], 0, 0, 0);
+    for (int qs = 0; qs < 2; ++qs) qk_mfma(sc[qs], a, qf[qs][ks], ks == 0);
   }
+  qk_drain();   // callers read the scores right away
 }
 
 // Per-row softmax state of the wide kernel.  The exponent base of a row is
 // fixed by its first step with an allowed key and never moves afterwards, so
 // the accumulator is never rescaled inside the loop: exponentials of later,
 // larger scores simply exceed 1.  That is exact as long as they stay far
-// from the float range.  A step whose exponentials of one row sum to more
-// than 2^64 (so some exceeded 2^59) raises `over`, and the whole row is then
+// from the float range.  A row whose exponentials sum to more than 2^64 in
+// the end (the sum only grows, so no term ever exceeded it; an overflow to
+// +inf shows up the same way) raises `over`, and the whole row is then
 // computed again with its exact max as the base (found by a QK-only pass),
 // where every exponential is at most 1.
 constexpr float kOverflowSum = 18446744073709551616.f;   // 2^64
@@ -616,7 +635,7 @@ constexpr float kUnderflowSum = 5.421010862427522e-20f;   // 2^-64
 struct RowState {
   float base[2];   // exponent base, base-2 units (-inf until the first allowed key)
   float l[2];      // this lane's share of the running sum
-  bool over;       // some step's sum exceeded kOverflowSum
+  bool over;       // the row needs the exact-max recompute
 };
 
 // Scores of one step -> capped (base-2 units), masked.  MASK: label-1 step.
@@ -889,9 +908,9 @@ void splash_fwd_wide(const FwdParams p) {
   // half), so every matrix instruction has a little VALU work to hide under
   // and no operand lives longer than a few slices.  The softmax runs against
   // the row's fixed base; the step's row sums come from dot products of the
-  // bf16 exponentials with ones (the same rounded values PV multiplies) and
-  // double as the overflow test.
-  auto body = [&](int u, f32x16 *sc_cur, f32x16 *sc_nxt, bf16x8 (*pf_cur)[2], bf16x8 (*pf_prv)[2]) {
+  // bf16 exponentials with ones (the same rounded values PV multiplies).
+  auto body = [&](int u, f32x16 *sc_cur, f32x16 *sc_nxt, bf16x8 (*pf_cur)[2], bf16x8 (*pf_prv)[2],
+                  auto &&issue_loads) {
     constexpr int kPVOps = 2 * kDT;       // PV A operands per step: (h, dt)
     const char *kst = k_st[(u + 1) % kStages];
     const char *vst = v_st[(u + kStages - 1) % kStages];
@@ -959,6 +978,7 @@ void splash_fwd_wide(const FwdParams p) {
       pf_cur[qs][h][e0 + 3] = p23[1];
       sum[qs] = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, sum[qs], false);
       sum[qs] = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, sum[qs], false);
+      asm volatile("" : "+v"(sum[qs]));   // keep the sums in this slice
     };
 
     // slice 0: operands of MFMA slices 0 and 1
@@ -970,16 +990,14 @@ void splash_fwd_wide(const FwdParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i + 2 < 8) reads_slice(i + 2);
+      issue_loads(i);
       mfma_slice(i);
       exps(i);
       __builtin_amdgcn_sched_barrier(0);
     }
     static_assert(kKS <= 8 && kPVOps <= 8, "slice plan assumes at most 8 operands");
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      rs.l[qs] += sum[qs];
-      rs.over |= sum[qs] > kOverflowSum;
-    }
+    for (int qs = 0; qs < 2; ++qs) rs.l[qs] += sum[qs];
     // Keep this step's softmax results here: without a use in this block
     // the compiler sinks the exponentials into the next step, after its
     // branches, where they no longer overlap these MFMAs.
@@ -1008,11 +1026,13 @@ void splash_fwd_wide(const FwdParams p) {
       if (nb == 0) continue;
       const int N = kSteps * nb;   // pipeline steps
 
-      // Loads of (virtual) iteration w: K(w+4), V(w+2) and, for dense masks,
-      // the mask words of step w+4 -- those that exist.  Counted per wave.
+      // Loads of (virtual) iteration w, counted per wave: K(w+4) with, for
+      // dense masks, the mask words of step w+4, and V(w+2).  Iterations
+      // -4 and -3 of the prologue issue K only; from -2 on every iteration
+      // issues both (in the last block, whose successors do not exist, they
+      // load the block's own K and V again into stages it has finished with).
       auto count = [&](int w) -> int {
-        return (w + 4 >= 0 && w + 4 < N ? SG::kInsts + (has_bits ? 1 : 0) : 0) +
-               (w + 2 >= 0 && w + 2 < N ? SG::kInsts : 0);
+        return SG::kInsts + (has_bits ? 1 : 0) + (w >= -2 ? SG::kInsts : 0);
       };
       auto load_k = [&](int stage, int kv, int t) {
         issue_stage<D, false>(k_st[stage], k_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane);
@@ -1022,6 +1042,37 @@ void splash_fwd_wide(const FwdParams p) {
       };
       auto load_m = [&](int stage, int mn, int t) {
         if (has_bits) issue_mask(mn, t, stage);
+      };
+      // Half h of this wave's segments of a K or V stage.
+      auto load_k_half = [&](int h, int stage, int kv, int t) {
+        const int64_t r0 = static_cast<int64_t>(kv) * kBK + kSK * t;
+        if constexpr (SG::kInsts == 4) {
+          if (h == 0) {
+            issue_seg<D, false, 0>(k_st[stage], k_res, r0, wave, lane);
+            issue_seg<D, false, 1>(k_st[stage], k_res, r0, wave, lane);
+          } else {
+            issue_seg<D, false, 2>(k_st[stage], k_res, r0, wave, lane);
+            issue_seg<D, false, 3>(k_st[stage], k_res, r0, wave, lane);
+          }
+        } else {
+          if (h == 0) issue_seg<D, false, 0>(k_st[stage], k_res, r0, wave, lane);
+          else issue_seg<D, false, 1>(k_st[stage], k_res, r0, wave, lane);
+        }
+      };
+      auto load_v_half = [&](int h, int stage, int kv, int t) {
+        const int64_t r0 = static_cast<int64_t>(kv) * kBK + kSK * t;
+        if constexpr (SG::kInsts == 4) {
+          if (h == 0) {
+            issue_seg<D, true, 0>(v_st[stage], v_res, r0, wave, lane);
+            issue_seg<D, true, 1>(v_st[stage], v_res, r0, wave, lane);
+          } else {
+            issue_seg<D, true, 2>(v_st[stage], v_res, r0, wave, lane);
+            issue_seg<D, true, 3>(v_st[stage], v_res, r0, wave, lane);
+          }
+        } else {
+          if (h == 0) issue_seg<D, true, 0>(v_st[stage], v_res, r0, wave, lane);
+          else issue_seg<D, true, 1>(v_st[stage], v_res, r0, wave, lane);
+        }
       };
 
       f32x16 sc_a[2], sc_b[2];         // scores: step being exponentiated / step being formed
@@ -1085,14 +1136,19 @@ void splash_fwd_wide(const FwdParams p) {
           // top
           wait_at_most<kMaxInFlight>(count(u - 2) + count(u - 1));
           lds_barrier();
-          if (more) {
-            load_k(t, kv1, t);
-            load_m(t, mn1, t);
-          }
-          if (t < 2) load_v(t + 2, kv0, t + 2);
-          else if (more) load_v(t - 2, kv1, t - 2);
-          // body, then the finish of S(u+1)
-          body(u, sc_cur, sc_nxt, pf_cur, pf_prv);
+          // refills of the stages step u-1 finished with, spread over the
+          // first four slices: K(u+4) and its mask words, then V(u+2)
+          auto refill = [&](int i) {
+            if (i < 2) {
+              load_k_half(i, t, kv1, t);
+              if (i == 0) load_m(t, mn1, t);
+            } else if (i < 4) {
+              if (t < 2) load_v_half(i - 2, t + 2, kv0, t + 2);
+              else load_v_half(i - 2, t - 2, kv1, t - 2);
+            }
+          };
+          // body (with the refills), then the finish of S(u+1)
+          body(u, sc_cur, sc_nxt, pf_cur, pf_prv, refill);
           if (t < kSteps - 1) finish(sc_nxt, lab0, t + 1, kv0 * kBK + kSK * (t + 1));
           else if (more) finish(sc_nxt, lab1, 0, kv1 * kBK);
         }
@@ -1109,11 +1165,15 @@ void splash_fwd_wide(const FwdParams p) {
       wide_pv<D>(v_st[(N - 1) % kStages], pf_b, lane, half, o);
     }
 
-    // Rows whose sum is tiny had a base far above their max (or no allowed
-    // key at all); they join the recompute too, where the exact max is the
-    // base.  Workgroup-uniform decision: both waves run the same barriers.
+    // Rows whose sum outgrew kOverflowSum had a base far below their max;
+    // rows whose sum is tiny had a base far above it (or no allowed key at
+    // all).  Both run again with the exact max as base.  Workgroup-uniform
+    // decision: both waves run the same barriers.
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) rs.over |= attempt == 0 && pair_sum(rs.l[qs]) < kUnderflowSum;
+    for (int qs = 0; qs < 2; ++qs) {
+      const float l_tot = pair_sum(rs.l[qs]);
+      rs.over |= attempt == 0 && (l_tot < kUnderflowSum || !(l_tot <= kOverflowSum));
+    }
     const int any_over = __syncthreads_or(rs.over ? 1 : 0);
     if (attempt == 1 || any_over == 0) break;
 
