@@ -22,12 +22,26 @@ combined as max + log(sum)).
 
 GQA/MQA: query head h reads key/value head h // (Hq // Hkv).
 Mask heads: Hm == 1 is shared by every query head; Hm == Hq is per head.
+
+Attention sinks (softmax_aux of the EasyDeL BlockSparseAttn.forward_native
+signature, typed [num_kv_heads, num_sinks] or [num_sinks]): the pages give
+the argument, not its arithmetic.  The reading taken is the usual one: each
+sink logit a_k is one more column of the softmax that carries no value, so
+
+  lse_i = ln( sum_{allowed j} exp(s_ij) + sum_k exp(a_k) ),
+  o_i   = sum_{allowed j} exp(s_ij - lse_i) v_j,
+
+unscaled and uncapped (the logits are given as they enter the softmax).  A
+[num_kv_heads, ns] array gives query head h the row of its key/value head
+h // (Hq // Hkv); a [Hq, ns] array one row per query head; [ns] is shared.
+A row with no allowed key then has o_i = 0 and lse_i = ln sum_k exp(a_k).
 """
 import numpy as np
 
 
-def attention_rows(q, k, v, allowed, scale=None, soft_cap=None):
-    """One (batch, head): q [n, D], k [Skv, D], v [Skv, Dv], allowed [n, Skv] bool.
+def attention_rows(q, k, v, allowed, scale=None, soft_cap=None, sinks=None):
+    """One (batch, head): q [n, D], k [Skv, D], v [Skv, Dv], allowed [n, Skv] bool;
+    sinks: this head's sink logits [ns] or None.
 
     Returns (o [n, Dv] float64, lse [n] float64).
     """
@@ -40,6 +54,11 @@ def attention_rows(q, k, v, allowed, scale=None, soft_cap=None):
     if soft_cap is not None:
         s = soft_cap * np.tanh(s / soft_cap)
     s = np.where(allowed, s, -np.inf)
+    if sinks is not None and len(sinks):
+        # the sinks are extra softmax columns whose value rows are zero
+        a = np.broadcast_to(np.asarray(sinks, dtype=np.float64), (s.shape[0], len(sinks)))
+        s = np.concatenate([s, a], axis=1)
+        v = np.concatenate([v, np.zeros((len(sinks), v.shape[1]))], axis=0)
     m = s.max(axis=1)
     has = np.isfinite(m)
     m_safe = np.where(has, m, 0.0)
@@ -51,7 +70,21 @@ def attention_rows(q, k, v, allowed, scale=None, soft_cap=None):
     return o, lse
 
 
-def attention(q, k, v, mask_rows, scale=None, soft_cap=None, row_chunk=512):
+def sink_row(softmax_aux, h, hq, hkv):
+    """Sink logits of query head h, or None (see the module docstring)."""
+    if softmax_aux is None:
+        return None
+    a = np.asarray(softmax_aux, dtype=np.float64)
+    if a.ndim == 1:
+        return a
+    if a.shape[0] == hkv:
+        return a[h // (hq // hkv)]
+    if a.shape[0] == hq:
+        return a[h]
+    raise ValueError("softmax_aux must be [ns], [Hkv, ns] or [Hq, ns]")
+
+
+def attention(q, k, v, mask_rows, scale=None, soft_cap=None, row_chunk=512, softmax_aux=None):
     """Full attention.
 
     q [B, Hq, Sq, D], k [B, Hkv, Skv, D], v [B, Hkv, Skv, Dv] (any float type,
@@ -75,13 +108,14 @@ def attention(q, k, v, mask_rows, scale=None, soft_cap=None, row_chunk=512):
             vv = np.asarray(v[b, h // group], dtype=np.float64)
             for i0 in range(0, sq, row_chunk):
                 rows = np.arange(i0, min(sq, i0 + row_chunk))
-                ob, lb = attention_rows(q[b, h, rows], kk, vv, mask_rows(h, rows), scale, soft_cap)
+                ob, lb = attention_rows(q[b, h, rows], kk, vv, mask_rows(h, rows), scale, soft_cap,
+                                        sink_row(softmax_aux, h, hq, hkv))
                 o[b, h, rows] = ob
                 lse[b, h, rows] = lb
     return o, lse
 
 
-def attention_sampled(q, k, v, mask_rows, samples, scale=None, soft_cap=None):
+def attention_sampled(q, k, v, mask_rows, samples, scale=None, soft_cap=None, softmax_aux=None):
     """Selected output rows only: samples = iterable of (b, h, i).
 
     Returns (o [n, Dv], lse [n]) in the order given.  Used at full workload
@@ -92,7 +126,8 @@ def attention_sampled(q, k, v, mask_rows, samples, scale=None, soft_cap=None):
     outs, lses = [], []
     for b, h, i in samples:
         ob, lb = attention_rows(q[b, h, [i]], k[b, h // group], v[b, h // group],
-                                mask_rows(h, np.array([i])), scale, soft_cap)
+                                mask_rows(h, np.array([i])), scale, soft_cap,
+                                sink_row(softmax_aux, h, hq, hkv))
         outs.append(ob[0])
         lses.append(lb[0])
     return np.stack(outs), np.array(lses)

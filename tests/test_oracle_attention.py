@@ -192,3 +192,82 @@ def test_sampled_rows_equal_full():
         # one row vs a block of rows: only the BLAS summation order differs
         np.testing.assert_allclose(os_[n], o[b, h, i], rtol=0, atol=1e-14)
         assert abs(ls_[n] - lse[b, h, i]) < 1e-14
+
+
+# ---- attention sinks (softmax_aux) ----
+
+def test_sinks_zero_query_closed_form():
+    """q = 0: every allowed score is 0, so with n allowed keys and sink logits
+    a_k the denominator is n + sum_k e^(a_k); o_i is the mean of the allowed
+    v_j scaled by n / (n + sum e^a) and lse_i = ln(n + sum e^a)."""
+    rng = np.random.default_rng(11)
+    sq = 13
+    q = np.zeros((1, 1, sq, 8))
+    k, v = _rand(rng, 1, 1, sq, 8), _rand(rng, 1, 1, sq, 6)
+    m = omasks.materialize("causal", sq, sq)
+    sinks = np.array([0.7, -1.3])
+    o, lse = oatt.attention(q, k, v, _rows_fn(m), softmax_aux=sinks)
+    extra = math.exp(0.7) + math.exp(-1.3)
+    for i in range(sq):
+        n = i + 1
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, :n].mean(axis=0) * n / (n + extra), rtol=0, atol=1e-13)
+        assert abs(lse[0, 0, i] - math.log(n + extra)) < 1e-13
+
+
+def test_sinks_equal_torch_sdpa_with_extra_zero_value_keys():
+    """A sink is a softmax column with logit a_k and a zero value row: SDPA on
+    keys extended by zero vectors, with the logit supplied as an additive
+    bias (scaled zero score + a_k), must agree.  Per-kv-head sink rows with
+    GQA check that query head h takes row h // G."""
+    rng = np.random.default_rng(12)
+    hq, hkv, sq, skv, d = 4, 2, 9, 11, 8
+    q, k, v = _rand(rng, 1, hq, sq, d), _rand(rng, 1, hkv, skv, d), _rand(rng, 1, hkv, skv, d)
+    m = rng.random((1, sq, skv)) < 0.6
+    m[:, :, 0] = True
+    aux = rng.standard_normal((hkv, 3))
+    o, lse = oatt.attention(q, k, v, _rows_fn(m), softmax_aux=aux)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        kk = np.concatenate([k[0, g], np.zeros((3, d))])
+        vv = np.concatenate([v[0, g], np.zeros((3, d))])
+        bias = np.concatenate([np.where(m[0], 0.0, -np.inf), np.broadcast_to(aux[g], (sq, 3))], axis=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[0, h])[None], torch.from_numpy(kk)[None], torch.from_numpy(vv)[None],
+            attn_mask=torch.from_numpy(bias)[None]).numpy()[0]
+        np.testing.assert_allclose(o[0, h], ref, rtol=0, atol=1e-12)
+        s = (q[0, h] @ kk.T) * d ** -0.5 + bias
+        np.testing.assert_allclose(lse[0, h], torch.logsumexp(torch.from_numpy(s), dim=-1).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_sinks_minus_inf_and_per_query_head_rows():
+    """A sink of logit -inf adds e^(-inf) = 0: the result equals no sinks.  A
+    [Hq, ns] array gives each query head its own row."""
+    rng = np.random.default_rng(13)
+    q, k, v = _rand(rng, 1, 3, 7, 8), _rand(rng, 1, 1, 7, 8), _rand(rng, 1, 1, 7, 8)
+    m = omasks.materialize("causal", 7, 7)
+    o0, l0 = oatt.attention(q, k, v, _rows_fn(m))
+    o1, l1 = oatt.attention(q, k, v, _rows_fn(m), softmax_aux=np.array([-np.inf]))
+    # (the product with one more, zero, value row may round differently by an ulp)
+    np.testing.assert_allclose(o0, o1, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(l0, l1)
+    aux = np.array([[0.5], [-np.inf], [2.0]])
+    o2, l2 = oatt.attention(q, k, v, _rows_fn(m), softmax_aux=aux)
+    np.testing.assert_allclose(o2[:, 1], o0[:, 1], rtol=0, atol=1e-15)
+    for h in (0, 2):
+        # one sink a scales the weights by e^lse0 / (e^lse0 + e^a)
+        f = np.exp(l0[:, h]) / (np.exp(l0[:, h]) + math.exp(aux[h, 0]))
+        np.testing.assert_allclose(o2[:, h], o0[:, h] * f[..., None], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l2[:, h], np.logaddexp(l0[:, h], aux[h, 0]), rtol=0, atol=1e-13)
+
+
+def test_sinks_on_row_without_allowed_keys():
+    """No allowed key: o_i = 0 and lse_i is the log-sum-exp of the sinks alone."""
+    rng = np.random.default_rng(14)
+    q, k, v = _rand(rng, 1, 1, 4, 8), _rand(rng, 1, 1, 6, 8), _rand(rng, 1, 1, 6, 8)
+    m = np.ones((1, 4, 6), dtype=bool)
+    m[0, 2] = False
+    o, lse = oatt.attention(q, k, v, _rows_fn(m), softmax_aux=np.array([1.0, 2.0]))
+    np.testing.assert_array_equal(o[0, 0, 2], np.zeros(8))
+    assert abs(lse[0, 0, 2] - np.logaddexp(1.0, 2.0)) < 1e-15
+    assert np.all(np.abs(o[0, 0, [0, 1, 3]]) > 0)
