@@ -159,13 +159,13 @@ extern "C" SPLASH_API splash_status splash_mask_info_read_device(const splash_ma
   return SPLASH_OK;
 }
 
-extern "C" SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void *q, const void *k,
-                                               const void *v, void *out, float *lse, int64_t B,
-                                               int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
-                                               int64_t D, int64_t Dv, int32_t dtype,
-                                               float softmax_scale, float logits_soft_cap,
-                                               void *hip_stream) {
-  clear_error();
+namespace {
+
+splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const void *v, void *out,
+                       float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                       int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
+                       float logits_soft_cap, const float *aux, int32_t aux_heads,
+                       int32_t num_sinks, void *hip_stream) {
   // ---- validation: nothing below launches or allocates until all passes ----
   if (!mi) return fail(SPLASH_EINVAL, "MaskInfo is NULL");
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || D <= 0 || Dv <= 0)
@@ -183,6 +183,13 @@ extern "C" SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void 
     return fail(SPLASH_EUNSUPPORTED, "the forward kernel runs 128 x 128 MaskInfo blocks");
   if (D != Dv || (D != 64 && D != 128))
     return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
+  if (num_sinks < 0) return fail(SPLASH_EINVAL, "num_sinks must be >= 0");
+  if (num_sinks > 0) {
+    if (!aux) return fail(SPLASH_EINVAL, "softmax_aux is NULL with num_sinks > 0");
+    if (aux_heads != 1 && aux_heads != Hkv && aux_heads != Hq)
+      return fail(SPLASH_EINVAL, "softmax_aux must have 1, Hkv or Hq rows");
+    if (reinterpret_cast<uintptr_t>(aux) % 4 != 0) return fail(SPLASH_EINVAL, "softmax_aux must be 4-byte aligned");
+  }
   if (B == 0 || Hq == 0 || Sq == 0) return SPLASH_OK;
   if (!q || !out || (Skv > 0 && (!k || !v)))
     return fail(SPLASH_EINVAL, "NULL tensor pointer");
@@ -239,8 +246,36 @@ extern "C" SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void 
   p.c2 = cap ? static_cast<float>(static_cast<double>(scale) / logits_soft_cap)
              : static_cast<float>(scale * log2e);
   p.cap_out = cap ? static_cast<float>(logits_soft_cap * log2e) : 0.f;
+  p.aux = num_sinks > 0 ? aux : nullptr;
+  p.aux_heads = num_sinks > 0 ? aux_heads : 0;
+  p.num_sinks = num_sinks;
 
   hipError_t e = launch_fwd(p, dtype, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return SPLASH_OK;
+}
+
+}  // namespace
+
+extern "C" SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void *q, const void *k,
+                                               const void *v, void *out, float *lse, int64_t B,
+                                               int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                                               int64_t D, int64_t Dv, int32_t dtype,
+                                               float softmax_scale, float logits_soft_cap,
+                                               void *hip_stream) {
+  clear_error();
+  return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale,
+                  logits_soft_cap, nullptr, 0, 0, hip_stream);
+}
+
+extern "C" SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const void *q, const void *k,
+                                                     const void *v, void *out, float *lse, int64_t B,
+                                                     int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                                                     int64_t D, int64_t Dv, int32_t dtype,
+                                                     float softmax_scale, float logits_soft_cap,
+                                                     const float *softmax_aux, int32_t aux_heads,
+                                                     int32_t num_sinks, void *hip_stream) {
+  clear_error();
+  return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale,
+                  logits_soft_cap, softmax_aux, aux_heads, num_sinks, hip_stream);
 }

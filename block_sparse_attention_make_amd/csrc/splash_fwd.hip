@@ -47,6 +47,43 @@ constexpr int kMetaChunk = 256; // grid positions of metadata staged in LDS at a
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Attention sinks (softmax_aux of the EasyDeL BlockSparseAttn.forward_native
+// signature): logits that join the softmax denominator of every row of a
+// head and carry no value.  Returns log2 of the sum of e^(a_k) over the sink
+// logits of query head hq, or -inf without sinks.  Uniform per workgroup.
+__device__ __forceinline__ float sink_lse2(const FwdParams &p, int hq) {
+  if (p.aux == nullptr || p.num_sinks <= 0) return -INFINITY;
+  const int row = p.aux_heads == 1 ? 0 : (p.aux_heads == static_cast<int>(p.Hq) ? hq : hq / p.group);
+  const float *a = p.aux + static_cast<int64_t>(row) * p.num_sinks;
+  float mx = -INFINITY;
+  for (int k = 0; k < p.num_sinks; ++k) mx = fmaxf(mx, a[k]);
+  if (mx == -INFINITY) return -INFINITY;
+  float sum = 0.f;
+  for (int k = 0; k < p.num_sinks; ++k) sum += __builtin_amdgcn_exp2f((a[k] - mx) * kLog2e);
+  return mx * kLog2e + __builtin_amdgcn_logf(sum);
+}
+
+// Final normalisation of one row from its sum l_tot of exponentials taken
+// against base2 (log2 units) and the sinks' log2-sum sl2: the factor that
+// turns the accumulated numerator into the output, and the natural-log lse.
+// Without sinks: 1 / l_tot and (base2 + log2 l_tot) ln 2.  With sinks the
+// row's own log-sum L and the sinks' S combine as T = log2(2^L + 2^S), and
+// the output is scaled by 2^(L - T) / l_tot.  A row with no allowed key has
+// output 0 and lse = S (-inf without sinks).
+__device__ __forceinline__ void row_finish(float l_tot, float base2, float sl2, float &inv, float &lse) {
+  const bool has = l_tot > 0.f;
+  const float l2 = has ? base2 + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+  if (sl2 == -INFINITY) {
+    inv = has ? 1.f / l_tot : 0.f;
+    lse = has ? l2 * kLn2 : -INFINITY;
+    return;
+  }
+  const float mx = fmaxf(l2, sl2);
+  const float t2 = mx + __builtin_amdgcn_logf(__builtin_amdgcn_exp2f(l2 - mx) + __builtin_amdgcn_exp2f(sl2 - mx));
+  inv = has ? __builtin_amdgcn_exp2f(l2 - t2) / l_tot : 0.f;
+  lse = t2 * kLn2;
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -400,8 +437,11 @@ void splash_fwd_kernel(const FwdParams p) {
 
   // ---- epilogue: O / l, lse ----
   const float l_tot = pair_sum(l_run);
-  const bool has = l_tot > 0.f;
-  const float inv = has ? 1.f / l_tot : 0.f;
+  float inv, lse_row;
+  {
+    const float m_fin = m_run == -INFINITY ? 0.f : m_run;
+    row_finish(l_tot, m_fin * (CAP ? 1.f : c2), sink_lse2(p, hq), inv, lse_row);
+  }
   T *og = static_cast<T *>(p.out) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
@@ -420,12 +460,7 @@ void splash_fwd_kernel(const FwdParams p) {
         *reinterpret_cast<float4 *>(og + col) = x;
       }
     }
-  if (p.lse && half == 0) {
-    const float m_fin = m_run == -INFINITY ? 0.f : m_run;
-    const float cfin = CAP ? 1.f : c2;
-    p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] =
-        has ? (m_fin * cfin + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-  }
+  if (p.lse && half == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] = lse_row;
 }
 
 // ===========================================================================
@@ -446,9 +481,9 @@ void splash_fwd_kernel(const FwdParams p) {
 // Workgroup: two waves = 128 query rows = one mask block row; two workgroups
 // share a CU.  K and V arrive in LDS through direct-to-LDS loads (no VGPRs),
 // 32 keys per stage, four stages each.  The loads of K(u+4) and V(u+2) are
-// issued at the top of iteration u into the stages iteration u-1 finished
-// reading; step u+1's K and step u-1's V must have landed by the top of
-// iteration u, so each load has three iterations to arrive.
+// issued during the first slices of iteration u into the stages iteration
+// u-1 finished reading; step u+1's K and step u-1's V must have landed by the
+// top of iteration u, so each load has about three iterations to arrive.
 constexpr int kWWaves = 2;
 constexpr int kWThreads = 64 * kWWaves;
 constexpr int kSK = 32;            // keys per pipeline step
@@ -1114,10 +1149,11 @@ void splash_fwd_wide(const FwdParams p) {
 
       // Trip j runs the four steps u = 4j + t of block j.  Step u:
       //   top     wait for step u+1's K and mask words and step u-1's V
-      //           (issued three iterations ago), barrier, refill the stages
-      //           iteration u-1 finished with: K(u+4), mask(u+4), V(u+2);
-      //   body    QK(u+1) || softmax(u) || PV(u-1), straight-line;
-      //   finish  mask and base of S(u+1).
+      //           (issued three iterations ago), barrier;
+      //   body    QK(u+1) || softmax(u) || PV(u-1), straight-line, with the
+      //           refills of the stages iteration u-1 finished with --
+      //           K(u+4), mask(u+4), V(u+2) -- in its first four slices;
+      //   finish  mask of S(u+1).
       // Step 0's PV(-1) multiplies zero P, and step N-1's QK(N) reads a stale
       // stage whose result is dropped, so all steps share one body.
       for (int j = 0; j < nb; ++j) {
@@ -1213,12 +1249,13 @@ void splash_fwd_wide(const FwdParams p) {
   }
 
   // ---- epilogue: O / l, lse
+  const float sl2 = sink_lse2(p, hq);
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
     const int64_t q_row = q_row0 + 32 * qs;
     const float l_tot = pair_sum(rs.l[qs]);
-    const bool has = l_tot > 0.f;
-    const float inv = has ? 1.f / l_tot : 0.f;
+    float inv, lse_row;
+    row_finish(l_tot, rs.base[qs] == -INFINITY ? 0.f : rs.base[qs], sl2, inv, lse_row);
     __bf16 *og = static_cast<__bf16 *>(p.out) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
@@ -1230,11 +1267,7 @@ void splash_fwd_wide(const FwdParams p) {
         for (int e = 0; e < 4; ++e) pk.h[e] = static_cast<__bf16>(o[dt][qs][4 * g + e] * inv);
         *reinterpret_cast<u32x2 *>(og + col) = pk.u;
       }
-    if (p.lse && half == 0) {
-      const float base = rs.base[qs] == -INFINITY ? 0.f : rs.base[qs];
-      p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] =
-          has ? (base + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    }
+    if (p.lse && half == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] = lse_row;
   }
 }
 

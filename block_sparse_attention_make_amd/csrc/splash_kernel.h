@@ -28,6 +28,9 @@ struct FwdParams {
   float cap_out;  // cap * log2(e)
   int32_t cap;    // soft cap on
   int32_t dense;  // dense mask
+  const float *aux;   // device sink logits [aux_heads, num_sinks], or null
+  int32_t aux_heads;  // 1 (shared), Hkv (row h / group) or Hq (row h)
+  int32_t num_sinks;
 };
 
 // dtype: 0 = bf16, 1 = f32.  D in {64, 128}.  Returns hipGetLastError().

@@ -67,6 +67,9 @@ def load_library(path=None):
     lib.splash_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32,
                                ctypes.c_float, ctypes.c_float, vp]
     lib.splash_fwd.restype = ctypes.c_int
+    lib.splash_fwd_sinks.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32,
+                                     ctypes.c_float, ctypes.c_float, vp, i32, i32, vp]
+    lib.splash_fwd_sinks.restype = ctypes.c_int
     lib.splash_last_error.argtypes = []
     lib.splash_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -188,9 +191,11 @@ def make_mask_info(kind, q_len, kv_len, left=None, right=None, chunk=None, dense
 
 
 def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
-               out=None, lse=None, return_lse=True, stream=None):
+               out=None, lse=None, return_lse=True, stream=None, softmax_aux=None):
     """Splash-attention forward on GPU torch tensors (contiguous BHSD).
 
+    softmax_aux: optional attention-sink logits, a float32 GPU tensor [ns]
+    (shared), [Hkv, ns] (query head h uses row h // (Hq // Hkv)) or [Hq, ns].
     Returns (out, lse); lse is float32 [B, Hq, Sq] or None if return_lse is False.
     Launches asynchronously on `stream` (default: torch's current stream).
     """
@@ -215,10 +220,21 @@ def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
         stream = torch.cuda.current_stream(q.device)
     scale = math.nan if softmax_scale is None else float(softmax_scale)
     cap = 0.0 if logits_soft_cap is None else float(logits_soft_cap)
+    dt = BF16 if q.dtype == torch.bfloat16 else F32
+    lse_p = lse.data_ptr() if lse is not None else None
     with torch.cuda.device(q.device):
-        st = lib.splash_fwd(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr() if lse is not None else None,
-                            B, Hq, Hkv, Sq, Skv, D, Dv, BF16 if q.dtype == torch.bfloat16 else F32,
-                            scale, cap, ctypes.c_void_p(stream.cuda_stream))
+        if softmax_aux is None:
+            st = lib.splash_fwd(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse_p, B, Hq, Hkv, Sq, Skv, D, Dv, dt, scale, cap,
+                                ctypes.c_void_p(stream.cuda_stream))
+        else:
+            aux = softmax_aux
+            if not (aux.is_cuda and aux.dtype == torch.float32 and aux.is_contiguous() and aux.dim() in (1, 2)):
+                raise ValueError("softmax_aux must be a contiguous float32 GPU tensor [ns] or [rows, ns]")
+            rows, ns = (1, aux.shape[0]) if aux.dim() == 1 else (aux.shape[0], aux.shape[1])
+            st = lib.splash_fwd_sinks(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      out.data_ptr(), lse_p, B, Hq, Hkv, Sq, Skv, D, Dv, dt, scale, cap,
+                                      aux.data_ptr() if ns else None, rows, ns,
+                                      ctypes.c_void_p(stream.cuda_stream))
     _check(lib, st)
     return out, lse

@@ -186,6 +186,32 @@ SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void *q, const v
                                     int32_t dtype, float softmax_scale, float logits_soft_cap,
                                     void *hip_stream);
 
+/* splash_fwd with attention sinks (the softmax_aux argument of the EasyDeL
+ * BlockSparseAttn.forward_native signature, typed [num_kv_heads, num_sinks]
+ * or [num_sinks]).  The pages name the argument but not its arithmetic; the
+ * usual reading is taken: each sink logit a_k is one more softmax column with
+ * no value, so for every row
+ *   lse_i = log( sum_j exp(s_ij) + sum_k exp(a_k) ),
+ *   out_i = sum_j exp(s_ij - lse_i) v_j,
+ * with the a_k used as given (no softmax_scale, no soft cap).  A row with no
+ * allowed key gets out_i = 0 and lse_i = log sum_k exp(a_k).
+ *
+ * softmax_aux: DEVICE float32 [aux_heads, num_sinks], row-major, owned by
+ * the caller, valid until the kernel ends.  aux_heads == 1 shares one row
+ * with every head, aux_heads == Hkv gives query head h the row h / (Hq/Hkv)
+ * (the pages' [num_kv_heads, num_sinks]), aux_heads == Hq one row per query
+ * head.  Logits must be finite or -inf (a -inf sink adds nothing).
+ * num_sinks == 0 (softmax_aux may then be NULL) is exactly splash_fwd.
+ * Other arguments, errors and ownership as for splash_fwd; a bad aux_heads,
+ * a negative num_sinks or a NULL softmax_aux with num_sinks > 0 returns
+ * SPLASH_EINVAL before anything runs. */
+SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const void *q, const void *k,
+                                          const void *v, void *out, float *lse, int64_t B,
+                                          int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                                          int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
+                                          float logits_soft_cap, const float *softmax_aux,
+                                          int32_t aux_heads, int32_t num_sinks, void *hip_stream);
+
 /* Message of the last failed call on this thread ("" if none).  The string
  * stays valid until the next library call on this thread. */
 SPLASH_API const char *splash_last_error(void);

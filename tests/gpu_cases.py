@@ -18,7 +18,7 @@ def mask_rows_fn(kind, skv, left=None, right=None, chunk=None, dense=None):
 
 
 def run_gpu(q, k, v, kind, left=None, right=None, chunk=None, dense=None, cap=None, scale=None,
-            nan_fill=True):
+            nan_fill=True, aux=None):
     dev = torch.device("cuda:0")
     Sq, Skv = q.shape[2], k.shape[2]
     mi = make_mask_info(kind, Sq, Skv, left=left, right=right, chunk=chunk, dense=dense)
@@ -27,15 +27,19 @@ def run_gpu(q, k, v, kind, left=None, right=None, chunk=None, dense=None, cap=No
     if nan_fill:   # rows the kernel fails to write stay NaN and fail the comparison
         out = torch.full((q.shape[0], q.shape[1], Sq, v.shape[3]), float("nan"), dtype=q.dtype, device=dev)
         lse = torch.full((q.shape[0], q.shape[1], Sq), float("nan"), dtype=torch.float32, device=dev)
-    out, lse = splash_fwd(qd, kd, vd, mi, softmax_scale=scale, logits_soft_cap=cap, out=out, lse=lse)
+    auxd = None if aux is None else torch.as_tensor(np.asarray(aux, dtype=np.float32)).to(dev)
+    out, lse = splash_fwd(qd, kd, vd, mi, softmax_scale=scale, logits_soft_cap=cap, out=out, lse=lse,
+                          softmax_aux=auxd)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), mi
 
 
-def oracle_full(q, k, v, kind, left=None, right=None, chunk=None, dense=None, cap=None, scale=None):
+def oracle_full(q, k, v, kind, left=None, right=None, chunk=None, dense=None, cap=None, scale=None,
+                aux=None):
     fn = mask_rows_fn(kind, k.shape[2], left, right, chunk, dense)
     return oatt.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), fn,
-                          scale=scale, soft_cap=cap)
+                          scale=scale, soft_cap=cap,
+                          softmax_aux=None if aux is None else np.asarray(aux, dtype=np.float32))
 
 
 def compare(o, l, o_ref, l_ref, tol, what=""):

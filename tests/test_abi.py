@@ -21,8 +21,9 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "splash_fwd", "splash_last_error", "splash_make_mask_info", "splash_mask_info_destroy",
-        "splash_mask_info_read_device", "splash_mask_info_upload", "splash_mask_info_view"])
+        "splash_fwd", "splash_fwd_sinks", "splash_last_error", "splash_make_mask_info",
+        "splash_mask_info_destroy", "splash_mask_info_read_device", "splash_mask_info_upload",
+        "splash_mask_info_view"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -99,3 +100,26 @@ def test_null_arguments():
     # not uploaded -> read_device refuses
     buf = np.zeros(4, dtype=np.int8)
     assert lib.splash_mask_info_read_device(mi.handle, 0, buf.ctypes.data, 4) == splash.EINVAL
+
+
+@pytest.mark.parametrize("aux,rows,ns,status", [
+    (None, 1, 2, splash.EINVAL),     # NULL logits with sinks
+    (16, 3, 1, splash.EINVAL),       # rows neither 1, Hkv nor Hq
+    (16, 1, -1, splash.EINVAL),      # negative count
+    (18, 1, 1, splash.EINVAL),       # misaligned
+])
+def test_fwd_sinks_validation_errors_before_launch(aux, rows, ns, status):
+    lib = splash.load_library()
+    mi = splash.make_mask_info("causal", 512, 512)
+    a = _fwd_args(mi, Hq=4, Hkv=2)
+    st = lib.splash_fwd_sinks(*a[:-1], aux, rows, ns, None)
+    assert st == status, lib.splash_last_error()
+    assert lib.splash_last_error()
+
+
+def test_fwd_sinks_empty_batch_is_noop():
+    lib = splash.load_library()
+    mi = splash.make_mask_info("causal", 512, 512)
+    a = _fwd_args(mi, B=0, q=0, k=0, v=0, out=0)
+    assert lib.splash_fwd_sinks(*a[:-1], 16, 1, 1, None) == splash.OK
+    assert lib.splash_fwd_sinks(*a[:-1], None, 0, 0, None) == splash.OK
