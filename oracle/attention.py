@@ -131,3 +131,29 @@ def attention_sampled(q, k, v, mask_rows, samples, scale=None, soft_cap=None, so
         outs.append(ob[0])
         lses.append(lb[0])
     return np.stack(outs), np.array(lses)
+
+
+def merge(o_a, lse_a, o_b, lse_b):
+    """Combine two attention results over disjoint key sets into the result
+    over their union (ring attention on the splash page: each shard's
+    partial result carries its own max and normaliser, and the partials are
+    rescaled the way flash attention rescales inside one kernel).  With
+    lse = ln(e^lse_a + e^lse_b), the union's output is
+    e^(lse_a - lse) o_a + e^(lse_b - lse) o_b.  A part whose lse is -inf (no
+    allowed key in that shard) contributes nothing, whatever its output
+    holds -- the tokamax variant's rule of zeroing inactive shards.
+
+    o_* [..., Dv], lse_* [...]; returns (o, lse) in float64."""
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    lse_a = np.asarray(lse_a, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    lse = np.logaddexp(lse_a, lse_b)
+    has = np.isfinite(lse)
+    ref = np.where(has, lse, 0.0)
+    wa = np.where(np.isfinite(lse_a), np.exp(np.where(np.isfinite(lse_a), lse_a, 0.0) - ref), 0.0)
+    wb = np.where(np.isfinite(lse_b), np.exp(np.where(np.isfinite(lse_b), lse_b, 0.0) - ref), 0.0)
+    pa = np.where(np.isfinite(lse_a)[..., None], o_a, 0.0)
+    pb = np.where(np.isfinite(lse_b)[..., None], o_b, 0.0)
+    o = wa[..., None] * pa + wb[..., None] * pb
+    return o, lse

@@ -271,3 +271,40 @@ def test_sinks_on_row_without_allowed_keys():
     np.testing.assert_array_equal(o[0, 0, 2], np.zeros(8))
     assert abs(lse[0, 0, 2] - np.logaddexp(1.0, 2.0)) < 1e-15
     assert np.all(np.abs(o[0, 0, [0, 1, 3]]) > 0)
+
+
+# ---- merge of results over disjoint key sets ----
+
+@pytest.mark.parametrize("kind,kw", [("causal", {}), ("local", dict(left=6, right=3)), ("dense", {})])
+def test_merge_of_key_shards_equals_full_attention(kind, kw):
+    """Attention over keys [0, a) and over keys [a, Skv), merged, must equal
+    attention over all keys (the identity ring attention rests on), for
+    every split point, including shards where some rows have no allowed key."""
+    rng = np.random.default_rng(15)
+    sq = skv = 20
+    q, k, v = _rand(rng, 1, 2, sq, 8), _rand(rng, 1, 2, skv, 8), _rand(rng, 1, 2, skv, 5)
+    if kind == "dense":
+        m = rng.random((1, sq, skv)) < 0.3
+        m[0, 3] = False                      # a row with no key anywhere
+    else:
+        m = omasks.materialize(kind, sq, skv, **kw)
+    o, lse = oatt.attention(q, k, v, _rows_fn(m), soft_cap=2.5)
+    for a in (1, 7, 13, 19):
+        oa, la = oatt.attention(q, k[:, :, :a], v[:, :, :a], _rows_fn(m[:, :, :a]), soft_cap=2.5)
+        ob, lb = oatt.attention(q, k[:, :, a:], v[:, :, a:], _rows_fn(m[:, :, a:]), soft_cap=2.5)
+        om, lm = oatt.merge(oa, la, ob, lb)
+        np.testing.assert_allclose(om, o, rtol=0, atol=1e-12)
+        fin = np.isfinite(lse)
+        assert np.array_equal(fin, np.isfinite(lm))
+        np.testing.assert_allclose(lm[fin], lse[fin], rtol=0, atol=1e-12)
+
+
+def test_merge_ignores_output_of_inactive_part():
+    """A part with lse = -inf contributes nothing even if its output is garbage."""
+    o_a = np.array([[1.0, 2.0], [3.0, 4.0]])
+    l_a = np.array([0.5, -np.inf])
+    o_b = np.array([[np.nan, 7.0], [np.nan, np.inf]])
+    l_b = np.array([-np.inf, -np.inf])
+    o, l = oatt.merge(o_a, l_a, o_b, l_b)
+    np.testing.assert_array_equal(o, [[1.0, 2.0], [0.0, 0.0]])
+    np.testing.assert_array_equal(l, [0.5, -np.inf])
