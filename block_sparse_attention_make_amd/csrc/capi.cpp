@@ -9,6 +9,7 @@
 
 #include "mask_info.h"
 #include "splash_kernel.h"
+#include "lse_merge.h"
 
 namespace splash {
 
@@ -237,6 +238,7 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
   p.left = mi->left;
   p.right = mi->right;
   p.chunk = mi->chunk;
+  p.kv_offset = mi->kv_offset;
   p.dense = mi->kind == SPLASH_MASK_DENSE;
   const float scale = std::isnan(softmax_scale) ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D)))
                                                 : softmax_scale;
@@ -278,4 +280,28 @@ extern "C" SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const
   clear_error();
   return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale,
                   logits_soft_cap, softmax_aux, aux_heads, num_sinks, hip_stream);
+}
+
+extern "C" SPLASH_API splash_status splash_lse_merge(const void *out_a, const float *lse_a, int32_t dtype_a,
+                                                     const void *out_b, const float *lse_b, int32_t dtype_b,
+                                                     void *out, float *lse, int32_t dtype_out, int64_t rows,
+                                                     int64_t Dv, void *hip_stream) {
+  clear_error();
+  auto ok_dt = [](int32_t d) { return d == SPLASH_BF16 || d == SPLASH_F32; };
+  if (!ok_dt(dtype_a) || !ok_dt(dtype_b) || !ok_dt(dtype_out)) return fail(SPLASH_EINVAL, "unknown dtype");
+  if (rows < 0) return fail(SPLASH_EINVAL, "rows must be >= 0");
+  if (Dv <= 0 || Dv % 8 != 0 || 64 % (Dv / 8) != 0)
+    return fail(SPLASH_EUNSUPPORTED, "Dv must be one of 8, 16, 32, 64, 128, 256, 512");
+  if (rows == 0) return SPLASH_OK;
+  if (!out_a || !lse_a || !out_b || !lse_b || !out || !lse) return fail(SPLASH_EINVAL, "NULL pointer");
+  if ((reinterpret_cast<uintptr_t>(out_a) | reinterpret_cast<uintptr_t>(out_b) | reinterpret_cast<uintptr_t>(out)) % 16)
+    return fail(SPLASH_EINVAL, "outputs must be 16-byte aligned");
+  if ((out == out_a && dtype_out != dtype_a) || (out == out_b && dtype_out != dtype_b))
+    return fail(SPLASH_EINVAL, "an output written in place must keep its dtype");
+  if (rows > (int64_t(1) << 40) / Dv) return fail(SPLASH_EUNSUPPORTED, "too many elements");
+  hipError_t e = launch_lse_merge(out_a, lse_a, dtype_a == SPLASH_BF16 ? 0 : 1, out_b, lse_b,
+                                  dtype_b == SPLASH_BF16 ? 0 : 1, out, lse, dtype_out == SPLASH_BF16 ? 0 : 1,
+                                  rows, static_cast<int>(Dv), static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return SPLASH_OK;
 }

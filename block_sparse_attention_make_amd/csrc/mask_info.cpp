@@ -156,8 +156,8 @@ void compile(splash_mask_info &m, const splash_mask_desc &d) {
   if (!dense) {
     for (int64_t r = 0; r < nq; ++r)
       for (int64_t c = 0; c < nk; ++c)
-        label[r * nk + c] = static_cast<uint8_t>(
-            label_computable(m, r * bq, r * bq + bq - 1, c * bk, c * bk + bk - 1));
+        label[r * nk + c] = static_cast<uint8_t>(label_computable(
+            m, r * bq, r * bq + bq - 1, m.kv_offset + c * bk, m.kv_offset + c * bk + bk - 1));
   } else {
     std::vector<uint8_t> seen_one(static_cast<size_t>(nk)), seen_zero(static_cast<size_t>(nk));
     for (int64_t h = 0; h < hm; ++h)
@@ -165,7 +165,7 @@ void compile(splash_mask_info &m, const splash_mask_desc &d) {
         std::fill(seen_one.begin(), seen_one.end(), 0);
         std::fill(seen_zero.begin(), seen_zero.end(), 0);
         for (int64_t i = r * bq; i < r * bq + bq; ++i) {
-          const uint8_t *row = d.dense + (h * m.q_len + i) * m.kv_len;
+          const uint8_t *row = d.dense + (h * m.q_len + i) * m.kv_total + m.kv_offset;
           for (int64_t c = 0; c < nk; ++c) {
             const uint8_t *seg = row + c * bk;
             for (int64_t j = 0; j < bk; ++j) {
@@ -192,7 +192,7 @@ void compile(splash_mask_info &m, const splash_mask_desc &d) {
           const size_t at = static_cast<size_t>((h * nq + r) * nk + c);
           if (label[at] != 1) continue;
           for (int64_t i = 0; i < bq; ++i) {
-            const uint8_t *src = d.dense + (h * m.q_len + r * bq + i) * m.kv_len + c * bk;
+            const uint8_t *src = d.dense + (h * m.q_len + r * bq + i) * m.kv_total + m.kv_offset + c * bk;
             for (int64_t j = 0; j < bk; ++j) cur[i * bk + j] = src[j] ? 1 : 0;
           }
           const uint64_t key = fnv1a(cur.data(), blk);
@@ -294,15 +294,19 @@ void compile(splash_mask_info &m, const splash_mask_desc &d) {
 }  // namespace
 }  // namespace splash
 
-extern "C" SPLASH_API splash_status splash_make_mask_info(const splash_mask_desc *mask,
-                                                          int32_t block_q, int32_t block_kv,
-                                                          uint32_t flags, splash_mask_info **out) {
-  using namespace splash;
-  clear_error();
+namespace splash {
+namespace {
+
+splash_status make_impl(const splash_mask_desc *mask, int64_t kv_start, int64_t kv_count,
+                        int32_t block_q, int32_t block_kv, uint32_t flags, splash_mask_info **out) {
   if (!out) return fail(SPLASH_EINVAL, "out is NULL");
   *out = nullptr;
   splash_status st = validate(mask, block_q, block_kv);
   if (st != SPLASH_OK) return st;
+  if (kv_start < 0 || kv_count < 0 || kv_start > mask->kv_len || kv_count > mask->kv_len - kv_start)
+    return fail(SPLASH_EINVAL, "key slice lies outside [0, kv_len)");
+  if (kv_start % block_kv || kv_count % block_kv)
+    return fail(SPLASH_EINVAL, "block_kv must divide the key slice's start and length");
   if (flags & ~static_cast<uint32_t>(SPLASH_FLAG_SHRINK | SPLASH_FLAG_DOWNCAST))
     return fail(SPLASH_EINVAL, "unknown flag bits");
   splash_mask_info *m = new (std::nothrow) splash_mask_info();
@@ -310,14 +314,16 @@ extern "C" SPLASH_API splash_status splash_make_mask_info(const splash_mask_desc
   m->kind = mask->kind;
   m->num_heads = mask->num_heads;
   m->q_len = mask->q_len;
-  m->kv_len = mask->kv_len;
+  m->kv_len = kv_count;
+  m->kv_offset = kv_start;
+  m->kv_total = mask->kv_len;
   m->left = mask->kind == SPLASH_MASK_LOCAL ? mask->left : -1;
   m->right = mask->kind == SPLASH_MASK_LOCAL ? mask->right : -1;
   m->chunk = mask->kind == SPLASH_MASK_CHUNKED_CAUSAL ? mask->chunk : 0;
   m->block_q = block_q;
   m->block_kv = block_kv;
   m->nq = mask->q_len / block_q;
-  m->nk = mask->kv_len / block_kv;
+  m->nk = kv_count / block_kv;
   m->flags = flags;
   try {
     compile(*m, *mask);
@@ -330,6 +336,29 @@ extern "C" SPLASH_API splash_status splash_make_mask_info(const splash_mask_desc
   }
   *out = m;
   return SPLASH_OK;
+}
+
+}  // namespace
+}  // namespace splash
+
+extern "C" SPLASH_API splash_status splash_make_mask_info(const splash_mask_desc *mask,
+                                                          int32_t block_q, int32_t block_kv,
+                                                          uint32_t flags, splash_mask_info **out) {
+  splash::clear_error();
+  return splash::make_impl(mask, 0, mask ? mask->kv_len : 0, block_q, block_kv, flags, out);
+}
+
+extern "C" SPLASH_API splash_status splash_make_mask_info_kv_slice(const splash_mask_desc *mask,
+                                                                   int64_t kv_start, int64_t kv_count,
+                                                                   int32_t block_q, int32_t block_kv,
+                                                                   uint32_t flags,
+                                                                   splash_mask_info **out) {
+  splash::clear_error();
+  if (!mask) {
+    if (out) *out = nullptr;
+    return splash::fail(SPLASH_EINVAL, "mask descriptor is NULL");
+  }
+  return splash::make_impl(mask, kv_start, kv_count, block_q, block_kv, flags, out);
 }
 
 extern "C" SPLASH_API splash_status splash_mask_info_view(const splash_mask_info *mi, int32_t which,

@@ -46,6 +46,9 @@ struct splash_mask_info {
   int32_t kind = 0;
   int32_t num_heads = 1;  // Hm
   int64_t q_len = 0, kv_len = 0;
+  // Key-axis slice: this MaskInfo covers keys [kv_offset, kv_offset + kv_len)
+  // of a mask over kv_total keys (0 and kv_len for a whole mask).
+  int64_t kv_offset = 0, kv_total = 0;
   int64_t left = -1, right = -1, chunk = 0;
   int32_t block_q = 0, block_kv = 0;
   int64_t nq = 0, nk = 0, width = 0;

@@ -231,6 +231,8 @@ void splash_fwd_kernel(const FwdParams p) {
     if (p.mask_kind == 0) { lo = -big; hi = qpos; }
     else if (p.mask_kind == 1) { lo = p.left < 0 ? -big : qpos - p.left; hi = p.right < 0 ? big : qpos + p.right; }
     else { lo = (qpos / p.chunk) * p.chunk; hi = qpos; }
+    lo -= p.kv_offset;   // into this (possibly key-sliced) MaskInfo's key coordinates
+    hi -= p.kv_offset;
   }
 
   // ---- running softmax state ----------------------------------------------
@@ -836,12 +838,14 @@ void splash_fwd_wide(const FwdParams p) {
       // Every computable mask admits, for query position i, one key interval:
       // causal (-inf, i]; local [i - left, i + right]; chunked [chunk start, i].
       const int64_t qpos = p.q_seq[q_row0 + 32 * qs];
+      const int64_t big = int64_t(1) << 40;   // an unbounded side
       int64_t l64, h64;
-      if (p.mask_kind == 0) { l64 = -1; h64 = qpos; }
-      else if (p.mask_kind == 1) { l64 = p.left < 0 ? -1 : qpos - p.left; h64 = p.right < 0 ? p.Skv : qpos + p.right; }
+      if (p.mask_kind == 0) { l64 = -big; h64 = qpos; }
+      else if (p.mask_kind == 1) { l64 = p.left < 0 ? -big : qpos - p.left; h64 = p.right < 0 ? big : qpos + p.right; }
       else { l64 = (qpos / p.chunk) * p.chunk; h64 = qpos; }
-      lo[qs] = static_cast<int>(clamp64(l64, -1, p.Skv));
-      hi[qs] = static_cast<int>(clamp64(h64, -1, p.Skv));
+      // into this (possibly key-sliced) MaskInfo's key coordinates
+      lo[qs] = static_cast<int>(clamp64(l64 - p.kv_offset, -1, p.Skv));
+      hi[qs] = static_cast<int>(clamp64(h64 - p.kv_offset, -1, p.Skv));
     }
   }
   const float c2e = CAP ? 1.f : p.c2;

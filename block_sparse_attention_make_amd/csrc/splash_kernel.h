@@ -24,6 +24,7 @@ struct FwdParams {
   int32_t bm_bytes, dn_bytes, mn_bytes;
   int32_t mask_kind;                  // 0 causal, 1 local, 2 chunked causal, 3 dense
   int64_t left, right, chunk;
+  int64_t kv_offset;  // computable masks: global position of local key 0 (key-axis slices)
   float c2;       // no cap: softmax_scale * log2(e); cap: softmax_scale / cap
   float cap_out;  // cap * log2(e)
   int32_t cap;    // soft cap on

@@ -70,6 +70,11 @@ def load_library(path=None):
     lib.splash_fwd_sinks.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32,
                                      ctypes.c_float, ctypes.c_float, vp, i32, i32, vp]
     lib.splash_fwd_sinks.restype = ctypes.c_int
+    lib.splash_make_mask_info_kv_slice.argtypes = [ctypes.POINTER(_MaskDesc), i64, i64, i32, i32,
+                                                   ctypes.c_uint32, ctypes.POINTER(vp)]
+    lib.splash_make_mask_info_kv_slice.restype = ctypes.c_int
+    lib.splash_lse_merge.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, i32, i64, i64, vp]
+    lib.splash_lse_merge.restype = ctypes.c_int
     lib.splash_last_error.argtypes = []
     lib.splash_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -160,9 +165,11 @@ class MaskInfo:
 
 
 def make_mask_info(kind, q_len, kv_len, left=None, right=None, chunk=None, dense=None,
-                   block_q=128, block_kv=128, shrink=True, downcast=True):
+                   block_q=128, block_kv=128, shrink=True, downcast=True, kv_slice=None):
     """Compile a mask.  kind: "causal" | "local" | "chunked" | "dense".
-    dense: host array [Hm, q_len, kv_len] (or [q_len, kv_len]), nonzero = allowed."""
+    dense: host array [Hm, q_len, kv_len] (or [q_len, kv_len]), nonzero = allowed.
+    kv_slice: optional (kv_start, kv_count) -- the MaskInfo of that key-axis
+    slice of the mask (for a key/value shard); its kv_len is kv_count."""
     lib = load_library()
     if kind not in MASK_KINDS:
         raise ValueError(f"unknown mask kind {kind!r}")
@@ -185,9 +192,17 @@ def make_mask_info(kind, q_len, kv_len, left=None, right=None, chunk=None, dense
         d.dense = keep.ctypes.data
     flags = (FLAG_SHRINK if shrink else 0) | (FLAG_DOWNCAST if downcast else 0)
     h = ctypes.c_void_p()
-    _check(lib, lib.splash_make_mask_info(ctypes.byref(d), int(block_q), int(block_kv), flags, ctypes.byref(h)))
+    if kv_slice is None:
+        _check(lib, lib.splash_make_mask_info(ctypes.byref(d), int(block_q), int(block_kv), flags,
+                                              ctypes.byref(h)))
+        local_kv = int(kv_len)
+    else:
+        k0, kn = int(kv_slice[0]), int(kv_slice[1])
+        _check(lib, lib.splash_make_mask_info_kv_slice(ctypes.byref(d), k0, kn, int(block_q), int(block_kv),
+                                                       flags, ctypes.byref(h)))
+        local_kv = kn
     del keep
-    return MaskInfo(h.value, lib, kind, int(q_len), int(kv_len), int(block_q), int(block_kv), d.num_heads)
+    return MaskInfo(h.value, lib, kind, int(q_len), local_kv, int(block_q), int(block_kv), d.num_heads)
 
 
 def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
@@ -238,3 +253,61 @@ def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
                                       ctypes.c_void_p(stream.cuda_stream))
     _check(lib, st)
     return out, lse
+
+
+def lse_merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, out_dtype=None, stream=None):
+    """Merge two attention results over disjoint key sets (GPU tensors
+    [..., Dv] and float32 [...]) into the result over their union.  out / lse
+    may be out_a / lse_a for an in-place accumulation.  Returns (out, lse)."""
+    import torch
+    lib = load_library()
+    dts = {torch.bfloat16: BF16, torch.float32: F32}
+    if out_a.shape != out_b.shape or lse_a.shape != lse_b.shape or out_a.shape[:-1] != lse_a.shape:
+        raise ValueError("shapes of the two parts do not match")
+    for t in (out_a, lse_a, out_b, lse_b):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("merge operands must be contiguous GPU tensors")
+    if lse_a.dtype != torch.float32 or lse_b.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    if out is None:
+        out = torch.empty(out_a.shape, dtype=out_dtype or out_a.dtype, device=out_a.device)
+    if lse is None:
+        lse = torch.empty(lse_a.shape, dtype=torch.float32, device=out_a.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(out_a.device)
+    rows, dv = lse_a.numel(), out_a.shape[-1]
+    with torch.cuda.device(out_a.device):
+        st = lib.splash_lse_merge(out_a.data_ptr(), lse_a.data_ptr(), dts[out_a.dtype],
+                                  out_b.data_ptr(), lse_b.data_ptr(), dts[out_b.dtype],
+                                  out.data_ptr(), lse.data_ptr(), dts[out.dtype], rows, dv,
+                                  ctypes.c_void_p(stream.cuda_stream))
+    _check(lib, st)
+    return out, lse
+
+
+def splash_fwd_kv_sharded(q, k_shards, v_shards, mask_infos, softmax_scale=None, logits_soft_cap=None,
+                          stream=None):
+    """Attention over key/value shards on one GPU -- the per-device part of
+    ring attention: splash_fwd on each shard with its key-sliced MaskInfo,
+    then an lse merge of each shard's result into a float32 accumulator.
+    k_shards[s], v_shards[s]: [B, Hkv, n_s, D]; mask_infos[s] the MaskInfo of
+    keys [sum of earlier n, + n_s) (make_mask_info(..., kv_slice=...)).
+    Attention sinks are not accepted here (the tokamax ring variant refuses
+    them too): a sink would be counted once per shard.  Returns (out, lse)."""
+    import torch
+    if not (len(k_shards) == len(v_shards) == len(mask_infos)) or not k_shards:
+        raise ValueError("need one k, v and MaskInfo per shard")
+    kw = dict(softmax_scale=softmax_scale, logits_soft_cap=logits_soft_cap, stream=stream)
+    if len(k_shards) == 1:
+        return splash_fwd(q, k_shards[0], v_shards[0], mask_infos[0], **kw)
+    acc = lse = None
+    for s, (k, v, mi) in enumerate(zip(k_shards, v_shards, mask_infos)):
+        o_s, l_s = splash_fwd(q, k, v, mi, **kw)
+        last = s == len(k_shards) - 1
+        if acc is None:
+            acc, lse = o_s, l_s
+            continue
+        dst = torch.empty(acc.shape, dtype=q.dtype if last else torch.float32, device=q.device) \
+            if (last or acc.dtype != torch.float32) else acc
+        acc, lse = lse_merge(acc, lse, o_s, l_s, out=dst, lse=lse, stream=stream)
+    return acc, lse

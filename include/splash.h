@@ -212,6 +212,46 @@ SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const void *q, c
                                           float logits_soft_cap, const float *softmax_aux,
                                           int32_t aux_heads, int32_t num_sinks, void *hip_stream);
 
+/* Key-axis slice of a mask (ring attention on the splash-attention explainer
+ * page, FAQ "What does ring attention add on top of the splash kernel?": the
+ * MaskInfo is cut along the key axis to match the key/value shard a device
+ * holds).  Builds the MaskInfo of keys [kv_start, kv_start + kv_count) of the
+ * mask `mask` describes over all mask->kv_len keys, exactly as
+ * splash_make_mask_info would for the mask's columns in that range: its
+ * kv_len is kv_count, its block columns are local to the slice, and a
+ * computable mask keeps its kind, recomputed in the kernel at the slice's
+ * key offset.  A dense mask is read from mask->dense over all kv_len keys.
+ * Use it with splash_fwd on the shard's k and v ([B, Hkv, kv_count, D]) and
+ * combine the shards' (out, lse) with splash_lse_merge.
+ * kv_start and kv_count must be multiples of block_kv with
+ * 0 <= kv_start <= kv_start + kv_count <= mask->kv_len (else SPLASH_EINVAL);
+ * other arguments, errors and ownership as for splash_make_mask_info. */
+SPLASH_API splash_status splash_make_mask_info_kv_slice(const splash_mask_desc *mask, int64_t kv_start,
+                                                        int64_t kv_count, int32_t block_q,
+                                                        int32_t block_kv, uint32_t flags,
+                                                        splash_mask_info **out);
+
+/* Merge two attention results over disjoint key sets into the result over
+ * their union (same FAQ: each shard's result carries its own max and sum,
+ * combined with flash attention's rescaling):
+ *   lse = log(e^lse_a + e^lse_b),  out = e^(lse_a - lse) out_a + e^(lse_b - lse) out_b,
+ * per row of `rows` rows of Dv elements.  A part whose lse is -inf adds
+ * nothing, whatever its out holds; rows empty in both give out = 0 and
+ * lse = -inf.
+ *
+ * out_a, out_b, out: DEVICE [rows, Dv] in dtype_a / dtype_b / dtype_out
+ * (SPLASH_BF16 or SPLASH_F32; a float32 accumulator keeps a chain of merges
+ * from rounding at every step), 16-byte aligned.  lse_a, lse_b, lse: DEVICE
+ * float32 [rows].  out may be out_a (or out_b) and lse may be lse_a (or
+ * lse_b) -- an in-place accumulation -- when the dtypes agree; any other
+ * overlap is not allowed.  Dv in {8, 16, 32, 64, 128, 256, 512}
+ * (else SPLASH_EUNSUPPORTED).  Asynchronous on hip_stream; allocates
+ * nothing.  Errors as for splash_fwd. */
+SPLASH_API splash_status splash_lse_merge(const void *out_a, const float *lse_a, int32_t dtype_a,
+                                          const void *out_b, const float *lse_b, int32_t dtype_b,
+                                          void *out, float *lse, int32_t dtype_out, int64_t rows,
+                                          int64_t Dv, void *hip_stream);
+
 /* Message of the last failed call on this thread ("" if none).  The string
  * stays valid until the next library call on this thread. */
 SPLASH_API const char *splash_last_error(void);

@@ -21,9 +21,9 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "splash_fwd", "splash_fwd_sinks", "splash_last_error", "splash_make_mask_info",
-        "splash_mask_info_destroy", "splash_mask_info_read_device", "splash_mask_info_upload",
-        "splash_mask_info_view"])
+        "splash_fwd", "splash_fwd_sinks", "splash_last_error", "splash_lse_merge",
+        "splash_make_mask_info", "splash_make_mask_info_kv_slice", "splash_mask_info_destroy",
+        "splash_mask_info_read_device", "splash_mask_info_upload", "splash_mask_info_view"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -123,3 +123,26 @@ def test_fwd_sinks_empty_batch_is_noop():
     a = _fwd_args(mi, B=0, q=0, k=0, v=0, out=0)
     assert lib.splash_fwd_sinks(*a[:-1], 16, 1, 1, None) == splash.OK
     assert lib.splash_fwd_sinks(*a[:-1], None, 0, 0, None) == splash.OK
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dta=5), splash.EINVAL),
+    (dict(rows=-1), splash.EINVAL),
+    (dict(dv=96), splash.EUNSUPPORTED),
+    (dict(dv=1024), splash.EUNSUPPORTED),
+    (dict(oa=0), splash.EINVAL),
+    (dict(oa=8), splash.EINVAL),
+    (dict(oo=16, dto=splash.F32), splash.EINVAL),   # in place with another dtype
+])
+def test_lse_merge_validation_errors_before_launch(over, status):
+    lib = splash.load_library()
+    a = dict(oa=16, la=16, dta=splash.BF16, ob=32, lb=32, dtb=splash.BF16, oo=16, lo=16,
+             dto=splash.BF16, rows=4, dv=128, stream=None)
+    a.update(over)
+    assert lib.splash_lse_merge(*a.values()) == status, lib.splash_last_error()
+    assert lib.splash_last_error()
+
+
+def test_lse_merge_zero_rows_is_noop():
+    lib = splash.load_library()
+    assert lib.splash_lse_merge(None, None, 0, None, None, 0, None, None, 0, 0, 128, None) == splash.OK

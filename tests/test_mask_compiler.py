@@ -150,3 +150,39 @@ def test_invalid_masks_rejected(args, msg):
         splash.make_mask_info(**args)
     assert ei.value.status == splash.EINVAL
     assert msg in str(ei.value)
+
+
+# ---- key-axis slices (the MaskInfo of one key/value shard) ----
+
+@pytest.mark.parametrize("kind,kw", [
+    ("causal", {}), ("local", {"left": 300, "right": 70}), ("local", {"left": None, "right": 10}),
+    ("chunked", {"chunk": 200}),
+])
+@pytest.mark.parametrize("k0,kn", [(0, 384), (256, 512), (640, 256), (896, 0), (0, 1024)])
+def test_kv_slice_equals_mask_of_the_slice(kind, kw, k0, kn):
+    """The native slice labels computable masks in closed form at the slice's
+    key offset; the oracle builds the MaskInfo of the materialised mask's
+    columns [k0, k0 + kn).  They must agree byte for byte."""
+    sq = skv = 1024 if kn else 1024
+    nat = splash.make_mask_info(kind, sq, skv, kv_slice=(k0, kn), **kw)
+    m = omasks.materialize(kind, sq, skv, **kw)[:, :, k0:k0 + kn]
+    ref = omi.build(m, 128, 128, computable=True)
+    assert_same(nat, ref)
+    assert nat.kv_len == kn
+
+
+@pytest.mark.parametrize("k0,kn", [(128, 256), (0, 128), (384, 256)])
+def test_kv_slice_dense(k0, kn):
+    rng = np.random.default_rng(7)
+    dense = rng.random((2, 256, 640)) < 0.15
+    dense[:, :, 130:140] = True
+    nat = splash.make_mask_info("dense", 256, 640, dense=dense, kv_slice=(k0, kn))
+    ref = omi.build(dense[:, :, k0:k0 + kn], 128, 128, computable=False)
+    assert_same(nat, ref)
+
+
+@pytest.mark.parametrize("k0,kn", [(-128, 256), (0, 1152), (64, 128), (128, 100), (1024, 128)])
+def test_kv_slice_rejected(k0, kn):
+    with pytest.raises(splash.SplashError) as e:
+        splash.make_mask_info("causal", 1024, 1024, kv_slice=(k0, kn))
+    assert e.value.status == splash.EINVAL
