@@ -1,6 +1,7 @@
 """Benchmark: splash-attention forward TFLOP/s on computed blocks (MI355X).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--sinks N] [--kv-shards P]
 
 A step is one splash_fwd call (the whole forward path: block walk over the
 MaskInfo, K/V staging, QK^T, soft cap, masking, online softmax, PV, epilogue)
@@ -12,6 +13,13 @@ separately and reported as mask_compile_ms.
 FLOPs on computed blocks = sum over (b, h) of the non-empty grid positions x
 2 * 128 * 128 * (D + Dv); softmax and masking work are not counted.  Prints
 one JSON line.
+
+--sinks N adds N attention-sink logits per key/value head (splash_fwd_sinks).
+--kv-shards P splits the keys into P equal shards and times the per-device
+part of ring attention instead: P splash_fwd calls on key-sliced MaskInfos
+plus P - 1 lse merges into a float32 accumulator (the computed blocks, and so
+the FLOPs, are the same).  It also times the merge kernel alone and reports
+its HBM roofline under "merge".
 """
 import argparse
 import hashlib
@@ -26,6 +34,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz (AMD: 2.5 PFLOP/s)
 PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_make_amd", "csrc", "splash_fwd.hip")
 
 
@@ -115,6 +124,8 @@ def main():
     ap.add_argument("--workload", default="causal_mha_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--sinks", type=int, default=0, help="attention-sink logits per kv head")
+    ap.add_argument("--kv-shards", type=int, default=1, help="time the key/value-sharded path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -127,7 +138,8 @@ def main():
     import numpy as np
     import torch
 
-    from block_sparse_attention_make_amd import make_mask_info, splash_fwd, synthetic
+    from block_sparse_attention_make_amd import (lse_merge, make_mask_info, splash_fwd, splash_fwd_kv_sharded,
+                                                 synthetic)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -164,9 +176,32 @@ def main():
     out = torch.empty((w.B, w.Hq, w.Sq, w.Dv), dtype=q.dtype, device=dev)
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    aux = None
+    if args.sinks:
+        g = torch.Generator().manual_seed(7)
+        aux = torch.randn((w.Hkv, args.sinks), generator=g, dtype=torch.float32).to(dev)
+    P = args.kv_shards
+    if P > 1:
+        if args.sinks:
+            print("--kv-shards and --sinks do not combine (a sink would count once per shard)", file=sys.stderr)
+            sys.exit(2)
+        if w.Skv % (128 * P):
+            print(f"--kv-shards {P} must split {w.Skv} keys into whole 128-key blocks", file=sys.stderr)
+            sys.exit(2)
+        n = w.Skv // P
+        shard_mis = [make_mask_info(m.kind, w.Sq, w.Skv, left=m.left, right=m.right, chunk=m.chunk,
+                                    dense=dense, kv_slice=(s * n, n)) for s in range(P)]
+        for smi in shard_mis:
+            smi.upload()
+        ks = [kd[:, :, s * n:(s + 1) * n].contiguous() for s in range(P)]
+        vs = [vd[:, :, s * n:(s + 1) * n].contiguous() for s in range(P)]
 
     def step():
-        splash_fwd(qd, kd, vd, mi, logits_soft_cap=w.soft_cap, out=out, lse=lse, stream=stream)
+        if P > 1:
+            splash_fwd_kv_sharded(qd, ks, vs, shard_mis, logits_soft_cap=w.soft_cap, stream=stream)
+        else:
+            splash_fwd(qd, kd, vd, mi, logits_soft_cap=w.soft_cap, out=out, lse=lse, stream=stream,
+                       softmax_aux=aux)
 
     for _ in range(args.warmup):
         step()
@@ -181,6 +216,28 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [a.elapsed_time(b) for a, b in ev]
+    merge_info = None
+    if P > 1:
+        # the merge kernel alone: float32 accumulator (in place) + one bf16 shard result
+        rows = w.B * w.Hq * w.Sq
+        acc = torch.zeros((rows, w.Dv), dtype=torch.float32, device=dev)
+        acc_l = torch.zeros(rows, dtype=torch.float32, device=dev)
+        part = torch.randn((rows, w.Dv), dtype=torch.float32, device=dev).to(q.dtype)
+        part_l = torch.randn(rows, dtype=torch.float32, device=dev)
+        for _ in range(20):
+            lse_merge(acc, acc_l, part, part_l, out=acc, lse=acc_l, stream=stream)
+        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        for a, b in mev:
+            a.record(stream)
+            lse_merge(acc, acc_l, part, part_l, out=acc, lse=acc_l, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        m_ms = float(np.mean([a.elapsed_time(b) for a, b in mev]))
+        m_bytes = rows * w.Dv * (4 + part.element_size() + 4) + rows * 4 * 3
+        merge_info = {"kernel": "lse_merge_kernel", "bound": "hbm", "bytes_per_launch": m_bytes,
+                      "kernel_ms_avg": round(m_ms, 5), "achieved": round(m_bytes / (m_ms * 1e-3) / 1e9, 1),
+                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                      "frac": round(m_bytes / (m_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     ms_per_step = wall * 1e3 / args.steps
     kern_avg = float(np.mean(kern_ms))
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -203,7 +260,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "seq_len": w.Sq, "head_dim": w.D, "mask": m.kind, "block": w.block,
-                   "soft_cap": w.soft_cap, "parallelism": "single-gpu"},
+                   "soft_cap": w.soft_cap, "parallelism": "single-gpu",
+                   "sinks_per_kv_head": args.sinks, "kv_shards": P},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "dense_equiv_tflops": round(flops_dense / (ms_per_step * 1e-3) / 1e12, 2),
         "blocks_skipped": blocks_total - blocks_computed,
@@ -219,6 +277,11 @@ def main():
                      "kernel_ms_avg": round(kern_avg, 5)},
         "cpu_baseline": None,
     }
+    if merge_info is not None:
+        res["merge"] = merge_info
+        # with shards the timed step holds several kernels: achieved is per step, not per launch
+        res["roofline"]["kernel"] = "splash_fwd_wide x P + lse_merge_kernel x (P-1)"
+        res["roofline"]["traffic"] = None
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, dense, bm, args.cpu_budget)
     print(json.dumps(res), flush=True)
