@@ -1,7 +1,7 @@
 /*
  * splash.h -- C ABI of the MI355X (gfx950) splash-attention forward library.
  *
- * Two operations, as the splash-attention explainer page
+ * The operations, as the splash-attention explainer page
  * (explainers.rudrite.com/splash-attention) describes them:
  *
  *  1. A mask compiler (FAQ "What is MaskInfo in splash attention?", "Does
@@ -22,7 +22,13 @@
  *     keeps for its backward pass, pallas-flash-attention-tpu page, FAQ
  *     "What does the TPU flash attention kernel save for the backward
  *     pass?"), and takes the softmax scale and optional logits soft cap of
- *     the EasyDeL BlockSparseAttn.forward_native signature.
+ *     the EasyDeL BlockSparseAttn.forward_native signature, optionally with
+ *     the attention-sink logits (softmax_aux) of that signature.
+ *
+ *  3. The per-device part of ring attention (explainer FAQ "What does ring
+ *     attention add on top of the splash kernel?"): MaskInfo slices along
+ *     the key axis for key/value shards, and the log-sum-exp merge of the
+ *     shards' results.
  *
  * Conventions
  *  - Every entry point returns a splash_status; on failure a message is
