@@ -157,3 +157,73 @@ def merge(o_a, lse_a, o_b, lse_b):
     pb = np.where(np.isfinite(lse_b)[..., None], o_b, 0.0)
     o = wa[..., None] * pa + wb[..., None] * pb
     return o, lse
+
+
+def attention_bwd_rows(q, k, v, do, allowed, scale=None, soft_cap=None):
+    """Gradients of one (batch, head): q [n, D], k [Skv, D], v [Skv, Dv],
+    do [n, Dv] (the gradient of the output), allowed [n, Skv] bool.
+
+    The backward the pages describe for flash attention (pallas flash
+    attention page, "What does the TPU flash attention kernel save for the
+    backward pass?" and "Why does the TPU flash attention backward pass run
+    two kernels instead of one?"): the weights are rebuilt from q, k and the
+    forward's log-sum-exp, and the row-wise dot product di = <do_i, o_i> is
+    formed once.  With p_ij = exp(s'_ij - lse_i) on allowed pairs (0
+    elsewhere), s' the capped or plain scaled logit:
+
+      dv_j  = sum_i p_ij do_i
+      dp_ij = <do_i, v_j>
+      ds'_ij = p_ij (dp_ij - di_i)
+      ds_ij = ds'_ij * (1 - tanh^2(s_ij / c))     (soft cap c; else ds = ds')
+      dq_i  = scale * sum_j ds_ij k_j
+      dk_j  = scale * sum_i ds_ij q_i
+
+    Returns (dq [n, D], dk [Skv, D], dv [Skv, Dv]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    o, lse = attention_rows(q, k, v, allowed, scale, soft_cap)
+    s = scale * (q @ k.T)
+    if soft_cap is not None:
+        t = np.tanh(s / soft_cap)
+        sc = soft_cap * t
+    else:
+        sc = s
+    has = np.isfinite(lse)
+    p = np.where(allowed & has[:, None], np.exp(sc - np.where(has, lse, 0.0)[:, None]), 0.0)
+    di = (do * o).sum(axis=1)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - di[:, None])
+    if soft_cap is not None:
+        ds = ds * (1.0 - t * t)
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_bwd(q, k, v, do, mask_rows, scale=None, soft_cap=None, row_chunk=512):
+    """Gradients of attention(...) for the output gradient do [B, Hq, Sq, Dv].
+    Key/value gradients of a GQA group sum over its query heads.
+    Returns (dq, dk, dv) in float64, shaped like q, k, v."""
+    b_, hq, sq, _ = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(b_):
+        for h in range(hq):
+            g = h // group
+            for i0 in range(0, sq, row_chunk):
+                rows = np.arange(i0, min(sq, i0 + row_chunk))
+                a, bk_, bv = attention_bwd_rows(q[b, h, rows], k[b, g], v[b, g], do[b, h, rows],
+                                                mask_rows(h, rows), scale, soft_cap)
+                dq[b, h, rows] = a
+                dk[b, g] += bk_
+                dv[b, g] += bv
+    return dq, dk, dv

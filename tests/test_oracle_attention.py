@@ -308,3 +308,75 @@ def test_merge_ignores_output_of_inactive_part():
     o, l = oatt.merge(o_a, l_a, o_b, l_b)
     np.testing.assert_array_equal(o, [[1.0, 2.0], [0.0, 0.0]])
     np.testing.assert_array_equal(l, [0.5, -np.inf])
+
+
+# ---- backward ----
+
+def _torch_forward(q, k, v, allowed, scale, cap):
+    """The attention definition in torch float64 ops, for autograd to
+    differentiate (rows with no allowed key are left out of the check)."""
+    s = scale * (q @ k.transpose(-1, -2))
+    if cap is not None:
+        s = cap * torch.tanh(s / cap)
+    s = s.masked_fill(~allowed, float("-inf"))
+    return torch.softmax(s, dim=-1) @ v
+
+
+@pytest.mark.parametrize("kind,kw,cap", [
+    ("causal", {}, None), ("local", dict(left=4, right=2), None), ("chunked", dict(chunk=5), 2.0),
+    ("dense", {}, 1.5),
+])
+def test_bwd_equals_torch_autograd(kind, kw, cap):
+    """The hand-derived gradients against torch autograd of the forward
+    definition, float64 (GQA: two query heads per kv head)."""
+    rng = np.random.default_rng(16)
+    sq, skv, d = 14, 14, 8
+    q, k, v = _rand(rng, 1, 4, sq, d), _rand(rng, 1, 2, skv, d), _rand(rng, 1, 2, skv, 6)
+    do = _rand(rng, 1, 4, sq, 6)
+    if kind == "dense":
+        m = rng.random((1, sq, skv)) < 0.4
+        m[0, :, 0] = True
+    else:
+        m = omasks.materialize(kind, sq, skv, **kw)
+    dq, dk, dv = oatt.attention_bwd(q, k, v, do, _rows_fn(m), soft_cap=cap)
+    tq = torch.from_numpy(q).requires_grad_()
+    tk = torch.from_numpy(k).requires_grad_()
+    tv = torch.from_numpy(v).requires_grad_()
+    allowed = torch.from_numpy(m)[None]
+    o = _torch_forward(tq, tk.repeat_interleave(2, dim=1), tv.repeat_interleave(2, dim=1), allowed,
+                       d ** -0.5, cap)
+    o.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_bwd_finite_differences():
+    """Central differences of L = <do, attention(q, k, v)> in float64, soft
+    cap on, a row with no allowed key: its gradients are zero."""
+    rng = np.random.default_rng(17)
+    sq, skv, d = 5, 6, 4
+    q, k, v = _rand(rng, 1, 1, sq, d), _rand(rng, 1, 1, skv, d), _rand(rng, 1, 1, skv, 3)
+    do = _rand(rng, 1, 1, sq, 3)
+    m = rng.random((1, sq, skv)) < 0.6
+    m[0, :, 1] = True
+    m[0, 2] = False
+    fn = _rows_fn(m)
+    dq, dk, dv = oatt.attention_bwd(q, k, v, do, fn, soft_cap=1.7)
+
+    def loss(qq, kk, vv):
+        o, _ = oatt.attention(qq, kk, vv, fn, soft_cap=1.7)
+        return float((o * do).sum())
+    eps = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            save = arr[idx]
+            arr[idx] = save + eps
+            lp = loss(q, k, v)
+            arr[idx] = save - eps
+            lm = loss(q, k, v)
+            arr[idx] = save
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=0, atol=1e-8)
+    assert np.all(dq[0, 0, 2] == 0)
