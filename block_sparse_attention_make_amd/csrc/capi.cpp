@@ -2,6 +2,8 @@
 // the forward kernel.  Declarations and contracts are in include/splash.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <initializer_list>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -46,6 +48,12 @@ void free_copy(DeviceCopy &dc) {
   if (dc.mask_bits) (void)hipFree(dc.mask_bits);
   dc.mask_bits = nullptr;
   dc.mask_bits_bytes = 0;
+  for (int32_t **c : {&dc.col_n, &dc.col_ent, &dc.col_mn}) {
+    if (*c) (void)hipFree(*c);
+    *c = nullptr;
+  }
+  dc.has_cols = false;
+  dc.col_w = 0;
   dc.device = -1;
   if (prev >= 0) (void)hipSetDevice(prev);
 }
@@ -117,6 +125,68 @@ splash_status ensure_device_copy(splash_mask_info *mi, DeviceCopy **out) {
   return SPLASH_OK;
 }
 
+int64_t host_index(const HostArray &a, int64_t i) {
+  const uint8_t *p = a.bytes.data();
+  if (a.elem_bits == 8) return static_cast<int8_t>(p[i]);
+  if (a.elem_bits == 16) {
+    int16_t x;
+    std::memcpy(&x, p + 2 * i, 2);
+    return x;
+  }
+  int32_t x;
+  std::memcpy(&x, p + 4 * i, 4);
+  return x;
+}
+
+// The transposed block lists of the backward's key-major kernel, on the
+// device copy `dc` (already uploaded).  Called under the MaskInfo's lock.
+splash_status ensure_cols(splash_mask_info *mi, DeviceCopy &dc) {
+  if (dc.has_cols) return SPLASH_OK;
+  const int64_t hm = mi->num_heads, nq = mi->nq, nk = mi->nk, W = mi->width;
+  const HostArray &bm = mi->arr[SPLASH_MI_BLOCK_MASK], &dn = mi->arr[SPLASH_MI_DATA_NEXT];
+  const HostArray &mn = mi->arr[SPLASH_MI_MASK_NEXT];
+  std::vector<std::vector<int32_t>> ent(static_cast<size_t>(hm * nk)), pm(static_cast<size_t>(hm * nk));
+  for (int64_t h = 0; h < hm; ++h)
+    for (int64_t r = 0; r < nq; ++r)
+      for (int64_t s = 0; s < W; ++s) {
+        const int64_t at = (h * nq + r) * W + s;
+        const int64_t label = host_index(bm, at);
+        if (label <= 0) continue;
+        const int64_t c = host_index(dn, at);
+        ent[h * nk + c].push_back(static_cast<int32_t>(r | (label << 30)));
+        pm[h * nk + c].push_back(mn.present ? static_cast<int32_t>(host_index(mn, at)) : 0);
+      }
+  int64_t w = 1;
+  for (const auto &e : ent) w = std::max<int64_t>(w, static_cast<int64_t>(e.size()));
+  std::vector<int32_t> n(static_cast<size_t>(std::max<int64_t>(hm * nk, 1)), 0);
+  std::vector<int32_t> flat(static_cast<size_t>(std::max<int64_t>(hm * nk, 1) * w), 0), flat_mn(flat.size(), 0);
+  for (int64_t i = 0; i < hm * nk; ++i) {
+    n[i] = static_cast<int32_t>(ent[i].size());
+    for (size_t e = 0; e < ent[i].size(); ++e) {
+      flat[i * w + e] = ent[i][e];
+      flat_mn[i * w + e] = pm[i][e];
+    }
+  }
+  hipError_t e = hipSuccess;
+  int32_t **dst[3] = {&dc.col_n, &dc.col_ent, &dc.col_mn};
+  const std::vector<int32_t> *src[3] = {&n, &flat, &flat_mn};
+  for (int i = 0; i < 3 && e == hipSuccess; ++i) {
+    const size_t nb = src[i]->size() * sizeof(int32_t);
+    e = hipMalloc(reinterpret_cast<void **>(dst[i]), nb);
+    if (e == hipSuccess) e = hipMemcpy(*dst[i], src[i]->data(), nb, hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) {
+    for (int i = 0; i < 3; ++i) {
+      if (*dst[i]) (void)hipFree(*dst[i]);
+      *dst[i] = nullptr;
+    }
+    return hip_fail(e, "uploading the transposed block lists");
+  }
+  dc.col_w = static_cast<int32_t>(w);
+  dc.has_cols = true;
+  return SPLASH_OK;
+}
+
 }  // namespace
 }  // namespace splash
 
@@ -162,12 +232,9 @@ extern "C" SPLASH_API splash_status splash_mask_info_read_device(const splash_ma
 
 namespace {
 
-splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const void *v, void *out,
-                       float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
-                       int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
-                       float logits_soft_cap, const float *aux, int32_t aux_heads,
-                       int32_t num_sinks, void *hip_stream) {
-  // ---- validation: nothing below launches or allocates until all passes ----
+// Checks shared by the forward and the backward entry points.
+splash_status validate_call(const splash_mask_info *mi, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                            int64_t Skv, int64_t D, int64_t Dv, int32_t dtype, float softmax_scale) {
   if (!mi) return fail(SPLASH_EINVAL, "MaskInfo is NULL");
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || D <= 0 || Dv <= 0)
     return fail(SPLASH_EINVAL, "negative size or non-positive head dim");
@@ -181,32 +248,24 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
   if (!(std::isnan(softmax_scale) || (std::isfinite(softmax_scale) && softmax_scale > 0.f)))
     return fail(SPLASH_EINVAL, "softmax_scale must be NaN (default) or finite and > 0");
   if (mi->block_q != 128 || mi->block_kv != 128)
-    return fail(SPLASH_EUNSUPPORTED, "the forward kernel runs 128 x 128 MaskInfo blocks");
+    return fail(SPLASH_EUNSUPPORTED, "the kernels run 128 x 128 MaskInfo blocks");
   if (D != Dv || (D != 64 && D != 128))
     return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
-  if (num_sinks < 0) return fail(SPLASH_EINVAL, "num_sinks must be >= 0");
-  if (num_sinks > 0) {
-    if (!aux) return fail(SPLASH_EINVAL, "softmax_aux is NULL with num_sinks > 0");
-    if (aux_heads != 1 && aux_heads != Hkv && aux_heads != Hq)
-      return fail(SPLASH_EINVAL, "softmax_aux must have 1, Hkv or Hq rows");
-    if (reinterpret_cast<uintptr_t>(aux) % 4 != 0) return fail(SPLASH_EINVAL, "softmax_aux must be 4-byte aligned");
-  }
-  if (B == 0 || Hq == 0 || Sq == 0) return SPLASH_OK;
-  if (!q || !out || (Skv > 0 && (!k || !v)))
-    return fail(SPLASH_EINVAL, "NULL tensor pointer");
   const int64_t n_wg = B * Hq * mi->nq;
-  if (n_wg > 0x7fffffffLL || B * Hq > 0x7fffffffLL)
+  if (n_wg > 0x7fffffffLL || B * Hq > 0x7fffffffLL || B * Hkv * mi->nk > 0x7fffffffLL)
     return fail(SPLASH_EUNSUPPORTED, "grid too large");
-  const size_t elt = dtype == SPLASH_BF16 ? 2 : 4;
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
-       reinterpret_cast<uintptr_t>(out)) % 16 != 0)
-    return fail(SPLASH_EINVAL, "q, k, v and out must be 16-byte aligned");
-  (void)elt;
+  return SPLASH_OK;
+}
 
-  DeviceCopy *dc = nullptr;
-  splash_status st = ensure_device_copy(mi, &dc);
-  if (st != SPLASH_OK) return st;
+bool aligned16(std::initializer_list<const void *> ptrs) {
+  uintptr_t acc = 0;
+  for (const void *p : ptrs) acc |= reinterpret_cast<uintptr_t>(p);
+  return acc % 16 == 0;
+}
 
+FwdParams make_params(const splash_mask_info *mi, const DeviceCopy *dc, const void *q, const void *k,
+                      const void *v, void *out, float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                      int64_t Skv, int64_t D, float scale, float logits_soft_cap) {
   FwdParams p{};
   p.q = q;
   p.k = k;
@@ -240,14 +299,45 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
   p.chunk = mi->chunk;
   p.kv_offset = mi->kv_offset;
   p.dense = mi->kind == SPLASH_MASK_DENSE;
-  const float scale = std::isnan(softmax_scale) ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D)))
-                                                : softmax_scale;
   const bool cap = std::isfinite(logits_soft_cap) && logits_soft_cap > 0.f;
   p.cap = cap;
   const double log2e = 1.4426950408889634;
   p.c2 = cap ? static_cast<float>(static_cast<double>(scale) / logits_soft_cap)
              : static_cast<float>(scale * log2e);
   p.cap_out = cap ? static_cast<float>(logits_soft_cap * log2e) : 0.f;
+  return p;
+}
+
+float resolve_scale(float softmax_scale, int64_t D) {
+  return std::isnan(softmax_scale) ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D))) : softmax_scale;
+}
+
+splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const void *v, void *out,
+                       float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
+                       int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
+                       float logits_soft_cap, const float *aux, int32_t aux_heads,
+                       int32_t num_sinks, void *hip_stream) {
+  // ---- validation: nothing below launches or allocates until all passes ----
+  splash_status st = validate_call(mi, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale);
+  if (st != SPLASH_OK) return st;
+  if (num_sinks < 0) return fail(SPLASH_EINVAL, "num_sinks must be >= 0");
+  if (num_sinks > 0) {
+    if (!aux) return fail(SPLASH_EINVAL, "softmax_aux is NULL with num_sinks > 0");
+    if (aux_heads != 1 && aux_heads != Hkv && aux_heads != Hq)
+      return fail(SPLASH_EINVAL, "softmax_aux must have 1, Hkv or Hq rows");
+    if (reinterpret_cast<uintptr_t>(aux) % 4 != 0) return fail(SPLASH_EINVAL, "softmax_aux must be 4-byte aligned");
+  }
+  if (B == 0 || Hq == 0 || Sq == 0) return SPLASH_OK;
+  if (!q || !out || (Skv > 0 && (!k || !v)))
+    return fail(SPLASH_EINVAL, "NULL tensor pointer");
+  if (!aligned16({q, k, v, out})) return fail(SPLASH_EINVAL, "q, k, v and out must be 16-byte aligned");
+
+  DeviceCopy *dc = nullptr;
+  st = ensure_device_copy(mi, &dc);
+  if (st != SPLASH_OK) return st;
+
+  FwdParams p = make_params(mi, dc, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, resolve_scale(softmax_scale, D),
+                            logits_soft_cap);
   p.aux = num_sinks > 0 ? aux : nullptr;
   p.aux_heads = num_sinks > 0 ? aux_heads : 0;
   p.num_sinks = num_sinks;
@@ -302,6 +392,53 @@ extern "C" SPLASH_API splash_status splash_lse_merge(const void *out_a, const fl
   hipError_t e = launch_lse_merge(out_a, lse_a, dtype_a == SPLASH_BF16 ? 0 : 1, out_b, lse_b,
                                   dtype_b == SPLASH_BF16 ? 0 : 1, out, lse, dtype_out == SPLASH_BF16 ? 0 : 1,
                                   rows, static_cast<int>(Dv), static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return SPLASH_OK;
+}
+
+extern "C" SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void *q, const void *k, const void *v,
+                                               const void *out, const float *lse, const void *dout, void *dq,
+                                               void *dk, void *dv, float *delta, int64_t B, int64_t Hq,
+                                               int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D, int64_t Dv,
+                                               int32_t dtype, float softmax_scale, float logits_soft_cap,
+                                               void *hip_stream) {
+  clear_error();
+  // ---- validation: nothing below launches or allocates until all passes ----
+  splash_status st = validate_call(mi, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale);
+  if (st != SPLASH_OK) return st;
+  if (dtype != SPLASH_BF16) return fail(SPLASH_EUNSUPPORTED, "the backward kernels run bf16 only");
+  if (B == 0 || Hq == 0 || (Sq == 0 && Skv == 0)) return SPLASH_OK;
+  if (Sq > 0 && (!q || !out || !lse || !dout || !dq || !delta)) return fail(SPLASH_EINVAL, "NULL tensor pointer");
+  if (Skv > 0 && (!k || !v || !dk || !dv)) return fail(SPLASH_EINVAL, "NULL tensor pointer");
+  if (!aligned16({q, k, v, out, dout, dq, dk, dv}))
+    return fail(SPLASH_EINVAL, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) % 4 || reinterpret_cast<uintptr_t>(delta) % 4)
+    return fail(SPLASH_EINVAL, "lse and delta must be 4-byte aligned");
+
+  DeviceCopy *dc = nullptr;
+  st = ensure_device_copy(mi, &dc);
+  if (st != SPLASH_OK) return st;
+  {
+    std::lock_guard<std::mutex> lock(mi->mu);
+    st = ensure_cols(mi, *dc);
+  }
+  if (st != SPLASH_OK) return st;
+
+  BwdParams p{};
+  p.f = make_params(mi, dc, q, k, v, const_cast<void *>(out), const_cast<float *>(lse), B, Hq, Hkv, Sq, Skv, D,
+                    resolve_scale(softmax_scale, D), logits_soft_cap);
+  p.dout = dout;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.scale = resolve_scale(softmax_scale, D);
+  p.nk = static_cast<int32_t>(mi->nk);
+  p.col_n = dc->col_n;
+  p.col_ent = dc->col_ent;
+  p.col_mn = dc->col_mn;
+  p.col_w = dc->col_w;
+  hipError_t e = launch_bwd(p, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return SPLASH_OK;
 }

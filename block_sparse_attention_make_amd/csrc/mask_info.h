@@ -38,6 +38,13 @@ struct DeviceCopy {
   // the block width is not a multiple of 32.
   uint32_t *mask_bits = nullptr;
   int64_t mask_bits_bytes = 0;
+  // Transposed block lists for the key-major backward kernel, made on the
+  // first backward call: for mask head hm and key block c, col_n[hm * nk + c]
+  // entries col_ent[(hm * nk + c) * col_w + e] = r | label << 30, query block
+  // rows in ascending order, and col_mn[...] their partial block (dense).
+  bool has_cols = false;
+  int32_t *col_n = nullptr, *col_ent = nullptr, *col_mn = nullptr;
+  int32_t col_w = 0;
 };
 
 }  // namespace splash

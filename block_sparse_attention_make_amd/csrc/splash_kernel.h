@@ -37,4 +37,23 @@ struct FwdParams {
 // dtype: 0 = bf16, 1 = f32.  D in {64, 128}.  Returns hipGetLastError().
 hipError_t launch_fwd(const FwdParams &p, int dtype, hipStream_t stream);
 
+// Backward launch parameters (bf16 only).  The forward's MaskInfo fields
+// (`f`) drive the query-major dQ kernel; the key-major dK/dV kernel walks the
+// transposed lists: for mask head hm and key block c, col_n[hm * nk + c]
+// entries col_ent[(hm * nk + c) * col_w + e] = r | label << 30 (query block
+// rows in ascending order) with, for dense masks, the partial block index
+// col_mn[...] of each.
+struct BwdParams {
+  FwdParams f;            // q, k, v, out, lse (read), sizes, mask fields, c2 / cap_out / cap
+  const void *dout;       // gradient of out, [B, Hq, Sq, Dv]
+  float *delta;           // workspace [B, Hq, Sq]: <dout_i, out_i>
+  void *dq, *dk, *dv;     // outputs, shaped like q, k, v
+  float scale;            // softmax scale (applied to dq and dk)
+  int32_t nk;             // key blocks
+  const int32_t *col_n, *col_ent, *col_mn;
+  int32_t col_w;
+};
+
+hipError_t launch_bwd(const BwdParams &p, hipStream_t stream);
+
 }  // namespace splash

@@ -75,6 +75,9 @@ def load_library(path=None):
     lib.splash_make_mask_info_kv_slice.restype = ctypes.c_int
     lib.splash_lse_merge.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, i32, i64, i64, vp]
     lib.splash_lse_merge.restype = ctypes.c_int
+    lib.splash_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                               i32, ctypes.c_float, ctypes.c_float, vp]
+    lib.splash_bwd.restype = ctypes.c_int
     lib.splash_last_error.argtypes = []
     lib.splash_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -311,3 +314,80 @@ def splash_fwd_kv_sharded(q, k_shards, v_shards, mask_infos, softmax_scale=None,
             if (last or acc.dtype != torch.float32) else acc
         acc, lse = lse_merge(acc, lse, o_s, l_s, out=dst, lse=lse, stream=stream)
     return acc, lse
+
+
+def splash_bwd(q, k, v, out, lse, dout, mask_info, softmax_scale=None, logits_soft_cap=None,
+               dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Gradients (dq, dk, dv) of splash_fwd's output for the output gradient
+    dout (bf16 GPU tensors, contiguous BHSD; lse is splash_fwd's).  delta is
+    an optional float32 [B, Hq, Sq] workspace."""
+    import torch
+    lib = load_library()
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the backward runs bf16 only")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if not (t.is_cuda and t.is_contiguous() and t.dim() == 4 and t.dtype == torch.bfloat16):
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor [B, H, S, D]")
+    if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be splash_fwd's float32 [B, Hq, Sq]")
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if out.shape != (B, Hq, Sq, Dv) or dout.shape != out.shape or lse.shape != (B, Hq, Sq):
+        raise ValueError("out / dout / lse shapes do not match q")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    scale = math.nan if softmax_scale is None else float(softmax_scale)
+    cap = 0.0 if logits_soft_cap is None else float(logits_soft_cap)
+    with torch.cuda.device(q.device):
+        st = lib.splash_bwd(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            delta.data_ptr(), B, Hq, Hkv, Sq, Skv, D, Dv, BF16, scale, cap,
+                            ctypes.c_void_p(stream.cuda_stream))
+    _check(lib, st)
+    return dq, dk, dv
+
+
+def splash_attention(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None):
+    """Differentiable splash attention (bf16): forward through splash_fwd,
+    backward through splash_bwd, as a torch.autograd.Function."""
+    return _SplashFn.apply(q, k, v, mask_info, softmax_scale, logits_soft_cap)
+
+
+def _make_fn():
+    import torch
+
+    class SplashFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, mask_info, softmax_scale, logits_soft_cap):
+            out, lse = splash_fwd(q.contiguous(), k.contiguous(), v.contiguous(), mask_info,
+                                  softmax_scale=softmax_scale, logits_soft_cap=logits_soft_cap)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.mask_info, ctx.scale, ctx.cap = mask_info, softmax_scale, logits_soft_cap
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse = ctx.saved_tensors
+            dq, dk, dv = splash_bwd(q.contiguous(), k.contiguous(), v.contiguous(), out, lse,
+                                    dout.contiguous(), ctx.mask_info, softmax_scale=ctx.scale,
+                                    logits_soft_cap=ctx.cap)
+            return dq, dk, dv, None, None, None
+
+    return SplashFn
+
+
+class _LazyFn:
+    _fn = None
+
+    def apply(self, *a):
+        if _LazyFn._fn is None:
+            _LazyFn._fn = _make_fn()
+        return _LazyFn._fn.apply(*a)
+
+
+_SplashFn = _LazyFn()

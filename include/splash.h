@@ -258,6 +258,36 @@ SPLASH_API splash_status splash_lse_merge(const void *out_a, const float *lse_a,
                                           void *out, float *lse, int32_t dtype_out, int64_t rows,
                                           int64_t Dv, void *hip_stream);
 
+/* Backward of splash_fwd (no sinks): the gradients dq, dk, dv of the output
+ * for the output gradient dout, as the pallas flash attention page describes
+ * the flash backward (FAQ "What does the TPU flash attention kernel save for
+ * the backward pass?", "Why does the TPU flash attention backward pass run
+ * two kernels instead of one?"): the weights are rebuilt from q, k and the
+ * forward's lse, di = <dout_i, out_i> is formed once into `delta`, then a
+ * key-major kernel (one workgroup per key block, over the query blocks of
+ * every query head of its GQA group that the MaskInfo's transposed block
+ * lists give) writes dk and dv, and a query-major kernel (one workgroup per
+ * query block, over the MaskInfo row) writes dq.  With s' the scaled (or
+ * soft-capped) logit and p_ij = exp(s'_ij - lse_i) on allowed pairs:
+ *   dv_j = sum_i p_ij dout_i,  ds_ij = p_ij (<dout_i, v_j> - di_i) g_ij
+ *   (g = 1, or 1 - tanh^2 under the cap),  dq_i = scale sum_j ds_ij k_j,
+ *   dk_j = scale sum_i ds_ij q_i  (summed over the group's query heads).
+ *
+ * q, k, v, out, lse: as passed to and returned by splash_fwd for the same
+ * MaskInfo, scale and cap (lse is required).  dout: DEVICE [B, Hq, Sq, Dv].
+ * dq, dk, dv: DEVICE outputs shaped like q, k, v, fully overwritten (key
+ * blocks no query sees get zeros).  delta: DEVICE float32 workspace of
+ * B * Hq * Sq elements, overwritten.  All caller-owned, 16-byte aligned
+ * (lse and delta 4-byte), valid until the kernels end.  bf16 only (float32
+ * returns SPLASH_EUNSUPPORTED); other requirements as splash_fwd.  The first
+ * backward call on a device also uploads the transposed block lists of the
+ * MaskInfo; later calls allocate nothing.  Asynchronous on hip_stream. */
+SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void *q, const void *k, const void *v,
+                                    const void *out, const float *lse, const void *dout, void *dq, void *dk,
+                                    void *dv, float *delta, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                                    int64_t Skv, int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
+                                    float logits_soft_cap, void *hip_stream);
+
 /* Message of the last failed call on this thread ("" if none).  The string
  * stays valid until the next library call on this thread. */
 SPLASH_API const char *splash_last_error(void);

@@ -21,7 +21,7 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "splash_fwd", "splash_fwd_sinks", "splash_last_error", "splash_lse_merge",
+        "splash_bwd", "splash_fwd", "splash_fwd_sinks", "splash_last_error", "splash_lse_merge",
         "splash_make_mask_info", "splash_make_mask_info_kv_slice", "splash_mask_info_destroy",
         "splash_mask_info_read_device", "splash_mask_info_upload", "splash_mask_info_view"])
 
