@@ -1,7 +1,7 @@
 """Benchmark: splash-attention forward TFLOP/s on computed blocks (MI355X).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--sinks N] [--kv-shards P]
+                    [--sinks N] [--kv-shards P] [--backward]
 
 A step is one splash_fwd call (the whole forward path: block walk over the
 MaskInfo, K/V staging, QK^T, soft cap, masking, online softmax, PV, epilogue)
@@ -20,6 +20,12 @@ part of ring attention instead: P splash_fwd calls on key-sliced MaskInfos
 plus P - 1 lse merges into a float32 accumulator (the computed blocks, and so
 the FLOPs, are the same).  It also times the merge kernel alone and reports
 its HBM roofline under "merge".
+--backward times splash_bwd instead (the forward runs once beforehand): a
+step is the delta kernel, the key-major dK/dV kernel and the query-major dQ
+kernel.  Its FLOPs are the usual backward count, 5 products of
+2 * 128 * 128 * D per computed block (S recomputed, dP, dV, dQ, dK);
+roofline.achieved counts the 7 products the two kernels execute (S and dP
+are formed in both).
 """
 import argparse
 import hashlib
@@ -126,6 +132,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--sinks", type=int, default=0, help="attention-sink logits per kv head")
     ap.add_argument("--kv-shards", type=int, default=1, help="time the key/value-sharded path")
+    ap.add_argument("--backward", action="store_true", help="time splash_bwd")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -138,8 +145,8 @@ def main():
     import numpy as np
     import torch
 
-    from block_sparse_attention_make_amd import (lse_merge, make_mask_info, splash_fwd, splash_fwd_kv_sharded,
-                                                 synthetic)
+    from block_sparse_attention_make_amd import (lse_merge, make_mask_info, splash_bwd, splash_fwd,
+                                                 splash_fwd_kv_sharded, synthetic)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -171,6 +178,11 @@ def main():
     blocks_total = nq * nk * w.Hq * w.B
     flops = blocks_computed * flops_per_block(w)
     flops_dense = w.B * w.Hq * w.Sq * w.Skv * 2 * (w.D + w.Dv)
+    flops_exec = flops
+    if args.backward:
+        flops = blocks_computed * 5 * 2 * w.block * w.block * w.D
+        flops_exec = blocks_computed * 7 * 2 * w.block * w.block * w.D
+        flops_dense = w.B * w.Hq * w.Sq * w.Skv * 5 * 2 * w.D
 
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty((w.B, w.Hq, w.Sq, w.Dv), dtype=q.dtype, device=dev)
@@ -196,8 +208,21 @@ def main():
         ks = [kd[:, :, s * n:(s + 1) * n].contiguous() for s in range(P)]
         vs = [vd[:, :, s * n:(s + 1) * n].contiguous() for s in range(P)]
 
+    if args.backward:
+        if w.dtype != "bf16" or P > 1 or args.sinks:
+            print("--backward runs bf16 workloads without shards or sinks", file=sys.stderr)
+            sys.exit(2)
+        splash_fwd(qd, kd, vd, mi, logits_soft_cap=w.soft_cap, out=out, lse=lse, stream=stream)
+        g = torch.Generator().manual_seed(11)
+        dout = torch.randn(out.shape, generator=g).to(q.dtype).to(dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        delta = torch.empty(lse.shape, dtype=torch.float32, device=dev)
+
     def step():
-        if P > 1:
+        if args.backward:
+            splash_bwd(qd, kd, vd, out, lse, dout, mi, logits_soft_cap=w.soft_cap, dq=dq, dk=dk, dv=dv,
+                       delta=delta, stream=stream)
+        elif P > 1:
             splash_fwd_kv_sharded(qd, ks, vs, shard_mis, logits_soft_cap=w.soft_cap, stream=stream)
         else:
             splash_fwd(qd, kd, vd, mi, logits_soft_cap=w.soft_cap, out=out, lse=lse, stream=stream,
@@ -241,12 +266,13 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     kern_avg = float(np.mean(kern_ms))
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kern_avg * 1e-3) / 1e12
+    achieved = flops_exec / (kern_avg * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     traffic = measured_traffic(w.name)
 
     res = {
-        "metric": "splash fwd TFLOP/s on computed blocks + % bf16 MFMA peak; blocks skipped",
+        "metric": ("splash bwd TFLOP/s on computed blocks (5 products per block)" if args.backward else
+                   "splash fwd TFLOP/s on computed blocks + % bf16 MFMA peak; blocks skipped"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -261,7 +287,7 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "seq_len": w.Sq, "head_dim": w.D, "mask": m.kind, "block": w.block,
                    "soft_cap": w.soft_cap, "parallelism": "single-gpu",
-                   "sinks_per_kv_head": args.sinks, "kv_shards": P},
+                   "sinks_per_kv_head": args.sinks, "kv_shards": P, "pass": "backward" if args.backward else "forward"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "dense_equiv_tflops": round(flops_dense / (ms_per_step * 1e-3) / 1e12, 2),
         "blocks_skipped": blocks_total - blocks_computed,
@@ -277,12 +303,17 @@ def main():
                      "kernel_ms_avg": round(kern_avg, 5)},
         "cpu_baseline": None,
     }
+    if args.backward:
+        res["roofline"]["kernel"] = "bwd_delta + bwd_dkdv + bwd_dq (executed products: 7 per block)"
+        res["roofline"]["flops_per_launch"] = flops_exec
+        res["roofline"]["traffic"] = None
+        res["vs_baseline"] = None
     if merge_info is not None:
         res["merge"] = merge_info
         # with shards the timed step holds several kernels: achieved is per step, not per launch
         res["roofline"]["kernel"] = "splash_fwd_wide x P + lse_merge_kernel x (P-1)"
         res["roofline"]["traffic"] = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.backward and P == 1 and not args.sinks:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, dense, bm, args.cpu_budget)
     print(json.dumps(res), flush=True)
 
