@@ -48,7 +48,7 @@ void free_copy(DeviceCopy &dc) {
   if (dc.mask_bits) (void)hipFree(dc.mask_bits);
   dc.mask_bits = nullptr;
   dc.mask_bits_bytes = 0;
-  for (int32_t **c : {&dc.col_n, &dc.col_ent, &dc.col_mn}) {
+  for (int32_t **c : {&dc.col_n, &dc.col_ent, &dc.col_mn, &dc.col_order}) {
     if (*c) (void)hipFree(*c);
     *c = nullptr;
   }
@@ -167,16 +167,23 @@ splash_status ensure_cols(splash_mask_info *mi, DeviceCopy &dc) {
       flat_mn[i * w + e] = pm[i][e];
     }
   }
+  // Launch order of the key-major kernel: longest lists first.
+  std::vector<int64_t> work(static_cast<size_t>(std::max<int64_t>(nk, 1)), 0);
+  for (int64_t h = 0; h < hm; ++h)
+    for (int64_t c = 0; c < nk; ++c) work[c] += static_cast<int64_t>(ent[h * nk + c].size());
+  std::vector<int32_t> order(static_cast<size_t>(std::max<int64_t>(nk, 1)), 0);
+  for (int64_t c = 0; c < nk; ++c) order[c] = static_cast<int32_t>(c);
+  std::stable_sort(order.begin(), order.begin() + nk, [&](int32_t a, int32_t b2) { return work[a] > work[b2]; });
   hipError_t e = hipSuccess;
-  int32_t **dst[3] = {&dc.col_n, &dc.col_ent, &dc.col_mn};
-  const std::vector<int32_t> *src[3] = {&n, &flat, &flat_mn};
-  for (int i = 0; i < 3 && e == hipSuccess; ++i) {
+  int32_t **dst[4] = {&dc.col_n, &dc.col_ent, &dc.col_mn, &dc.col_order};
+  const std::vector<int32_t> *src[4] = {&n, &flat, &flat_mn, &order};
+  for (int i = 0; i < 4 && e == hipSuccess; ++i) {
     const size_t nb = src[i]->size() * sizeof(int32_t);
     e = hipMalloc(reinterpret_cast<void **>(dst[i]), nb);
     if (e == hipSuccess) e = hipMemcpy(*dst[i], src[i]->data(), nb, hipMemcpyHostToDevice);
   }
   if (e != hipSuccess) {
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < 4; ++i) {
       if (*dst[i]) (void)hipFree(*dst[i]);
       *dst[i] = nullptr;
     }
@@ -437,6 +444,7 @@ extern "C" SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void 
   p.col_n = dc->col_n;
   p.col_ent = dc->col_ent;
   p.col_mn = dc->col_mn;
+  p.col_order = dc->col_order;
   p.col_w = dc->col_w;
   hipError_t e = launch_bwd(p, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));

@@ -44,6 +44,7 @@ struct DeviceCopy {
   // rows in ascending order, and col_mn[...] their partial block (dense).
   bool has_cols = false;
   int32_t *col_n = nullptr, *col_ent = nullptr, *col_mn = nullptr;
+  int32_t *col_order = nullptr;   // key blocks by descending list length (over mask heads)
   int32_t col_w = 0;
 };
 

@@ -176,24 +176,111 @@ __global__ __launch_bounds__(256) void bwd_delta(const __bf16 *o, const __bf16 *
   if (row < rows && (t % kPerRow) == 0) delta[row] = acc;
 }
 
+// ---- staging ----------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes at `base`; uniform, kept in SGPRs.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, int64_t bytes) {
+  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+  i32x4 v;
+  __builtin_memcpy(&v, &r, sizeof(v));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  return v;
+}
+
+// Offset within its 1 KiB segment of the 16 bytes lane `lane` moves for
+// segment `seg` of a tile: the lane that lands on chunk pc of a row fetches
+// the row's logical chunk pc ^ swz(row), so the tile comes out swizzled.
+template <int D>
+__device__ __forceinline__ uint32_t seg_voff(int seg, int lane) {
+  using T = BTile<D>;
+  constexpr int kRowsPerSeg = 1024 / T::kRowBytes;
+  const int rin = lane / T::kChunks;
+  const int row = seg * kRowsPerSeg + rin;
+  const int c = (lane % T::kChunks) ^ T::swz(row);
+  return static_cast<uint32_t>(rin * T::kRowBytes + c * 16);
+}
+
+// Direct-to-LDS loads (buffer_load_dwordx4 ... lds) of this wave's quarter of
+// a 128-row tile starting at byte `goff` of the resource: segments
+// 4 g + 0..3 of the wave's share, one M0 per group of four (the instruction
+// offset advances both the LDS and the global address).  Issued from inline
+// assembly, awaited with an explicit vmcnt wait before the barrier that
+// publishes the buffer.
+template <int D>
+__device__ __forceinline__ void issue_tile(char *lds, i32x4 res, uint32_t goff, int wave, int lane) {
+  constexpr int kSegs = BTile<D>::kBytes / 1024 / 4;   // per wave
+#pragma unroll
+  for (int g = 0; g < kSegs / 4; ++g) {
+    const int seg0 = wave * kSegs + 4 * g;
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) char *)(lds + seg0 * 1024)));
+    const uint32_t soff = goff + static_cast<uint32_t>(seg0 * 1024);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
+        :: "s"(m0), "v"(seg_voff<D>(seg0, lane)), "v"(seg_voff<D>(seg0 + 1, lane)),
+           "v"(seg_voff<D>(seg0 + 2, lane)), "v"(seg_voff<D>(seg0 + 3, lane)), "s"(res), "s"(soff)
+        : "memory", "m0");
+#pragma clang diagnostic pop
+  }
+}
+
+__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Computable masks: the key interval [lo, hi] of query position qpos in the
+// MaskInfo's key coordinates.
+__device__ __forceinline__ void key_interval(const FwdParams &f, int64_t qpos, int64_t &lo, int64_t &hi) {
+  const int64_t big = int64_t(1) << 40;
+  if (f.mask_kind == 0) { lo = -big; hi = qpos; }
+  else if (f.mask_kind == 1) { lo = f.left < 0 ? -big : qpos - f.left; hi = f.right < 0 ? big : qpos + f.right; }
+  else { lo = (qpos / f.chunk) * f.chunk; hi = qpos; }
+  lo -= f.kv_offset;
+  hi -= f.kv_offset;
+}
+
+// Workgroup id -> (batch-head unit, rank): consecutive ids go round-robin
+// over the 8 XCDs, and XCD x gets a contiguous range of units so a unit's
+// shared operands stay in one L2; ranks (longest work first) vary fastest.
+__device__ __forceinline__ void xcd_map(int pid, int units, int &unit, int &rank) {
+  if ((units & 7) == 0) {
+    const int per = units >> 3, x = pid & 7, j = pid >> 3;
+    unit = x * per + j % per;
+    rank = j / per;
+  } else {
+    unit = pid % units;
+    rank = pid / units;
+  }
+}
+
 // ---- key-major kernel: dK, dV ---------------------------------------------
-// Workgroup (b, hkv, key block c); wave w owns keys 32 w .. 32 w + 31.
+// Workgroup (b, hkv, key block c); wave w owns keys 32 w .. 32 w + 31.  The
+// query blocks to visit -- every (query head g of the group, entry e of the
+// transposed list of mask head hm(g)) -- stream through two LDS buffers: the
+// next block's Q and dO tiles load while the current one is computed.
 template <int D, bool CAP, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
   using T = BTile<D>;
   constexpr int kKS = D / 16, kDT = D / 32;
-  __shared__ __attribute__((aligned(16))) char q_t[T::kBytes];
-  __shared__ __attribute__((aligned(16))) char do_t[T::kBytes];
-  __shared__ __attribute__((aligned(16))) float lse_s[kBlk], di_s[kBlk];
-  __shared__ __attribute__((aligned(16))) int lo_s[kBlk], hi_s[kBlk];
-  __shared__ __attribute__((aligned(16))) unsigned mw_s[4 * kBlk];
+  __shared__ __attribute__((aligned(1024))) char q_t[2][T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char do_t[2][T::kBytes];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][kBlk], di_s[2][kBlk];
+  __shared__ __attribute__((aligned(16))) int lo_s[2][kBlk], hi_s[2][kBlk];
+  __shared__ __attribute__((aligned(16))) unsigned mw_s[2][4 * kBlk];
 
   const FwdParams &f = p.f;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pid = blockIdx.x;
-  const int c = pid % p.nk;
-  const int bh = pid / p.nk;
+  int bh, rank;
+  xcd_map(blockIdx.x, static_cast<int>(f.B * f.Hkv), bh, rank);
+  const int c = p.col_order[rank];
   const int b = bh / static_cast<int>(f.Hkv), hkv = bh % static_cast<int>(f.Hkv);
   const int64_t key0 = static_cast<int64_t>(c) * kBlk + 32 * wave;   // the wave's first key
   const int64_t kv_off = ((static_cast<int64_t>(b) * f.Hkv + hkv) * f.Skv + key0) * D;
@@ -207,101 +294,173 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) dk[dt][v] = dv[dt][v] = 0.f;
 
-  const int key_local = 32 * wave + (lane & 31);   // key of this lane's S column, within the block
-  for (int g = 0; g < f.group; ++g) {
+  // Walk of the (g, e) pairs.
+  auto list_of = [&](int g) -> int64_t {
     const int hq = hkv * f.group + g;
-    const int hm = f.hm == 1 ? 0 : hq;
-    const int64_t lst = static_cast<int64_t>(hm) * p.nk + c;
-    const int n = p.col_n[lst];
-    for (int e = 0; e < n; ++e) {
-      const int ent = p.col_ent[lst * p.col_w + e];
-      const int r = ent & 0x3fffffff, label = static_cast<int>(static_cast<unsigned>(ent) >> 30);
-      const int64_t row_base = (static_cast<int64_t>(b) * f.Hq + hq) * f.Sq + static_cast<int64_t>(r) * kBlk;
-      __syncthreads();   // the previous block's tiles are no longer read
-      stage<D>(q_t, static_cast<const __bf16 *>(f.q) + row_base * D, tid);
-      stage<D>(do_t, static_cast<const __bf16 *>(p.dout) + row_base * D, tid);
-      if (tid < kBlk) {
-        const float l = f.lse[row_base + tid];
-        lse_s[tid] = l * kLog2e;
-        di_s[tid] = p.delta[row_base + tid];
-        if constexpr (!DENSE) {
-          const int64_t qpos = f.q_seq[static_cast<int64_t>(r) * kBlk + tid];
-          const int64_t big = int64_t(1) << 40;
-          int64_t lo, hi;
-          if (f.mask_kind == 0) { lo = -big; hi = qpos; }
-          else if (f.mask_kind == 1) { lo = f.left < 0 ? -big : qpos - f.left; hi = f.right < 0 ? big : qpos + f.right; }
-          else { lo = (qpos / f.chunk) * f.chunk; hi = qpos; }
-          // relative to this key block's first key (in the MaskInfo's key coordinates)
-          const int64_t kb0 = f.kv_offset + static_cast<int64_t>(c) * kBlk;
-          lo -= kb0;
-          hi -= kb0;
-          lo_s[tid] = static_cast<int>(lo < -1 ? -1 : (lo > kBlk ? kBlk : lo));
-          hi_s[tid] = static_cast<int>(hi < -1 ? -1 : (hi > kBlk ? kBlk : hi));
-        }
-      }
-      if constexpr (DENSE) {
-        if (label == 1) {
-          const int mn = p.col_mn[lst * p.col_w + e];
-          for (int i = tid; i < 4 * kBlk; i += kThreads) mw_s[i] = f.pmb_bits[static_cast<int64_t>(mn) * 4 * kBlk + i];
-        }
-      }
-      __syncthreads();
+    return static_cast<int64_t>(f.hm == 1 ? 0 : hq) * p.nk + c;
+  };
+  auto count_of = [&](int g) -> int { return __builtin_amdgcn_readfirstlane(p.col_n[list_of(g)]); };
+  auto advance = [&](int &g, int &e, int &n) {
+    ++e;
+    while (e >= n && g < f.group) {
+      ++g;
+      e = 0;
+      n = g < f.group ? count_of(g) : 0;
+    }
+  };
+  int g = 0, e = -1, n = count_of(0);
+  advance(g, e, n);   // first pair (g == group when there is none)
 
-#pragma unroll 1
-      for (int qb = 0; qb < 4; ++qb) {
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          const bf16x8 aq = read_row<D>(q_t, 32 * qb + (lane & 31), ks, half);
-          const bf16x8 ad = read_row<D>(do_t, 32 * qb + (lane & 31), ks, half);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kb[ks], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vb[ks], dp, 0, 0, 0);
-        }
-        bf16x8 pb[2], sb[2];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qi0 = 32 * qb + 8 * g4 + 4 * half;   // rows of elements 4 g4 .. 4 g4 + 3
-          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[qi0]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&di_s[qi0]);
-          unsigned mword[4] = {0u, 0u, 0u, 0u};
-          int lo4[4] = {0, 0, 0, 0}, hi4[4] = {0, 0, 0, 0};
-          if (label == 1) {
-            if constexpr (DENSE) {
-#pragma unroll
-              for (int k = 0; k < 4; ++k) mword[k] = mw_s[wave * kBlk + qi0 + k];
-            } else {
-#pragma unroll
-              for (int k = 0; k < 4; ++k) { lo4[k] = lo_s[qi0 + k]; hi4[k] = hi_s[qi0 + k]; }
-            }
-          }
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int v = 4 * g4 + k;
-            float s2, gf = 1.f;
-            if constexpr (CAP) capped(s[v], f.c2, f.cap_out, s2, gf);
-            else s2 = s[v] * f.c2;
-            bool ok = l4[k] != -INFINITY;
-            if (label == 1) {
-              if constexpr (DENSE) ok = ok && ((mword[k] >> (lane & 31)) & 1u);
-              else ok = ok && key_local >= lo4[k] && key_local <= hi4[k];
-            }
-            const float pv = ok ? __builtin_amdgcn_exp2f(s2 - l4[k]) : 0.f;
-            const float dsv = pv * (dp[v] - d4[k]) * gf;
-            pb[v / 8][v % 8] = static_cast<__bf16>(pv);
-            sb[v / 8][v % 8] = static_cast<__bf16>(dsv);
-          }
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int dt = 0; dt < kDT; ++dt) {
-            const bf16x8 ado = read_tr<D>(do_t, 32 * qb, h2, dt, lane, half);
-            const bf16x8 aq = read_tr<D>(q_t, 32 * qb, h2, dt, lane, half);
-            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[h2], dv[dt], 0, 0, 0);
-            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[h2], dk[dt], 0, 0, 0);
-          }
+  const int key_local = 32 * wave + (lane & 31);
+  // Small per-block operands of pair (g, e), loaded to registers by the
+  // first 128 threads: lse (base 2), di, and the key interval or mask words.
+  struct Small { float l, d; int lo, hi; unsigned m0, m1; };
+  auto load_small = [&](int gg, int ee, int label, Small &sm) {
+    const int hq = hkv * f.group + gg;
+    const int ent = p.col_ent[list_of(gg) * p.col_w + ee];
+    const int r = ent & 0x3fffffff;
+    const int64_t row_base = (static_cast<int64_t>(b) * f.Hq + hq) * f.Sq + static_cast<int64_t>(r) * kBlk;
+    if (tid < kBlk) {
+      sm.l = f.lse[row_base + tid] * kLog2e;
+      sm.d = p.delta[row_base + tid];
+      if constexpr (!DENSE) {
+        int64_t lo, hi;
+        key_interval(f, f.q_seq[static_cast<int64_t>(r) * kBlk + tid], lo, hi);
+        const int64_t kb0 = static_cast<int64_t>(c) * kBlk;   // relative to this key block
+        lo -= kb0;
+        hi -= kb0;
+        sm.lo = static_cast<int>(lo < -1 ? -1 : (lo > kBlk ? kBlk : lo));
+        sm.hi = static_cast<int>(hi < -1 ? -1 : (hi > kBlk ? kBlk : hi));
       }
     }
+    if constexpr (DENSE) {
+      if (label == 1) {
+        const int mn = p.col_mn[list_of(gg) * p.col_w + ee];
+        const unsigned *src = f.pmb_bits + static_cast<int64_t>(mn) * 4 * kBlk;
+        sm.m0 = src[tid];
+        sm.m1 = src[tid + kThreads];
+      }
+    }
+  };
+  auto store_small = [&](int buf, int label, const Small &sm) {
+    if (tid < kBlk) {
+      lse_s[buf][tid] = sm.l;
+      di_s[buf][tid] = sm.d;
+      if constexpr (!DENSE) {
+        lo_s[buf][tid] = sm.lo;
+        hi_s[buf][tid] = sm.hi;
+      }
+    }
+    if constexpr (DENSE) {
+      if (label == 1) {
+        mw_s[buf][tid] = sm.m0;
+        mw_s[buf][tid + kThreads] = sm.m1;
+      }
+    }
+  };
+  auto entry = [&](int gg, int ee, int &r, int &label) {
+    const int ent = __builtin_amdgcn_readfirstlane(p.col_ent[list_of(gg) * p.col_w + ee]);
+    r = ent & 0x3fffffff;
+    label = static_cast<int>(static_cast<unsigned>(ent) >> 30);
+  };
+  auto issue = [&](int buf, int gg, int r) {
+    const int hq = hkv * f.group + gg;
+    const int64_t head = (static_cast<int64_t>(b) * f.Hq + hq) * f.Sq * D;
+    const i32x4 qr = make_rsrc(static_cast<const __bf16 *>(f.q) + head, f.Sq * D * 2);
+    const i32x4 dr = make_rsrc(static_cast<const __bf16 *>(p.dout) + head, f.Sq * D * 2);
+    const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(r) * T::kBytes);
+    issue_tile<D>(q_t[buf], qr, goff, wave, lane);
+    issue_tile<D>(do_t[buf], dr, goff, wave, lane);
+  };
+
+  int buf = 0;
+  if (g < f.group) {
+    int r, label;
+    entry(g, e, r, label);
+    Small sm{};
+    load_small(g, e, label, sm);
+    store_small(0, label, sm);   // waits for the small loads, issued before any tile load
+    issue(0, g, r);
+  }
+  wait_all_loads();
+  __syncthreads();
+
+  while (g < f.group) {
+    int r, label;
+    entry(g, e, r, label);
+    int g2 = g, e2 = e, n2 = n;
+    advance(g2, e2, n2);
+    const bool more = g2 < f.group;
+    int r2 = 0, label2 = 0;
+    Small sm{};
+    if (more) {
+      entry(g2, e2, r2, label2);
+      load_small(g2, e2, label2, sm);   // before the tile loads: their wait does not wait on those
+      issue(buf ^ 1, g2, r2);
+    }
+
+#pragma unroll 1
+    for (int qb = 0; qb < 4; ++qb) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const bf16x8 aq = read_row<D>(q_t[buf], 32 * qb + (lane & 31), ks, half);
+        const bf16x8 ad = read_row<D>(do_t[buf], 32 * qb + (lane & 31), ks, half);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kb[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vb[ks], dp, 0, 0, 0);
+      }
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qi0 = 32 * qb + 8 * g4 + 4 * half;   // rows of elements 4 g4 .. 4 g4 + 3
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[buf][qi0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&di_s[buf][qi0]);
+        unsigned mword[4] = {0u, 0u, 0u, 0u};
+        int lo4[4] = {0, 0, 0, 0}, hi4[4] = {0, 0, 0, 0};
+        if (label == 1) {
+          if constexpr (DENSE) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) mword[k] = mw_s[buf][wave * kBlk + qi0 + k];
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { lo4[k] = lo_s[buf][qi0 + k]; hi4[k] = hi_s[buf][qi0 + k]; }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int v = 4 * g4 + k;
+          float s2, gf = 1.f;
+          if constexpr (CAP) capped(s[v], f.c2, f.cap_out, s2, gf);
+          else s2 = s[v] * f.c2;
+          bool ok = l4[k] != -INFINITY;
+          if (label == 1) {
+            if constexpr (DENSE) ok = ok && ((mword[k] >> (lane & 31)) & 1u);
+            else ok = ok && key_local >= lo4[k] && key_local <= hi4[k];
+          }
+          const float pv = ok ? __builtin_amdgcn_exp2f(s2 - l4[k]) : 0.f;
+          const float dsv = pv * (dp[v] - d4[k]) * gf;
+          pb[v / 8][v % 8] = static_cast<__bf16>(pv);
+          sb[v / 8][v % 8] = static_cast<__bf16>(dsv);
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) {
+          const bf16x8 ado = read_tr<D>(do_t[buf], 32 * qb, h2, dt, lane, half);
+          const bf16x8 aq = read_tr<D>(q_t[buf], 32 * qb, h2, dt, lane, half);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[h2], dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[h2], dk[dt], 0, 0, 0);
+        }
+    }
+
+    if (more) store_small(buf ^ 1, label2, sm);
+    wait_all_loads();
+    __syncthreads();   // the next buffer is complete; this one is free for the pair after
+    buf ^= 1;
+    g = g2;
+    e = e2;
+    n = n2;
   }
   store_t<D>(static_cast<__bf16 *>(p.dk) + kv_off, dk, p.scale, lane, half);
   store_t<D>(static_cast<__bf16 *>(p.dv) + kv_off, dv, 1.f, lane, half);
@@ -309,20 +468,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
 
 // ---- query-major kernel: dQ -----------------------------------------------
 // Workgroup (b, hq, query block r); wave w owns queries 32 w .. 32 w + 31.
+// The row's non-empty key blocks stream through two LDS buffers.
 template <int D, bool CAP, bool DENSE>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq(const BwdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
   using T = BTile<D>;
   constexpr int kKS = D / 16, kDT = D / 32;
-  __shared__ __attribute__((aligned(16))) char k_t[T::kBytes];
-  __shared__ __attribute__((aligned(16))) char v_t[T::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned mw_s[4 * kBlk];
+  __shared__ __attribute__((aligned(1024))) char k_t[2][T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char v_t[2][T::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned mw_s[2][4 * kBlk];
 
   const FwdParams &f = p.f;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pid = blockIdx.x;
-  const int r = pid % f.nq;
-  const int bh = pid / f.nq;
+  int bh, rank;
+  xcd_map(blockIdx.x, static_cast<int>(f.B * f.Hq), bh, rank);
+  const int r = f.row_order[rank];
   const int b = bh / static_cast<int>(f.Hq), hq = bh % static_cast<int>(f.Hq);
   const int hkv = hq / f.group;
   const int hm = f.hm == 1 ? 0 : hq;
@@ -333,55 +493,81 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(const BwdParams p) {
   bf16x8 qb[kKS], dob[kKS];
   load_rows_b<D>(qb, static_cast<const __bf16 *>(f.q) + q0, lane, half);
   load_rows_b<D>(dob, static_cast<const __bf16 *>(p.dout) + q0, lane, half);
-  const float l_raw = f.lse[row_base + q_row];
-  const float lse2 = l_raw * kLog2e;
+  const float lse2 = f.lse[row_base + q_row] * kLog2e;
   const float di = p.delta[row_base + q_row];
   int64_t lo = 0, hi = 0;
-  if constexpr (!DENSE) {
-    const int64_t qpos = f.q_seq[q_row];
-    const int64_t big = int64_t(1) << 40;
-    if (f.mask_kind == 0) { lo = -big; hi = qpos; }
-    else if (f.mask_kind == 1) { lo = f.left < 0 ? -big : qpos - f.left; hi = f.right < 0 ? big : qpos + f.right; }
-    else { lo = (qpos / f.chunk) * f.chunk; hi = qpos; }
-    lo -= f.kv_offset;
-    hi -= f.kv_offset;
-  }
+  if constexpr (!DENSE) key_interval(f, f.q_seq[q_row], lo, hi);
   f32x16 dq[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) dq[dt][v] = 0.f;
 
-  const int64_t kv_base = (static_cast<int64_t>(b) * f.Hkv + hkv) * f.Skv;
+  const int64_t kv_head = (static_cast<int64_t>(b) * f.Hkv + hkv) * f.Skv * D;
+  const i32x4 kr = make_rsrc(static_cast<const __bf16 *>(f.k) + kv_head, f.Skv * D * 2);
+  const i32x4 vr = make_rsrc(static_cast<const __bf16 *>(f.v) + kv_head, f.Skv * D * 2);
   const int64_t meta = (static_cast<int64_t>(hm) * f.nq + r) * f.width;
-  for (int sl = 0; sl < f.width; ++sl) {
-    const int label = load_index(f.bm, f.bm_bytes, meta + sl);
-    if (label == 0) continue;
-    const int c = load_index(f.dn, f.dn_bytes, meta + sl);
-    __syncthreads();
-    stage<D>(k_t, static_cast<const __bf16 *>(f.k) + (kv_base + static_cast<int64_t>(c) * kBlk) * D, tid);
-    stage<D>(v_t, static_cast<const __bf16 *>(f.v) + (kv_base + static_cast<int64_t>(c) * kBlk) * D, tid);
+  auto label_at = [&](int sl) -> int { return __builtin_amdgcn_readfirstlane(load_index(f.bm, f.bm_bytes, meta + sl)); };
+  auto next_slot = [&](int sl) -> int {   // first slot >= sl with a non-empty block, else width
+    while (sl < f.width && label_at(sl) == 0) ++sl;
+    return sl;
+  };
+  auto issue = [&](int buf, int sl) {
+    const int c = __builtin_amdgcn_readfirstlane(load_index(f.dn, f.dn_bytes, meta + sl));
+    const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(c) * T::kBytes);
+    issue_tile<D>(k_t[buf], kr, goff, wave, lane);
+    issue_tile<D>(v_t[buf], vr, goff, wave, lane);
+  };
+  auto load_words = [&](int sl, unsigned &m0, unsigned &m1) {
+    const int mn = load_index(f.mn, f.mn_bytes, meta + sl);
+    const unsigned *src = f.pmb_bits + static_cast<int64_t>(mn) * 4 * kBlk;
+    m0 = src[tid];
+    m1 = src[tid + kThreads];
+  };
+
+  int sl = next_slot(0);
+  int buf = 0;
+  if (sl < f.width) {
     if constexpr (DENSE) {
-      if (label == 1) {
-        const int mn = load_index(f.mn, f.mn_bytes, meta + sl);
-        for (int i = tid; i < 4 * kBlk; i += kThreads) mw_s[i] = f.pmb_bits[static_cast<int64_t>(mn) * 4 * kBlk + i];
+      if (label_at(sl) == 1) {
+        unsigned m0, m1;
+        load_words(sl, m0, m1);
+        mw_s[0][tid] = m0;
+        mw_s[0][tid + kThreads] = m1;
       }
     }
-    __syncthreads();
-    const int64_t kbase = static_cast<int64_t>(c) * kBlk;
+    issue(0, sl);
+  }
+  wait_all_loads();
+  __syncthreads();
+
+  while (sl < f.width) {
+    const int label = label_at(sl);
+    const int64_t kbase = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(load_index(f.dn, f.dn_bytes, meta + sl))) * kBlk;
+    const int sl2 = next_slot(sl + 1);
+    const bool more = sl2 < f.width;
+    const int label2 = more ? label_at(sl2) : 0;
+    unsigned m0 = 0u, m1 = 0u;
+    if (more) {
+      if constexpr (DENSE) {
+        if (label2 == 1) load_words(sl2, m0, m1);   // before the tile loads
+      }
+      issue(buf ^ 1, sl2);
+    }
+
 #pragma unroll 1
     for (int kb4 = 0; kb4 < 4; ++kb4) {
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 ak = read_row<D>(k_t, 32 * kb4 + (lane & 31), ks, half);
-        const bf16x8 av = read_row<D>(v_t, 32 * kb4 + (lane & 31), ks, half);
+        const bf16x8 ak = read_row<D>(k_t[buf], 32 * kb4 + (lane & 31), ks, half);
+        const bf16x8 av = read_row<D>(v_t[buf], 32 * kb4 + (lane & 31), ks, half);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qb[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dob[ks], dp, 0, 0, 0);
       }
       unsigned mword = 0u;
       if constexpr (DENSE) {
-        if (label == 1) mword = mw_s[kb4 * kBlk + 32 * wave + (lane & 31)];
+        if (label == 1) mword = mw_s[buf][kb4 * kBlk + 32 * wave + (lane & 31)];
       }
       bf16x8 sb[2];
 #pragma unroll
@@ -402,10 +588,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(const BwdParams p) {
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          const bf16x8 ak = read_tr<D>(k_t, 32 * kb4, h2, dt, lane, half);
+          const bf16x8 ak = read_tr<D>(k_t[buf], 32 * kb4, h2, dt, lane, half);
           dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[h2], dq[dt], 0, 0, 0);
         }
     }
+
+    if constexpr (DENSE) {
+      if (more && label2 == 1) {
+        mw_s[buf ^ 1][tid] = m0;
+        mw_s[buf ^ 1][tid + kThreads] = m1;
+      }
+    }
+    wait_all_loads();
+    __syncthreads();
+    buf ^= 1;
+    sl = sl2;
   }
   store_t<D>(static_cast<__bf16 *>(p.dq) + q0, dq, p.scale, lane, half);
 }

@@ -51,6 +51,7 @@ struct BwdParams {
   float scale;            // softmax scale (applied to dq and dk)
   int32_t nk;             // key blocks
   const int32_t *col_n, *col_ent, *col_mn;
+  const int32_t *col_order;   // key blocks by descending list length (summed over mask heads)
   int32_t col_w;
 };
 
