@@ -1,7 +1,7 @@
 """Benchmark: splash-attention forward TFLOP/s on computed blocks (MI355X).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--sinks N] [--kv-shards P] [--backward]
+                    [--sinks N] [--kv-shards P] [--backward] [--decode]
 
 A step is one splash_fwd call (the whole forward path: block walk over the
 MaskInfo, K/V staging, QK^T, soft cap, masking, online softmax, PV, epilogue)
@@ -26,6 +26,9 @@ kernel.  Its FLOPs are the usual backward count, 5 products of
 2 * 128 * 128 * D per computed block (S recomputed, dP, dV, dQ, dK);
 roofline.achieved counts the 7 products the two kernels execute (S and dP
 are formed in both).
+--decode times splash_decode on the decode workload (one query per head
+against a 32k-key cache; --workload defaults to decode_gqa_32k) and reports
+the K/V read bandwidth against HBM's 8 TB/s.
 """
 import argparse
 import hashlib
@@ -121,6 +124,60 @@ def cpu_baseline(w, q, k, v, dense, block_mask, budget_s=12.0):
     }
 
 
+def bench_decode(args):
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_make_amd import splash_decode, synthetic
+
+    name = args.workload if args.workload in synthetic.DECODE_WORKLOADS else "decode_gqa_32k"
+    w = synthetic.DECODE_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v = synthetic.make_qkv(w.seed, w.B, w.Hq, w.Hkv, 1, w.Skv, w.D, w.Dv)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out, lse = splash_decode(qd, kd, vd)
+    stream = torch.cuda.current_stream(dev)
+    ws = torch.empty(1, device=dev)
+    import ctypes
+    from block_sparse_attention_make_amd.splash import load_library
+    nb = ctypes.c_size_t()
+    load_library().splash_decode_workspace_size(w.B, w.Hq, w.Hkv, w.Skv, w.D, ctypes.byref(nb))
+    ws = torch.empty(max(1, nb.value // 4), dtype=torch.float32, device=dev)
+
+    def step():
+        splash_decode(qd, kd, vd, out=out, lse=lse, workspace=ws, stream=stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = [a.elapsed_time(b) for a, b in ev]
+    kv_bytes = w.B * w.Hkv * w.Skv * (w.D + w.Dv) * 2
+    ms = wall * 1e3 / args.steps
+    kav = float(np.mean(kern))
+    res = {
+        "metric": "splash decode K/V read bandwidth (one query per head, every key)",
+        "value": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "kv_len": w.Skv,
+                   "head_dim": w.D, "pass": "decode", "parallelism": "single-gpu"},
+        "kernel_ms_median": round(float(np.median(kern)), 5),
+        "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (kav * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(kv_bytes / (kav * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "kernel": "decode_partial + decode_merge", "bytes_per_launch": kv_bytes,
+                     "kernel_ms_avg": round(kav, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +190,7 @@ def main():
     ap.add_argument("--sinks", type=int, default=0, help="attention-sink logits per kv head")
     ap.add_argument("--kv-shards", type=int, default=1, help="time the key/value-sharded path")
     ap.add_argument("--backward", action="store_true", help="time splash_bwd")
+    ap.add_argument("--decode", action="store_true", help="time splash_decode on a decode workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -160,6 +218,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "dispatches": 5}))
         return
+    if args.decode:
+        return bench_decode(args)
     w = synthetic.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     q, k, v, dense = synthetic.make_inputs(w)

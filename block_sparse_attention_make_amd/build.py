@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libsplash.so")
-SOURCES = ["splash_fwd.hip", "splash_bwd.hip", "lse_merge.hip", "capi.cpp", "mask_info.cpp"]
+SOURCES = ["splash_fwd.hip", "splash_bwd.hip", "splash_decode.hip", "lse_merge.hip", "capi.cpp", "mask_info.cpp"]
 ARCH = "gfx950"
 
 

@@ -450,3 +450,74 @@ extern "C" SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void 
   if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return SPLASH_OK;
 }
+
+namespace {
+int64_t decode_ws_floats(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv, int64_t D) {
+  const int64_t group = Hkv > 0 ? Hq / Hkv : 0;
+  return B * Hkv * decode_chunks(Skv) * group * (D + 2);
+}
+}  // namespace
+
+extern "C" SPLASH_API splash_status splash_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv,
+                                                                 int64_t D, size_t *bytes) {
+  clear_error();
+  if (!bytes) return fail(SPLASH_EINVAL, "bytes is NULL");
+  if (B < 0 || Hq < 0 || Hkv <= 0 || Skv < 0 || D <= 0 || Hq % Hkv)
+    return fail(SPLASH_EINVAL, "bad sizes (Hkv > 0 and Hq % Hkv == 0 required)");
+  *bytes = static_cast<size_t>(decode_ws_floats(B, Hq, Hkv, Skv, D)) * sizeof(float);
+  return SPLASH_OK;
+}
+
+extern "C" SPLASH_API splash_status splash_decode(const void *q, const void *k, const void *v, void *out, float *lse,
+                                                  void *workspace, size_t workspace_bytes, int64_t B, int64_t Hq,
+                                                  int64_t Hkv, int64_t Skv, int64_t D, int64_t Dv, int32_t dtype,
+                                                  float softmax_scale, float logits_soft_cap, void *hip_stream) {
+  clear_error();
+  if (B < 0 || Hq < 0 || Hkv < 0 || Skv < 0 || D <= 0 || Dv <= 0)
+    return fail(SPLASH_EINVAL, "negative size or non-positive head dim");
+  if (dtype != SPLASH_BF16 && dtype != SPLASH_F32) return fail(SPLASH_EINVAL, "unknown dtype");
+  if (dtype != SPLASH_BF16) return fail(SPLASH_EUNSUPPORTED, "decode runs bf16 only");
+  if (Hkv == 0 && Hq > 0) return fail(SPLASH_EINVAL, "Hkv must be positive");
+  if (Hkv > 0 && Hq % Hkv) return fail(SPLASH_EINVAL, "Hq must be a multiple of Hkv");
+  if (D != Dv || (D != 64 && D != 128)) return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
+  if (!(std::isnan(softmax_scale) || (std::isfinite(softmax_scale) && softmax_scale > 0.f)))
+    return fail(SPLASH_EINVAL, "softmax_scale must be NaN (default) or finite and > 0");
+  if (B == 0 || Hq == 0) return SPLASH_OK;
+  const int64_t group = Hq / Hkv;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return fail(SPLASH_EUNSUPPORTED, "decode runs GQA groups of 1, 2, 4, 8 or 16 query heads");
+  if (Skv == 0) return fail(SPLASH_EUNSUPPORTED, "decode needs at least one key");
+  if (B * Hkv > 0x7fffffffLL || decode_chunks(Skv) > 65535 || B * Hq > 0x7fffffffLL)
+    return fail(SPLASH_EUNSUPPORTED, "grid too large");
+  if (!q || !k || !v || !out || !workspace) return fail(SPLASH_EINVAL, "NULL pointer");
+  if (!aligned16({q, k, v, out, workspace})) return fail(SPLASH_EINVAL, "q, k, v, out and workspace must be 16-byte aligned");
+  const int64_t floats = decode_ws_floats(B, Hq, Hkv, Skv, D);
+  if (workspace_bytes < static_cast<size_t>(floats) * sizeof(float))
+    return fail(SPLASH_EINVAL, "workspace smaller than splash_decode_workspace_size");
+  DecodeParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.B = static_cast<int32_t>(B);
+  p.Hq = static_cast<int32_t>(Hq);
+  p.Hkv = static_cast<int32_t>(Hkv);
+  p.group = static_cast<int32_t>(group);
+  p.D = static_cast<int32_t>(D);
+  p.Skv = Skv;
+  p.n_chunks = static_cast<int32_t>(decode_chunks(Skv));
+  const float scale = resolve_scale(softmax_scale, D);
+  const bool cap = std::isfinite(logits_soft_cap) && logits_soft_cap > 0.f;
+  const double log2e = 1.4426950408889634;
+  p.cap = cap;
+  p.c2 = cap ? static_cast<float>(static_cast<double>(scale) / logits_soft_cap) : static_cast<float>(scale * log2e);
+  p.cap_out = cap ? static_cast<float>(logits_soft_cap * log2e) : 0.f;
+  const int64_t n_slot = B * Hkv * p.n_chunks * group;
+  p.ws_o = static_cast<float *>(workspace);
+  p.ws_m = p.ws_o + n_slot * D;
+  p.ws_l = p.ws_m + n_slot;
+  hipError_t e = launch_decode(p, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
+  return SPLASH_OK;
+}

@@ -57,4 +57,22 @@ struct BwdParams {
 
 hipError_t launch_bwd(const BwdParams &p, hipStream_t stream);
 
+// Decode (one query per (batch, query head), every key allowed), split into
+// 256-key chunks whose partial max / sum / unnormalised output go to the
+// workspace and are merged by a second kernel.
+struct DecodeParams {
+  const void *q, *k, *v;   // q [B, Hq, 1, D], k / v [B, Hkv, Skv, D] (bf16)
+  void *out;               // [B, Hq, 1, D] bf16
+  float *lse;              // [B, Hq] or null
+  int32_t B, Hq, Hkv, group, D;
+  int64_t Skv;
+  int32_t n_chunks;
+  float c2, cap_out;       // as FwdParams
+  int32_t cap;
+  float *ws_o, *ws_m, *ws_l;   // [B * Hkv * n_chunks * group] (x D for ws_o)
+};
+
+int64_t decode_chunks(int64_t Skv);
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+
 }  // namespace splash

@@ -66,6 +66,14 @@ WORKLOAD_ORDER = ["tiny_causal_f32", "causal_mha_8k", "local_gqa_8k",
                   "chunked_gqa_16k_cap", "random_dense_2k"]
 
 
+# Decode (one query per head against a key/value cache, every key allowed):
+# a GQA serving shape, measured against HBM bandwidth.
+DECODE_WORKLOADS = {
+    "decode_gqa_32k": Workload("decode_gqa_32k", 8, 32, 8, 1, 32768, 128, 128, "bf16",
+                               MaskSpec("dense"), seed=6),
+}
+
+
 def random_dense_mask(rng, heads, q_len, kv_len, p_keep, force_diagonal=True):
     """Bernoulli(p_keep) bool mask [heads, q_len, kv_len]; diagonal forced on."""
     m = rng.random((heads, q_len, kv_len)) < p_keep

@@ -288,6 +288,30 @@ SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void *q, const v
                                     int64_t Skv, int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
                                     float logits_soft_cap, void *hip_stream);
 
+/* Decode: one new query per (batch, query head) against every cached key
+ * (q_len = 1).  The EasyDeL block-sparse module switches the causal mask off
+ * in decode mode and sends a single query to plain attention on TPU
+ * (EasyDeL BlockSparseAttn.forward_native); this entry point is that case on
+ * MI355X: splash_fwd's attention with every key allowed,
+ *   out_h = sum_j softmax_j(s_hj) v_j,  lse_h = log sum_j exp(s_hj),
+ * s_hj = softmax_scale <q_h, k_j> (soft-capped if a cap is given), query head
+ * h reading kv head h / (Hq / Hkv).  The keys are split into 256-key chunks
+ * processed for a whole GQA group at once and merged by log-sum-exp.
+ *
+ * q: DEVICE bf16 [B, Hq, 1, D]; k, v: DEVICE bf16 [B, Hkv, Skv, D];
+ * out: DEVICE bf16 [B, Hq, 1, D]; lse: DEVICE float32 [B, Hq] or NULL;
+ * workspace: DEVICE scratch of at least splash_decode_workspace_size bytes,
+ * overwritten.  All caller-owned, 16-byte aligned, valid until the kernels
+ * end.  bf16 only; D == Dv in {64, 128}; Hq / Hkv in {1, 2, 4, 8, 16}; Skv >= 1
+ * (else SPLASH_EUNSUPPORTED).  Asynchronous on hip_stream; allocates
+ * nothing. */
+SPLASH_API splash_status splash_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv,
+                                                      int64_t D, size_t *bytes);
+SPLASH_API splash_status splash_decode(const void *q, const void *k, const void *v, void *out, float *lse,
+                                       void *workspace, size_t workspace_bytes, int64_t B, int64_t Hq,
+                                       int64_t Hkv, int64_t Skv, int64_t D, int64_t Dv, int32_t dtype,
+                                       float softmax_scale, float logits_soft_cap, void *hip_stream);
+
 /* Message of the last failed call on this thread ("" if none).  The string
  * stays valid until the next library call on this thread. */
 SPLASH_API const char *splash_last_error(void);

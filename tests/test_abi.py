@@ -21,7 +21,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "splash_bwd", "splash_fwd", "splash_fwd_sinks", "splash_last_error", "splash_lse_merge",
+        "splash_bwd", "splash_decode", "splash_decode_workspace_size", "splash_fwd", "splash_fwd_sinks",
+        "splash_last_error", "splash_lse_merge",
         "splash_make_mask_info", "splash_make_mask_info_kv_slice", "splash_mask_info_destroy",
         "splash_mask_info_read_device", "splash_mask_info_upload", "splash_mask_info_view"])
 
@@ -146,3 +147,29 @@ def test_lse_merge_validation_errors_before_launch(over, status):
 def test_lse_merge_zero_rows_is_noop():
     lib = splash.load_library()
     assert lib.splash_lse_merge(None, None, 0, None, None, 0, None, None, 0, 0, 128, None) == splash.OK
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=splash.F32), splash.EUNSUPPORTED),
+    (dict(Hq=3), splash.EINVAL),                     # head ratio
+    (dict(Hq=64, Hkv=2), splash.EUNSUPPORTED),       # group of 32
+    (dict(D=96, Dv=96), splash.EUNSUPPORTED),
+    (dict(Skv=0), splash.EUNSUPPORTED),
+    (dict(ws=0), splash.EINVAL),
+    (dict(ws_bytes=16), splash.EINVAL),              # too small
+    (dict(q=8), splash.EINVAL),
+])
+def test_decode_validation_errors_before_launch(over, status):
+    lib = splash.load_library()
+    a = dict(q=16, k=16, v=16, out=16, lse=None, ws=16, ws_bytes=1 << 30, B=1, Hq=4, Hkv=2, Skv=1000, D=128,
+             Dv=128, dtype=splash.BF16, scale=math.nan, cap=0.0, stream=None)
+    a.update(over)
+    assert lib.splash_decode(*a.values()) == status, lib.splash_last_error()
+
+
+def test_decode_workspace_size():
+    lib = splash.load_library()
+    n = ctypes.c_size_t()
+    assert lib.splash_decode_workspace_size(2, 8, 2, 1000, 128, ctypes.byref(n)) == splash.OK
+    assert n.value == 2 * 2 * 4 * 4 * (128 + 2) * 4      # 4 chunks of 256 keys, groups of 4
+    assert lib.splash_decode_workspace_size(1, 3, 2, 10, 64, ctypes.byref(n)) == splash.EINVAL
