@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--sinks N] [--kv-shards P] [--backward] [--decode]
+                    [--block-q BQ --block-kv BK]
 
 A step is one splash_fwd call (the whole forward path: block walk over the
 MaskInfo, K/V staging, QK^T, soft cap, masking, online softmax, PV, epilogue)
@@ -26,6 +27,9 @@ kernel.  Its FLOPs are the usual backward count, 5 products of
 2 * 128 * 128 * D per computed block (S recomputed, dP, dV, dQ, dK);
 roofline.achieved counts the 7 products the two kernels execute (S and dP
 are formed in both).
+--block-q / --block-kv compile the workload's mask with larger blocks (the
+EasyDeL example's 256 x 512); the kernels walk them as 128 x 128 sub-blocks, and
+FLOPs count every sub-block of a non-empty block.
 --decode times splash_decode on the decode workload (one query per head
 against a 32k-key cache; --workload defaults to decode_gqa_32k) and reports
 the K/V read bandwidth against HBM's 8 TB/s.
@@ -191,6 +195,8 @@ def main():
     ap.add_argument("--kv-shards", type=int, default=1, help="time the key/value-sharded path")
     ap.add_argument("--backward", action="store_true", help="time splash_bwd")
     ap.add_argument("--decode", action="store_true", help="time splash_decode on a decode workload")
+    ap.add_argument("--block-q", type=int, default=128, help="mask block rows (a multiple of 128)")
+    ap.add_argument("--block-kv", type=int, default=128, help="mask block columns (a multiple of 128)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -226,13 +232,15 @@ def main():
     m = w.mask
 
     t0 = time.perf_counter()
-    mi = make_mask_info(m.kind, w.Sq, w.Skv, left=m.left, right=m.right, chunk=m.chunk, dense=dense)
+    mi = make_mask_info(m.kind, w.Sq, w.Skv, left=m.left, right=m.right, chunk=m.chunk, dense=dense,
+                        block_q=args.block_q, block_kv=args.block_kv)
     mask_ms = (time.perf_counter() - t0) * 1e3
     mi.upload()
     bm = mi.block_mask
     hm = bm.shape[0]
     nq, nk = w.Sq // w.block, w.Skv // w.block
-    computed_slots = int((bm > 0).sum())                      # per mask head set
+    sub = (args.block_q // w.block) * (args.block_kv // w.block)   # 128 x 128 sub-blocks per mask block
+    computed_slots = int((bm > 0).sum()) * sub                # per mask head set
     heads_per_mask = w.Hq if hm == 1 else 1
     blocks_computed = computed_slots * heads_per_mask * w.B
     blocks_total = nq * nk * w.Hq * w.B
@@ -347,7 +355,8 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "seq_len": w.Sq, "head_dim": w.D, "mask": m.kind, "block": w.block,
                    "soft_cap": w.soft_cap, "parallelism": "single-gpu",
-                   "sinks_per_kv_head": args.sinks, "kv_shards": P, "pass": "backward" if args.backward else "forward"},
+                   "sinks_per_kv_head": args.sinks, "kv_shards": P,
+                   "mask_block": [args.block_q, args.block_kv], "pass": "backward" if args.backward else "forward"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "dense_equiv_tflops": round(flops_dense / (ms_per_step * 1e-3) / 1e12, 2),
         "blocks_skipped": blocks_total - blocks_computed,
@@ -373,7 +382,8 @@ def main():
         # with shards the timed step holds several kernels: achieved is per step, not per launch
         res["roofline"]["kernel"] = "splash_fwd_wide x P + lse_merge_kernel x (P-1)"
         res["roofline"]["traffic"] = None
-    if not args.no_cpu_baseline and not args.backward and P == 1 and not args.sinks:
+    if (not args.no_cpu_baseline and not args.backward and P == 1 and not args.sinks
+            and args.block_q == w.block and args.block_kv == w.block):
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, dense, bm, args.cpu_budget)
     print(json.dumps(res), flush=True)
 

@@ -48,6 +48,15 @@ void free_copy(DeviceCopy &dc) {
   if (dc.mask_bits) (void)hipFree(dc.mask_bits);
   dc.mask_bits = nullptr;
   dc.mask_bits_bytes = 0;
+  for (int32_t **c : {&dc.kbm, &dc.kdn, &dc.kmn, &dc.krow_order}) {
+    if (*c) (void)hipFree(*c);
+    *c = nullptr;
+  }
+  if (dc.kpmb) (void)hipFree(dc.kpmb);
+  dc.kpmb = nullptr;
+  if (dc.kbits) (void)hipFree(dc.kbits);
+  dc.kbits = nullptr;
+  dc.kbits_bytes = 0;
   for (int32_t **c : {&dc.col_n, &dc.col_ent, &dc.col_mn, &dc.col_order}) {
     if (*c) (void)hipFree(*c);
     *c = nullptr;
@@ -60,12 +69,12 @@ void free_copy(DeviceCopy &dc) {
 
 // Partial blocks [P, bq, bk] (one byte per element) packed to 32-key words:
 // word [(p * (bk / 32) + j) * bq + i], bit c <=> element (i, 32 j + c) != 0.
-std::vector<uint32_t> pack_mask_bits(const HostArray &pm) {
-  const int64_t P = pm.shape[0], bq = pm.shape[1], bk = pm.shape[2], groups = bk / 32;
+std::vector<uint32_t> pack_bits(const uint8_t *data, int64_t P, int64_t bq, int64_t bk) {
+  const int64_t groups = bk / 32;
   std::vector<uint32_t> bits(static_cast<size_t>(P * groups * bq), 0u);
   for (int64_t b = 0; b < P; ++b)
     for (int64_t i = 0; i < bq; ++i) {
-      const uint8_t *row = pm.bytes.data() + (b * bq + i) * bk;
+      const uint8_t *row = data + (b * bq + i) * bk;
       for (int64_t j = 0; j < groups; ++j) {
         uint32_t w = 0;
         for (int c = 0; c < 32; ++c) w |= (row[32 * j + c] != 0 ? 1u : 0u) << c;
@@ -73,6 +82,75 @@ std::vector<uint32_t> pack_mask_bits(const HostArray &pm) {
       }
     }
   return bits;
+}
+std::vector<uint32_t> pack_mask_bits(const HostArray &pm) {
+  return pack_bits(pm.bytes.data(), pm.shape[0], pm.shape[1], pm.shape[2]);
+}
+
+int64_t host_index(const HostArray &a, int64_t i);
+
+// The 128 x 128 kernel view of a MaskInfo with larger blocks (KernelView).
+void build_kview(splash_mask_info *mi) {
+  KernelView &kv = mi->kview;
+  const int64_t hm = mi->num_heads, W = mi->width;
+  const int64_t fq = mi->block_q / 128, fk = mi->block_kv / 128;
+  kv.nq = mi->q_len / 128;
+  kv.nk = mi->kv_len / 128;
+  kv.width = std::max<int64_t>(1, W * fk);
+  const HostArray &bm = mi->arr[SPLASH_MI_BLOCK_MASK], &dn = mi->arr[SPLASH_MI_DATA_NEXT];
+  const HostArray &mn = mi->arr[SPLASH_MI_MASK_NEXT], &pm = mi->arr[SPLASH_MI_PARTIAL_BLOCKS];
+  const size_t n = static_cast<size_t>(hm * kv.nq * kv.width);
+  kv.bm.assign(n, 0);
+  kv.dn.assign(n, 0);
+  kv.mn.assign(n, 0);
+  std::vector<int64_t> work(static_cast<size_t>(std::max<int64_t>(kv.nq, 1)), 0);
+  for (int64_t h = 0; h < hm; ++h)
+    for (int64_t r = 0; r < kv.nq; ++r) {
+      const int64_t R = r / fq, i = r % fq;
+      int64_t out = 0;
+      for (int64_t sl = 0; sl < W; ++sl) {
+        const int64_t at = (h * mi->nq + R) * W + sl;
+        const int64_t label = host_index(bm, at);
+        if (label <= 0) continue;
+        const int64_t c = host_index(dn, at);
+        const int64_t p = (label == 1 && mn.present) ? host_index(mn, at) : 0;
+        for (int64_t j = 0; j < fk; ++j, ++out) {
+          const size_t o = static_cast<size_t>((h * kv.nq + r) * kv.width + out);
+          kv.bm[o] = static_cast<int32_t>(label);
+          kv.dn[o] = static_cast<int32_t>(c * fk + j);
+          kv.mn[o] = static_cast<int32_t>(label == 1 ? (p * fq + i) * fk + j : 0);
+        }
+      }
+      work[r] += out;
+    }
+  kv.row_order.resize(static_cast<size_t>(kv.nq));
+  for (int64_t r = 0; r < kv.nq; ++r) kv.row_order[r] = static_cast<int32_t>(r);
+  std::stable_sort(kv.row_order.begin(), kv.row_order.end(),
+                   [&](int32_t a, int32_t b) { return work[a] > work[b]; });
+  kv.pmb.clear();
+  kv.bits.clear();
+  if (pm.present && pm.ndim == 3 && pm.shape[0] > 0) {
+    const int64_t P = pm.shape[0], bq = pm.shape[1], bk = pm.shape[2];
+    const int64_t Psub = P * fq * fk;
+    kv.pmb.assign(static_cast<size_t>(Psub * 128 * 128), 0);
+    for (int64_t p = 0; p < P; ++p)
+      for (int64_t i = 0; i < fq; ++i)
+        for (int64_t j = 0; j < fk; ++j) {
+          uint8_t *dst = kv.pmb.data() + ((p * fq + i) * fk + j) * 128 * 128;
+          for (int64_t row = 0; row < 128; ++row)
+            std::memcpy(dst + row * 128, pm.bytes.data() + (p * bq + i * 128 + row) * bk + j * 128, 128);
+        }
+    kv.bits = pack_bits(kv.pmb.data(), Psub, 128, 128);
+  }
+  mi->has_kview = true;
+}
+
+template <typename T>
+hipError_t upload_vec(const std::vector<T> &v, T **dst) {
+  const size_t nb = std::max<size_t>(v.size(), 1) * sizeof(T);
+  hipError_t e = hipMalloc(reinterpret_cast<void **>(dst), nb);
+  if (e == hipSuccess && !v.empty()) e = hipMemcpy(*dst, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice);
+  return e;
 }
 
 // Device copy for the current device, uploading it if needed.
@@ -120,6 +198,26 @@ splash_status ensure_device_copy(splash_mask_info *mi, DeviceCopy **out) {
     }
     fresh.mask_bits_bytes = static_cast<int64_t>(nb);
   }
+  if (mi->block_q != 128 || mi->block_kv != 128) {
+    try {
+      if (!mi->has_kview) build_kview(mi);
+    } catch (const std::bad_alloc &) {
+      free_copy(fresh);
+      return fail(SPLASH_ENOMEM, "out of host memory for the kernel view");
+    }
+    const KernelView &kv = mi->kview;
+    e = upload_vec(kv.bm, &fresh.kbm);
+    if (e == hipSuccess) e = upload_vec(kv.dn, &fresh.kdn);
+    if (e == hipSuccess) e = upload_vec(kv.mn, &fresh.kmn);
+    if (e == hipSuccess) e = upload_vec(kv.row_order, &fresh.krow_order);
+    if (e == hipSuccess && !kv.pmb.empty()) e = upload_vec(kv.pmb, &fresh.kpmb);
+    if (e == hipSuccess && !kv.bits.empty()) e = upload_vec(kv.bits, &fresh.kbits);
+    if (e != hipSuccess) {
+      free_copy(fresh);
+      return hip_fail(e, "uploading the kernel view");
+    }
+    fresh.kbits_bytes = static_cast<int64_t>(kv.bits.size() * sizeof(uint32_t));
+  }
   dc = fresh;
   *out = &dc;
   return SPLASH_OK;
@@ -142,7 +240,10 @@ int64_t host_index(const HostArray &a, int64_t i) {
 // device copy `dc` (already uploaded).  Called under the MaskInfo's lock.
 splash_status ensure_cols(splash_mask_info *mi, DeviceCopy &dc) {
   if (dc.has_cols) return SPLASH_OK;
-  const int64_t hm = mi->num_heads, nq = mi->nq, nk = mi->nk, W = mi->width;
+  const bool view = mi->has_kview;   // blocks larger than 128 x 128: walk the kernel view
+  const int64_t hm = mi->num_heads;
+  const int64_t nq = view ? mi->kview.nq : mi->nq, nk = view ? mi->kview.nk : mi->nk;
+  const int64_t W = view ? mi->kview.width : mi->width;
   const HostArray &bm = mi->arr[SPLASH_MI_BLOCK_MASK], &dn = mi->arr[SPLASH_MI_DATA_NEXT];
   const HostArray &mn = mi->arr[SPLASH_MI_MASK_NEXT];
   std::vector<std::vector<int32_t>> ent(static_cast<size_t>(hm * nk)), pm(static_cast<size_t>(hm * nk));
@@ -150,11 +251,12 @@ splash_status ensure_cols(splash_mask_info *mi, DeviceCopy &dc) {
     for (int64_t r = 0; r < nq; ++r)
       for (int64_t s = 0; s < W; ++s) {
         const int64_t at = (h * nq + r) * W + s;
-        const int64_t label = host_index(bm, at);
+        const int64_t label = view ? mi->kview.bm[at] : host_index(bm, at);
         if (label <= 0) continue;
-        const int64_t c = host_index(dn, at);
+        const int64_t c = view ? mi->kview.dn[at] : host_index(dn, at);
         ent[h * nk + c].push_back(static_cast<int32_t>(r | (label << 30)));
-        pm[h * nk + c].push_back(mn.present ? static_cast<int32_t>(host_index(mn, at)) : 0);
+        pm[h * nk + c].push_back(view ? mi->kview.mn[at]
+                                      : (mn.present ? static_cast<int32_t>(host_index(mn, at)) : 0));
       }
   int64_t w = 1;
   for (const auto &e : ent) w = std::max<int64_t>(w, static_cast<int64_t>(e.size()));
@@ -254,12 +356,12 @@ splash_status validate_call(const splash_mask_info *mi, int64_t B, int64_t Hq, i
     return fail(SPLASH_EINVAL, "MaskInfo head count must be 1 or Hq");
   if (!(std::isnan(softmax_scale) || (std::isfinite(softmax_scale) && softmax_scale > 0.f)))
     return fail(SPLASH_EINVAL, "softmax_scale must be NaN (default) or finite and > 0");
-  if (mi->block_q != 128 || mi->block_kv != 128)
-    return fail(SPLASH_EUNSUPPORTED, "the kernels run 128 x 128 MaskInfo blocks");
+  if (mi->block_q % 128 || mi->block_kv % 128)
+    return fail(SPLASH_EUNSUPPORTED, "the kernels run MaskInfo blocks that are multiples of 128 x 128");
   if (D != Dv || (D != 64 && D != 128))
     return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
-  const int64_t n_wg = B * Hq * mi->nq;
-  if (n_wg > 0x7fffffffLL || B * Hq > 0x7fffffffLL || B * Hkv * mi->nk > 0x7fffffffLL)
+  const int64_t n_wg = B * Hq * (Sq / 128);
+  if (n_wg > 0x7fffffffLL || B * Hq > 0x7fffffffLL || B * Hkv * (Skv / 128) > 0x7fffffffLL)
     return fail(SPLASH_EUNSUPPORTED, "grid too large");
   return SPLASH_OK;
 }
@@ -300,6 +402,18 @@ FwdParams make_params(const splash_mask_info *mi, const DeviceCopy *dc, const vo
   p.bm_bytes = mi->arr[SPLASH_MI_BLOCK_MASK].elem_bits / 8;
   p.dn_bytes = mi->arr[SPLASH_MI_DATA_NEXT].elem_bits / 8;
   p.mn_bytes = mi->arr[SPLASH_MI_MASK_NEXT].present ? mi->arr[SPLASH_MI_MASK_NEXT].elem_bits / 8 : 4;
+  if (dc->kbm) {   // blocks larger than 128 x 128: the kernel view
+    p.nq = static_cast<int32_t>(mi->kview.nq);
+    p.width = static_cast<int32_t>(mi->kview.width);
+    p.bm = dc->kbm;
+    p.dn = dc->kdn;
+    p.mn = dc->kmn;
+    p.pmb = dc->kpmb;
+    p.pmb_bits = dc->kbits;
+    p.pmb_bits_bytes = dc->kbits_bytes;
+    p.row_order = dc->krow_order;
+    p.bm_bytes = p.dn_bytes = p.mn_bytes = 4;
+  }
   p.mask_kind = mi->kind;
   p.left = mi->left;
   p.right = mi->right;
@@ -440,7 +554,7 @@ extern "C" SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void 
   p.dk = dk;
   p.dv = dv;
   p.scale = resolve_scale(softmax_scale, D);
-  p.nk = static_cast<int32_t>(mi->nk);
+  p.nk = static_cast<int32_t>(Skv / 128);
   p.col_n = dc->col_n;
   p.col_ent = dc->col_ent;
   p.col_mn = dc->col_mn;

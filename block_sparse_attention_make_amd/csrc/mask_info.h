@@ -42,10 +42,29 @@ struct DeviceCopy {
   // first backward call: for mask head hm and key block c, col_n[hm * nk + c]
   // entries col_ent[(hm * nk + c) * col_w + e] = r | label << 30, query block
   // rows in ascending order, and col_mn[...] their partial block (dense).
+  // Kernel view of a MaskInfo whose blocks are larger than 128 x 128 (see
+  // KernelView); null when the blocks are 128 x 128 and ptr[] serves.
+  int32_t *kbm = nullptr, *kdn = nullptr, *kmn = nullptr, *krow_order = nullptr;
+  uint8_t *kpmb = nullptr;
+  uint32_t *kbits = nullptr;
+  int64_t kbits_bytes = 0;
   bool has_cols = false;
   int32_t *col_n = nullptr, *col_ent = nullptr, *col_mn = nullptr;
   int32_t *col_order = nullptr;   // key blocks by descending list length (over mask heads)
   int32_t col_w = 0;
+};
+
+// A MaskInfo with mask blocks of bq x bk (multiples of 128) as the kernels
+// walk it: 128 x 128 sub-blocks.  Every 128-row block row r of parent row
+// r / (bq / 128) lists, for each non-empty parent slot in order, its bk / 128
+// sub-columns with the parent's label; a partial parent block p gives its
+// sub-blocks the indices (p * (bq/128) + i) * (bk/128) + j of the re-cut
+// partial blocks.  int32 arrays [Hm, Sq / 128, W * bk / 128].
+struct KernelView {
+  int64_t nq = 0, nk = 0, width = 0;
+  std::vector<int32_t> bm, dn, mn, row_order;
+  std::vector<uint8_t> pmb;       // [P', 128, 128]
+  std::vector<uint32_t> bits;     // pmb packed as the bf16 kernel reads it
 };
 
 }  // namespace splash
@@ -66,6 +85,8 @@ struct splash_mask_info {
   // heads), ties by row index: the launch hands the longest rows out first.
   std::vector<int32_t> row_order;
   std::mutex mu;
+  bool has_kview = false;         // built lazily for blocks larger than 128 x 128
+  splash::KernelView kview;
   splash::DeviceCopy dev[splash::kMaxDevices];
 };
 

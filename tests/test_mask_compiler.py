@@ -186,3 +186,14 @@ def test_kv_slice_rejected(k0, kn):
     with pytest.raises(splash.SplashError) as e:
         splash.make_mask_info("causal", 1024, 1024, kv_slice=(k0, kn))
     assert e.value.status == splash.EINVAL
+
+
+# ---- mask blocks larger than 128 x 128 (the EasyDeL example's 256 x 512) ----
+
+@pytest.mark.parametrize("kind,kw", [("causal", {}), ("local", {"left": 700, "right": 0}),
+                                     ("chunked", {"chunk": 1000})])
+@pytest.mark.parametrize("bq,bk", [(256, 512), (512, 128), (128, 256)])
+def test_coarse_blocks_match_oracle(kind, kw, bq, bk):
+    nat = splash.make_mask_info(kind, 2048, 3072, block_q=bq, block_kv=bk, **kw)
+    ref = omi.build(omasks.materialize(kind, 2048, 3072, **kw), bq, bk, computable=True)
+    assert_same(nat, ref)
