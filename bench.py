@@ -75,6 +75,32 @@ def measured_traffic(workload):
         return None
 
 
+def mfma_probe(torch):
+    """bf16 MFMA TFLOP/s the GPU sustains (4 independent 32x32x16 chains per
+    wave, one wave per SIMD, 1.5 s warm); None if the probe library is absent."""
+    import ctypes
+    path = os.path.join(ROOT, "block_sparse_attention_make_amd", "lib", "libsplash_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.splash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    props = torch.cuda.get_device_properties(0)
+    blocks, iters = props.multi_processor_count, 20000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    t0 = time.time()
+    while time.time() - t0 < 1.5:
+        lib.splash_probe_mfma(blocks, iters, sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    lib.splash_probe_mfma(blocks, iters, sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+    b.record(stream)
+    torch.cuda.synchronize()
+    flops = blocks * 4 * iters * 4 * 32768
+    return {"tflops": round(flops / (a.elapsed_time(b) * 1e-3) / 1e12, 1), "cus": blocks}
+
+
 def flops_per_block(w):
     return 2 * w.block * w.block * (w.D + w.Dv)
 
@@ -197,6 +223,8 @@ def main():
     ap.add_argument("--decode", action="store_true", help="time splash_decode on a decode workload")
     ap.add_argument("--block-q", type=int, default=128, help="mask block rows (a multiple of 128)")
     ap.add_argument("--block-kv", type=int, default=128, help="mask block columns (a multiple of 128)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time launches with a 512 MiB buffer rewritten before each (cold L2 and MALL)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -309,6 +337,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [a.elapsed_time(b) for a, b in ev]
+    cold = None
+    if args.cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in cev:
+            flush.fill_(1)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        cms = [a.elapsed_time(b) for a, b in cev]
+        cold = {"kernel_ms_median": round(float(np.median(cms)), 5),
+                "tflops": round(flops / (float(np.median(cms)) * 1e-3) / 1e12, 2)}
+        del flush
+    probe = mfma_probe(torch) if not args.backward and P == 1 else None
     merge_info = None
     if P > 1:
         # the merge kernel alone: float32 accumulator (in place) + one bf16 shard result
@@ -377,6 +420,10 @@ def main():
         res["roofline"]["flops_per_launch"] = flops_exec
         res["roofline"]["traffic"] = None
         res["vs_baseline"] = None
+    if probe is not None:
+        res["mfma_probe"] = {**probe, "frac_of_probe": round(achieved / probe["tflops"], 4)}
+    if cold is not None:
+        res["cold_cache"] = cold
     if merge_info is not None:
         res["merge"] = merge_info
         # with shards the timed step holds several kernels: achieved is per step, not per launch

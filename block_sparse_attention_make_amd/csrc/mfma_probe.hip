@@ -1,0 +1,40 @@
+// Measurement helper, not part of the attention path: the bf16 MFMA
+// throughput this GPU sustains, to put the kernels' MFMA rates against the
+// chip's own ceiling (clock under load included) beside the nominal peak.
+// Every wave keeps four independent 32x32x16 bf16 accumulator chains busy
+// back to back, from register operands only.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float *sink) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(0.001f * static_cast<float>((threadIdx.x + i) & 7));
+    b[i] = static_cast<__bf16>(0.002f * static_cast<float>((threadIdx.x * 3 + i) & 7));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// Launches `blocks` workgroups of 4 waves, each wave running `iters` x 4
+// MFMAs (32768 flops each) into sink[blocks * 256].
+extern "C" __attribute__((visibility("default"))) int splash_probe_mfma(int blocks, int iters, float *sink,
+                                                                       void *stream) {
+  if (blocks <= 0 || iters <= 0 || !sink) return 1;
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
