@@ -819,17 +819,28 @@ void splash_fwd_wide(const FwdParams p) {
 
   bf16x8 qf[2][kKS];       // Q (B operand of S^T = K Q^T), rows of both halves
   int lo[2], hi[2];        // computable masks: allowed key interval, clamped to [-1, Skv]
+  int64_t qpos_ld[2] = {0, 0};
   {
+    // All Q loads (and the rows' positions) go out before anything waits
+    // for them: a register move placed after each load would make every
+    // load wait for the one before it.
     const __bf16 *qg = static_cast<const __bf16 *>(p.q) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row0) * D;
+    bf16x8 x[2][kKS];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8 *>(qg + static_cast<int64_t>(32 * qs) * D + 16 * ks + 8 * half);
-        // Q lives in AGPRs for the whole kernel: the QK instructions read it
-        // from there, which leaves the VGPRs to the scores and P.
-        asm volatile("" : "=a"(qf[qs][ks]) : "0"(x));
-      }
+      for (int ks = 0; ks < kKS; ++ks)
+        x[qs][ks] = *reinterpret_cast<const bf16x8 *>(qg + static_cast<int64_t>(32 * qs) * D + 16 * ks + 8 * half);
+    if constexpr (!DENSE) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs) qpos_ld[qs] = p.q_seq[q_row0 + 32 * qs];
+    }
+    // Q lives in AGPRs for the whole kernel: the QK instructions read it
+    // from there, which leaves the VGPRs to the scores and P.
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) asm volatile("" : "=a"(qf[qs][ks]) : "0"(x[qs][ks]));
   }
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
@@ -837,7 +848,7 @@ void splash_fwd_wide(const FwdParams p) {
     if constexpr (!DENSE) {
       // Every computable mask admits, for query position i, one key interval:
       // causal (-inf, i]; local [i - left, i + right]; chunked [chunk start, i].
-      const int64_t qpos = p.q_seq[q_row0 + 32 * qs];
+      const int64_t qpos = qpos_ld[qs];
       const int64_t big = int64_t(1) << 40;   // an unbounded side
       int64_t l64, h64;
       if (p.mask_kind == 0) { l64 = -big; h64 = qpos; }
@@ -975,16 +986,15 @@ void splash_fwd_wide(const FwdParams p) {
       return r;
     };
     bf16x8 ka[kKS], va[kPVOps];
-    auto mfma_slice = [&](int i) {   // QK k-step i, PV operand i
-      if (i < kKS) {
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) qk_mfma(sc_nxt[qs], ka[i], qf[qs][i], i == 0);
-      }
-      if (i < kPVOps) {
+    // Matrix instruction sub of slice i: QK k-step i for row half sub/2
+    // (even sub), PV operand i for row half sub/2 (odd sub).
+    auto mfma_one = [&](int i, int sub) {
+      const int qs = sub >> 1;
+      if ((sub & 1) == 0) {
+        if (i < kKS) qk_mfma(sc_nxt[qs], ka[i], qf[qs][i], i == 0);
+      } else if (i < kPVOps) {
         const int h = i / kDT, dt = i % kDT;
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
-          o[dt][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pf_prv[qs][h], o[dt][qs], 0, 0, 0);
+        o[dt][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pf_prv[qs][h], o[dt][qs], 0, 0, 0);
       }
     };
     auto reads_slice = [&](int i) {
@@ -993,30 +1003,25 @@ void splash_fwd_wide(const FwdParams p) {
     };
     float b2[2], sum[2] = {0.f, 0.f};
     const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-    auto exps = [&](int i) {   // elements 4(i%4) .. +3 of row half i/4
-      const int qs = i / 4, v0 = 4 * (i % 4);
-      float e[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float x = sc_cur[qs][v0 + k];
-        if constexpr (CAP) {
-          // capped logit in base-2 units; a masked key stays at -inf
-          const float xs = x * p.c2;
-          const float t2 = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(xs));
-          const float th = (1.f - t2) * __builtin_amdgcn_rcpf(1.f + t2);
-          x = xs == -INFINITY ? -INFINITY : copysignf(th, xs) * p.cap_out;
-        }
-        e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2e, -b2[qs]));
+    float eg[2][4];   // exponentials of slices i (even / odd), until packed
+    auto exp_one = [&](int i, int k) {   // element 4(i%4) + k of row half i/4
+      const int qs = i / 4;
+      float x = sc_cur[qs][4 * (i % 4) + k];
+      if constexpr (CAP) {
+        // capped logit in base-2 units; a masked key stays at -inf
+        const float xs = x * p.c2;
+        const float t2 = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(xs));
+        const float th = (1.f - t2) * __builtin_amdgcn_rcpf(1.f + t2);
+        x = xs == -INFINITY ? -INFINITY : copysignf(th, xs) * p.cap_out;
       }
-      bf16x2 p01 = {static_cast<__bf16>(e[0]), static_cast<__bf16>(e[1])};
-      bf16x2 p23 = {static_cast<__bf16>(e[2]), static_cast<__bf16>(e[3])};
-      const int h = v0 / 8, e0 = v0 % 8;
-      pf_cur[qs][h][e0 + 0] = p01[0];
-      pf_cur[qs][h][e0 + 1] = p01[1];
-      pf_cur[qs][h][e0 + 2] = p23[0];
-      pf_cur[qs][h][e0 + 3] = p23[1];
-      sum[qs] = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, sum[qs], false);
-      sum[qs] = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, sum[qs], false);
+      eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2e, -b2[qs]));
+    };
+    auto pack = [&](int i, int pr) {   // elements 2pr, 2pr+1 of slice i -> P, row sum
+      const int qs = i / 4, v0 = 4 * (i % 4) + 2 * pr;
+      const bf16x2 pp = {static_cast<__bf16>(eg[i & 1][2 * pr]), static_cast<__bf16>(eg[i & 1][2 * pr + 1])};
+      pf_cur[qs][v0 / 8][v0 % 8] = pp[0];
+      pf_cur[qs][v0 / 8][v0 % 8 + 1] = pp[1];
+      sum[qs] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum[qs], false);
       asm volatile("" : "+v"(sum[qs]));   // keep the sums in this slice
     };
 
@@ -1026,14 +1031,26 @@ void splash_fwd_wide(const FwdParams p) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) b2[qs] = rs.base[qs] == -INFINITY ? 0.f : rs.base[qs];
     __builtin_amdgcn_sched_barrier(0);
+    // Each slice is four sub-slices of one matrix instruction each, with
+    // about one matrix instruction's worth of other work beneath it (an
+    // exponential, its FMA, half a pack): the wave issues in order, so
+    // back-to-back matrix instructions would leave the VALU idle while the
+    // matrix unit is busy, and the VALU work after them would run alone.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i + 2 < 8) reads_slice(i + 2);
-      issue_loads(i);
-      mfma_slice(i);
-      exps(i);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        mfma_one(i, sub);
+        __builtin_amdgcn_sched_barrier(0);   // the matrix instruction leads its sub-slice
+        if (sub == 0 && i + 2 < 8) reads_slice(i + 2);
+        if (sub == 1) issue_loads(i);
+        if (sub == 0 && i > 0) pack(i - 1, 1);
+        exp_one(i, sub);
+        if (sub == 2) pack(i, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    pack(7, 1);
     static_assert(kKS <= 8 && kPVOps <= 8, "slice plan assumes at most 8 operands");
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) rs.l[qs] += sum[qs];
