@@ -130,13 +130,13 @@ __device__ __forceinline__ void load_rows_b(bf16x8 (&dst)[D / 16], const __bf16 
 
 // Soft-cap pieces of one score: base-2 capped logit and the derivative
 // factor 1 - tanh^2.
-__device__ __forceinline__ void capped(float x, float c2, float cap_out, float &s2, float &g) {
-  const float xs = x * c2;
-  const float e = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(xs));
-  const float th = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
-  const float t = copysignf(th, xs);
-  s2 = t * cap_out;
-  g = 1.f - t * t;
+// With y = x c2 and kc2 = 2 c2 log2 e: tanh y = 1 - 2 / (1 + e^{2y}), which
+// reaches +-1 exactly at the float range's ends.
+__device__ __forceinline__ void capped(float x, float kc2, float cap_out, float &s2, float &g) {
+  const float t = __builtin_amdgcn_exp2f(x * kc2);
+  const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + t), 1.f);
+  s2 = th * cap_out;
+  g = __builtin_fmaf(-th, th, 1.f);
 }
 
 // Store a transposed fp32 accumulator (rows d, columns = the wave's 32 rows)
@@ -276,6 +276,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned mw_s[2][4 * kBlk];
 
   const FwdParams &f = p.f;
+  const float kc2 = 2.f * kLog2e * f.c2;   // soft cap: x -> 2 y log2 e
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bh, rank;
@@ -430,14 +431,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
         for (int k = 0; k < 4; ++k) {
           const int v = 4 * g4 + k;
           float s2, gf = 1.f;
-          if constexpr (CAP) capped(s[v], f.c2, f.cap_out, s2, gf);
+          if constexpr (CAP) capped(s[v], kc2, f.cap_out, s2, gf);
           else s2 = s[v] * f.c2;
+          // (bitwise &: short-circuit tests become branches)
           bool ok = l4[k] != -INFINITY;
           if (label == 1) {
-            if constexpr (DENSE) ok = ok && ((mword[k] >> (lane & 31)) & 1u);
-            else ok = ok && key_local >= lo4[k] && key_local <= hi4[k];
+            if constexpr (DENSE) ok = ok & (((mword[k] >> (lane & 31)) & 1u) != 0u);
+            else ok = ok & (key_local >= lo4[k]) & (key_local <= hi4[k]);
           }
-          const float pv = ok ? __builtin_amdgcn_exp2f(s2 - l4[k]) : 0.f;
+          // select the exponent, not the exponential: a select between an
+          // exponential and 0 becomes a branch around every exponential
+          const float pv = __builtin_amdgcn_exp2f(ok ? s2 - l4[k] : -INFINITY);
           const float dsv = pv * (dp[v] - d4[k]) * gf;
           pb[v / 8][v % 8] = static_cast<__bf16>(pv);
           sb[v / 8][v % 8] = static_cast<__bf16>(dsv);
@@ -478,6 +482,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned mw_s[2][4 * kBlk];
 
   const FwdParams &f = p.f;
+  const float kc2 = 2.f * kLog2e * f.c2;   // soft cap: x -> 2 y log2 e
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bh, rank;
@@ -544,6 +549,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
   while (sl < f.width) {
     const int label = label_at(sl);
     const int64_t kbase = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(load_index(f.dn, f.dn_bytes, meta + sl))) * kBlk;
+    // this lane's key interval relative to the block, clamped to [-1, kBlk]
+    const int rlo = static_cast<int>(lo - kbase < -1 ? -1 : (lo - kbase > kBlk ? kBlk : lo - kbase));
+    const int rhi = static_cast<int>(hi - kbase < -1 ? -1 : (hi - kbase > kBlk ? kBlk : hi - kbase));
     const int sl2 = next_slot(sl + 1);
     const bool more = sl2 < f.width;
     const int label2 = more ? label_at(sl2) : 0;
@@ -574,14 +582,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
       for (int v = 0; v < 16; ++v) {
         const int kl = 32 * kb4 + 8 * (v / 4) + 4 * half + (v % 4);   // key within the block
         float s2, gf = 1.f;
-        if constexpr (CAP) capped(s[v], f.c2, f.cap_out, s2, gf);
+        if constexpr (CAP) capped(s[v], kc2, f.cap_out, s2, gf);
         else s2 = s[v] * f.c2;
         bool ok = lse2 != -INFINITY;
-        if (label == 1) {
-          if constexpr (DENSE) ok = ok && ((mword >> (kl & 31)) & 1u);
-          else ok = ok && kbase + kl >= lo && kbase + kl <= hi;
+        if (label == 1) {   // (bitwise &: short-circuit tests become branches)
+          if constexpr (DENSE) ok = ok & (((mword >> (kl & 31)) & 1u) != 0u);
+          else ok = ok & (kl >= rlo) & (kl <= rhi);
         }
-        const float pv = ok ? __builtin_amdgcn_exp2f(s2 - lse2) : 0.f;
+        const float pv = __builtin_amdgcn_exp2f(ok ? s2 - lse2 : -INFINITY);   // (as in the dK/dV kernel)
         sb[v / 8][v % 8] = static_cast<__bf16>(pv * (dp[v] - di) * gf);
       }
 #pragma unroll

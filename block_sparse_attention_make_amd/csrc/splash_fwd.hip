@@ -1002,19 +1002,24 @@ void splash_fwd_wide(const FwdParams p) {
       if (i < kPVOps) va[i] = read_v(i);
     };
     float b2[2], sum[2] = {0.f, 0.f};
+    const float kc2 = 2.f * kLog2e * p.c2;   // CAP: x -> 2 y log2 e
     const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
     float eg[2][4];   // exponentials of slices i (even / odd), until packed
     auto exp_one = [&](int i, int k) {   // element 4(i%4) + k of row half i/4
       const int qs = i / 4;
-      float x = sc_cur[qs][4 * (i % 4) + k];
+      const float x = sc_cur[qs][4 * (i % 4) + k];
       if constexpr (CAP) {
-        // capped logit in base-2 units; a masked key stays at -inf
-        const float xs = x * p.c2;
-        const float t2 = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(xs));
-        const float th = (1.f - t2) * __builtin_amdgcn_rcpf(1.f + t2);
-        x = xs == -INFINITY ? -INFINITY : copysignf(th, xs) * p.cap_out;
+        // Capped logit in base-2 units: with y = x c2,
+        // tanh y = 1 - 2 / (1 + e^{2y}), which reaches +-1 exactly at the
+        // float range's ends.  x 2^-100 lies far below the rounding of any
+        // finite logit but keeps a masked key (-inf) at -inf, without a
+        // select (which the compiler turns into a branch around the cap).
+        const float t = __builtin_amdgcn_exp2f(x * kc2);
+        const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + t), 1.f);
+        eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(th, p.cap_out, __builtin_fmaf(x, 0x1p-100f, -b2[qs])));
+      } else {
+        eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2e, -b2[qs]));
       }
-      eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2e, -b2[qs]));
     };
     auto pack = [&](int i, int pr) {   // elements 2pr, 2pr+1 of slice i -> P, row sum
       const int qs = i / 4, v0 = 4 * (i % 4) + 2 * pr;
