@@ -119,6 +119,57 @@ __device__ __forceinline__ bf16x8 read_tr(const char *lds, int r0, int h, int dt
   return r;
 }
 
+// read_tr with the lane's addresses precomputed: for tile rows r0 + 16 h + t
+// (r0 a multiple of 16) the swizzle depends only on t, so each lane's byte
+// offsets for its two rows t and t + 8 and each column group dt are fixed,
+// and only the uniform row base changes from read to read.
+template <int D>
+struct TrRead {
+  using T = BTile<D>;
+  int off_lo[D / 32], off_hi[D / 32];
+  __device__ TrRead(int lane, int half) {
+    const int trow = 4 * half + ((lane & 15) >> 2);
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int col = 32 * dt + tcol;
+      const int c = col >> 3, within = (col & 7) * 2;
+      off_lo[dt] = trow * T::kRowBytes + ((c ^ T::swz(trow)) * 16) + within;
+      off_hi[dt] = (trow + 8) * T::kRowBytes + ((c ^ T::swz(trow + 8)) * 16) + within;
+    }
+  }
+  __device__ __forceinline__ bf16x8 operator()(const char *lds, int r0, int h, int dt) const {
+    const char *base = lds + (r0 + 16 * h) * T::kRowBytes;
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(base + off_lo[dt]));
+    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(base + off_hi[dt]));
+    const s16x4 both[2] = {lo4, hi4};
+    bf16x8 r;
+    __builtin_memcpy(&r, both, 16);
+    return r;
+  }
+};
+
+// A 32x32x16 bf16 MFMA from inline assembly, so its accumulator lives in
+// VGPRs where the VALU reads it (left to itself the compiler keeps the
+// score accumulators in AGPRs and copies every element out).  The compiler
+// does not see this instruction's latency: a VALU read of the accumulator
+// must wait for mfma_drain.  A first k-step (C = 0) must not share registers
+// with its inputs.
+__device__ __forceinline__ void mfma_v(f32x16 &acc, const bf16x8 &a, const bf16x8 &b, bool first) {
+  if (first)
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states covering the result latency of the last mfma_v writing acc
+// before a VALU instruction reads it (16 passes, generously).  Tied to the
+// accumulators so it stays between their last MFMA and their first read.
+__device__ __forceinline__ void mfma_drain(f32x16 &a, f32x16 &b) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(a), "+v"(b));
+}
+
 // B operands of a row block kept in registers: lane (j, half) holds row
 // row0 + j, elements 16 ks + 8 half .. + 7.
 template <int D>
@@ -269,8 +320,9 @@ template <int D, bool CAP, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
   using T = BTile<D>;
   constexpr int kKS = D / 16, kDT = D / 32;
-  __shared__ __attribute__((aligned(1024))) char q_t[2][T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char do_t[2][T::kBytes];
+  // [buffer][Q, dO]: a buffer's two tiles sit within one LDS instruction
+  // offset of each other, so their reads share address registers
+  __shared__ __attribute__((aligned(1024))) char qdo_t[2][2][T::kBytes];
   __shared__ __attribute__((aligned(16))) float lse_s[2][kBlk], di_s[2][kBlk];
   __shared__ __attribute__((aligned(16))) int lo_s[2][kBlk], hi_s[2][kBlk];
   __shared__ __attribute__((aligned(16))) unsigned mw_s[2][4 * kBlk];
@@ -313,6 +365,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
   advance(g, e, n);   // first pair (g == group when there is none)
 
   const int key_local = 32 * wave + (lane & 31);
+  const TrRead<D> tr(lane, half);
   // Small per-block operands of pair (g, e), loaded to registers by the
   // first 128 threads: lse (base 2), di, and the key interval or mask words.
   struct Small { float l, d; int lo, hi; unsigned m0, m1; };
@@ -370,8 +423,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
     const i32x4 qr = make_rsrc(static_cast<const __bf16 *>(f.q) + head, f.Sq * D * 2);
     const i32x4 dr = make_rsrc(static_cast<const __bf16 *>(p.dout) + head, f.Sq * D * 2);
     const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(r) * T::kBytes);
-    issue_tile<D>(q_t[buf], qr, goff, wave, lane);
-    issue_tile<D>(do_t[buf], dr, goff, wave, lane);
+    issue_tile<D>(qdo_t[buf][0], qr, goff, wave, lane);
+    issue_tile<D>(qdo_t[buf][1], dr, goff, wave, lane);
   };
 
   int buf = 0;
@@ -402,14 +455,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
 
 #pragma unroll 1
     for (int qb = 0; qb < 4; ++qb) {
-      f32x16 s = {}, dp = {};
+      f32x16 s, dp;
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 aq = read_row<D>(q_t[buf], 32 * qb + (lane & 31), ks, half);
-        const bf16x8 ad = read_row<D>(do_t[buf], 32 * qb + (lane & 31), ks, half);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kb[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vb[ks], dp, 0, 0, 0);
+        const bf16x8 aq = read_row<D>(qdo_t[buf][0], 32 * qb + (lane & 31), ks, half);
+        const bf16x8 ad = read_row<D>(qdo_t[buf][1], 32 * qb + (lane & 31), ks, half);
+        mfma_v(s, aq, kb[ks], ks == 0);
+        mfma_v(dp, ad, vb[ks], ks == 0);
       }
+      mfma_drain(s, dp);
       bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -451,8 +505,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          const bf16x8 ado = read_tr<D>(do_t[buf], 32 * qb, h2, dt, lane, half);
-          const bf16x8 aq = read_tr<D>(q_t[buf], 32 * qb, h2, dt, lane, half);
+          const bf16x8 ado = tr(qdo_t[buf][1], 32 * qb, h2, dt);
+          const bf16x8 aq = tr(qdo_t[buf][0], 32 * qb, h2, dt);
           dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[h2], dv[dt], 0, 0, 0);
           dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[h2], dk[dt], 0, 0, 0);
         }
@@ -477,8 +531,8 @@ template <int D, bool CAP, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
   using T = BTile<D>;
   constexpr int kKS = D / 16, kDT = D / 32;
-  __shared__ __attribute__((aligned(1024))) char k_t[2][T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char v_t[2][T::kBytes];
+  // [buffer][K, V] (as in the dK/dV kernel)
+  __shared__ __attribute__((aligned(1024))) char kv_t[2][2][T::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned mw_s[2][4 * kBlk];
 
   const FwdParams &f = p.f;
@@ -502,6 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
   const float di = p.delta[row_base + q_row];
   int64_t lo = 0, hi = 0;
   if constexpr (!DENSE) key_interval(f, f.q_seq[q_row], lo, hi);
+  const TrRead<D> tr(lane, half);
   f32x16 dq[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
@@ -520,8 +575,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
   auto issue = [&](int buf, int sl) {
     const int c = __builtin_amdgcn_readfirstlane(load_index(f.dn, f.dn_bytes, meta + sl));
     const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(c) * T::kBytes);
-    issue_tile<D>(k_t[buf], kr, goff, wave, lane);
-    issue_tile<D>(v_t[buf], vr, goff, wave, lane);
+    issue_tile<D>(kv_t[buf][0], kr, goff, wave, lane);
+    issue_tile<D>(kv_t[buf][1], vr, goff, wave, lane);
   };
   auto load_words = [&](int sl, unsigned &m0, unsigned &m1) {
     const int mn = load_index(f.mn, f.mn_bytes, meta + sl);
@@ -565,14 +620,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
 
 #pragma unroll 1
     for (int kb4 = 0; kb4 < 4; ++kb4) {
-      f32x16 s = {}, dp = {};
+      f32x16 s, dp;
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 ak = read_row<D>(k_t[buf], 32 * kb4 + (lane & 31), ks, half);
-        const bf16x8 av = read_row<D>(v_t[buf], 32 * kb4 + (lane & 31), ks, half);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qb[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dob[ks], dp, 0, 0, 0);
+        const bf16x8 ak = read_row<D>(kv_t[buf][0], 32 * kb4 + (lane & 31), ks, half);
+        const bf16x8 av = read_row<D>(kv_t[buf][1], 32 * kb4 + (lane & 31), ks, half);
+        mfma_v(s, ak, qb[ks], ks == 0);
+        mfma_v(dp, av, dob[ks], ks == 0);
       }
+      mfma_drain(s, dp);
       unsigned mword = 0u;
       if constexpr (DENSE) {
         if (label == 1) mword = mw_s[buf][kb4 * kBlk + 32 * wave + (lane & 31)];
@@ -596,7 +652,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          const bf16x8 ak = read_tr<D>(k_t[buf], 32 * kb4, h2, dt, lane, half);
+          const bf16x8 ak = tr(kv_t[buf][0], 32 * kb4, h2, dt);
           dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[h2], dq[dt], 0, 0, 0);
         }
     }
