@@ -453,63 +453,115 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
       issue(buf ^ 1, g2, r2);
     }
 
-#pragma unroll 1
-    for (int qb = 0; qb < 4; ++qb) {
-      f32x16 s, dp;
+    // The tile's four 32-row query blocks run as a software pipeline: step
+    // qb forms S and dP of block qb + 1 (A), the softmax gradient of block qb
+    // (B) and the dV / dK products of block qb - 1 (C).  A and C are
+    // independent matrix work and B is VALU work on results of the step
+    // before, so each step interleaves them one matrix instruction at a time
+    // (sub-slices separated by scheduling barriers): the wave issues in
+    // order, and phases run one after another would leave the matrix unit
+    // idle during the softmax gradient.
+    {
+      constexpr int kA = 2 * kKS;      // A instructions of a block: (k-step, S | dP)
+      constexpr int kC = 4 * kDT;      // C instructions: (h2, dt, dV | dK)
+      constexpr int kSub = kA > kC ? 2 * kA : 2 * kC;
+      const char *tq = qdo_t[buf][0];
+      const char *td = qdo_t[buf][1];
+      f32x16 sA[2], dpA[2];            // [block & 1]
+      bf16x8 pbB[2][2], sbB[2][2];     // [block & 1][h2]
+      auto a_read = [&](int qb, int a) -> bf16x8 {
+        return read_row<D>((a & 1) ? td : tq, 32 * qb + (lane & 31), a >> 1, half);
+      };
+      auto a_mfma = [&](int qb, int a, const bf16x8 &op) {
+        const int ks = a >> 1;
+        if ((a & 1) == 0) mfma_v(sA[qb & 1], op, kb[ks], ks == 0);
+        else mfma_v(dpA[qb & 1], op, vb[ks], ks == 0);
+      };
+      auto c_read = [&](int qb, int c) -> bf16x8 {
+        const int h2 = c / (2 * kDT), dt = (c >> 1) % kDT;
+        return tr((c & 1) ? tq : td, 32 * qb, h2, dt);   // dV contracts dO, dK contracts Q
+      };
+      auto c_mfma = [&](int qb, int c, const bf16x8 &op) {
+        const int h2 = c / (2 * kDT), dt = (c >> 1) % kDT;
+        if ((c & 1) == 0) dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pbB[qb & 1][h2], dv[dt], 0, 0, 0);
+        else dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, sbB[qb & 1][h2], dk[dt], 0, 0, 0);
+      };
+      // Per-row operands of elements 4 g4 .. 4 g4 + 3 (rows qi0 .. qi0 + 3).
+      // The mask data is read unconditionally (stale unless label == 1) so
+      // the step stays one basic block.
+      struct Grp { f32x4 l4, d4; i32x4 lo4, hi4; unsigned mw[4]; };
+      auto g_load = [&](int qb, int g4, Grp &G) {
+        const int qi0 = 32 * qb + 8 * g4 + 4 * half;
+        G.l4 = *reinterpret_cast<const f32x4 *>(&lse_s[buf][qi0]);
+        G.d4 = *reinterpret_cast<const f32x4 *>(&di_s[buf][qi0]);
+        if constexpr (DENSE) {
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 aq = read_row<D>(qdo_t[buf][0], 32 * qb + (lane & 31), ks, half);
-        const bf16x8 ad = read_row<D>(qdo_t[buf][1], 32 * qb + (lane & 31), ks, half);
-        mfma_v(s, aq, kb[ks], ks == 0);
-        mfma_v(dp, ad, vb[ks], ks == 0);
-      }
-      mfma_drain(s, dp);
-      bf16x8 pb[2], sb[2];
+          for (int k = 0; k < 4; ++k) G.mw[k] = mw_s[buf][wave * kBlk + qi0 + k];
+        } else {
+          G.lo4 = *reinterpret_cast<const i32x4 *>(&lo_s[buf][qi0]);
+          G.hi4 = *reinterpret_cast<const i32x4 *>(&hi_s[buf][qi0]);
+        }
+      };
+      const bool partial = label == 1;
+      auto elem = [&](int qb, int v, const Grp &G) {
+        const int k = v & 3;
+        const float sv = sA[qb & 1][v], dpv = dpA[qb & 1][v];
+        float s2, gf = 1.f;
+        if constexpr (CAP) capped(sv, kc2, f.cap_out, s2, gf);
+        else s2 = sv * f.c2;
+        // (bitwise &: short-circuit tests become branches)
+        bool in = true;
+        if constexpr (DENSE) in = ((G.mw[k] >> (lane & 31)) & 1u) != 0u;
+        else in = (key_local >= G.lo4[k]) & (key_local <= G.hi4[k]);
+        const bool ok = (G.l4[k] != -INFINITY) & (!partial | in);
+        // select the exponent, not the exponential: a select between an
+        // exponential and 0 becomes a branch around every exponential
+        const float pv = __builtin_amdgcn_exp2f(ok ? s2 - G.l4[k] : -INFINITY);
+        const float dsv = pv * (dpv - G.d4[k]) * gf;
+        pbB[qb & 1][v / 8][v % 8] = static_cast<__bf16>(pv);
+        sbB[qb & 1][v / 8][v % 8] = static_cast<__bf16>(dsv);
+      };
+
+      // One pipeline step: A(qa) (qa < 0: none), B(qbv) (qbv < 0: none),
+      // C(qc) (qc < 0: none).  Sub-slice j holds A instruction j / 2 (even
+      // j) or C instruction j / 2 (odd j), the operand reads of sub-slice
+      // j + 2, and one element of B every kSub / 16 sub-slices.
+      auto step = [&](int qa, int qbv, int qc) {
+        bf16x8 opA[kA], opC[kC];
+        auto reads = [&](int j) {
+          if (j >= kSub) return;
+          if ((j & 1) == 0) { if (qa >= 0 && (j >> 1) < kA) opA[j >> 1] = a_read(qa, j >> 1); }
+          else { if (qc >= 0 && (j >> 1) < kC) opC[j >> 1] = c_read(qc, j >> 1); }
+        };
+        Grp G[2];
+        if (qbv >= 0) g_load(qbv, 0, G[0]);
+        reads(0);
+        reads(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int qi0 = 32 * qb + 8 * g4 + 4 * half;   // rows of elements 4 g4 .. 4 g4 + 3
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(&lse_s[buf][qi0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&di_s[buf][qi0]);
-        unsigned mword[4] = {0u, 0u, 0u, 0u};
-        int lo4[4] = {0, 0, 0, 0}, hi4[4] = {0, 0, 0, 0};
-        if (label == 1) {
-          if constexpr (DENSE) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) mword[k] = mw_s[buf][wave * kBlk + qi0 + k];
-          } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) { lo4[k] = lo_s[buf][qi0 + k]; hi4[k] = hi_s[buf][qi0 + k]; }
+        for (int j = 0; j < kSub; ++j) {
+          if ((j & 1) == 0) { if (qa >= 0 && (j >> 1) < kA) a_mfma(qa, j >> 1, opA[j >> 1]); }
+          else { if (qc >= 0 && (j >> 1) < kC) c_mfma(qc, j >> 1, opC[j >> 1]); }
+          __builtin_amdgcn_sched_barrier(0);
+          reads(j + 2);
+          if (qbv >= 0 && j % (kSub / 16) == 0) {
+            const int v = j / (kSub / 16);
+            if ((v & 3) == 0 && v + 4 < 16) g_load(qbv, (v >> 2) + 1, G[((v >> 2) + 1) & 1]);
+            elem(qbv, v, G[(v >> 2) & 1]);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
+      };
+
+      // prologue: A(0), then the result latency of its last instruction
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int v = 4 * g4 + k;
-          float s2, gf = 1.f;
-          if constexpr (CAP) capped(s[v], kc2, f.cap_out, s2, gf);
-          else s2 = s[v] * f.c2;
-          // (bitwise &: short-circuit tests become branches)
-          bool ok = l4[k] != -INFINITY;
-          if (label == 1) {
-            if constexpr (DENSE) ok = ok & (((mword[k] >> (lane & 31)) & 1u) != 0u);
-            else ok = ok & (key_local >= lo4[k]) & (key_local <= hi4[k]);
-          }
-          // select the exponent, not the exponential: a select between an
-          // exponential and 0 becomes a branch around every exponential
-          const float pv = __builtin_amdgcn_exp2f(ok ? s2 - l4[k] : -INFINITY);
-          const float dsv = pv * (dp[v] - d4[k]) * gf;
-          pb[v / 8][v % 8] = static_cast<__bf16>(pv);
-          sb[v / 8][v % 8] = static_cast<__bf16>(dsv);
-        }
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          const bf16x8 ado = tr(qdo_t[buf][1], 32 * qb, h2, dt);
-          const bf16x8 aq = tr(qdo_t[buf][0], 32 * qb, h2, dt);
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ado, pb[h2], dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb[h2], dk[dt], 0, 0, 0);
-        }
+      for (int a = 0; a < kA; ++a) a_mfma(0, a, a_read(0, a));
+      mfma_drain(sA[0], dpA[0]);
+      step(1, 0, -1);
+      step(2, 1, 0);
+      step(3, 2, 1);
+      step(-1, 3, 2);
+      step(-1, -1, 3);
     }
 
     if (more) store_small(buf ^ 1, label2, sm);
