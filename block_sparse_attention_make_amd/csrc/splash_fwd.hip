@@ -802,12 +802,6 @@ void splash_fwd_wide(const FwdParams p) {
   const int row_in_block0 = 64 * wave + (lane & 31);      // qs = 0; qs = 1 adds 32
   const int64_t q_row0 = static_cast<int64_t>(r) * kBQ + row_in_block0;
 
-  // V stages start as zeros: the first step's PV(-1) reads the last stage
-  // with zero P, and 0 * (uninitialised LDS) could be NaN.
-#pragma unroll
-  for (int i = 0; i < kStages * SG::kBytes / (16 * kWThreads); ++i)
-    reinterpret_cast<u32x4 *>(&v_st[0][0])[tid + kWThreads * i] = u32x4{0u, 0u, 0u, 0u};
-
   const __bf16 *kg = static_cast<const __bf16 *>(p.k) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
   const __bf16 *vg = static_cast<const __bf16 *>(p.v) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
   const i32x4 k_res = make_rsrc(kg, p.Skv * D * 2);
@@ -816,6 +810,44 @@ void splash_fwd_wide(const FwdParams p) {
   const i32x4 m_res = make_rsrc(has_bits ? static_cast<const void *>(p.pmb_bits) : p.k,
                                 has_bits ? p.pmb_bits_bytes : 0);
   const int64_t meta_base = (static_cast<int64_t>(hm) * p.nq + r) * p.width;
+
+  // Packed mask words of step t of partial block pb (dense masks): this
+  // wave's 64 block rows, into mask stage `stage`.
+  auto issue_mask = [&](int pb, int t, int stage) {
+    const uint32_t soff = static_cast<uint32_t>(((pb * kSteps + t) * kBQ + 64 * wave) * 4);
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) char *)(m_st[stage] + 256 * wave)));
+    const uint32_t voff = static_cast<uint32_t>(4 * lane);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(m0), "v"(voff), "s"(m_res), "s"(soff) : "memory", "m0");
+#pragma clang diagnostic pop
+  };
+
+  // The first chunk's prologue loads (K of its block's four steps, their
+  // mask words, V of the first two) go out before the Q loads and the
+  // chunk's compaction, so the three latencies overlap: data_next at the
+  // row's first grid position is the column of the row's first non-empty
+  // block (and mask_next the first partial block's mask), which is where
+  // the pipeline starts.  (A row whose first chunk is empty loads an unused
+  // block; the chunk loop checks the block before relying on these loads.)
+  const int dn_first = __builtin_amdgcn_readfirstlane(load_index(p.dn, p.dn_bytes, meta_base));
+  const int mn_first = has_bits ? __builtin_amdgcn_readfirstlane(load_index(p.mn, p.mn_bytes, meta_base)) : 0;
+#pragma unroll
+  for (int t = 0; t < kSteps; ++t) {
+    issue_stage<D, false>(k_st[t], k_res, static_cast<int64_t>(dn_first) * kBK + kSK * t, wave, lane);
+    if (has_bits) issue_mask(mn_first, t, t);
+  }
+  issue_stage<D, true>(v_st[0], v_res, static_cast<int64_t>(dn_first) * kBK, wave, lane);
+  issue_stage<D, true>(v_st[1], v_res, static_cast<int64_t>(dn_first) * kBK + kSK, wave, lane);
+  static_assert(kSteps == kStages, "the prologue fills every K stage");
+
+  // The other V stages start as zeros: the first step's PV(-1) reads the
+  // last stage with zero P, and 0 * (uninitialised LDS) could be NaN.
+#pragma unroll
+  for (int i = 0; i < 2 * SG::kBytes / (16 * kWThreads); ++i)
+    reinterpret_cast<u32x4 *>(&v_st[2][0])[tid + kWThreads * i] = u32x4{0u, 0u, 0u, 0u};
 
   bf16x8 qf[2][kKS];       // Q (B operand of S^T = K Q^T), rows of both halves
   int lo[2], hi[2];        // computable masks: allowed key interval, clamped to [-1, Skv]
@@ -904,18 +936,6 @@ void splash_fwd_wide(const FwdParams p) {
     return __builtin_amdgcn_readfirstlane(c_kvb[u / kSteps]) * kBK + kSK * (u % kSteps);
   };
   auto label = [&](int u) -> int { return __builtin_amdgcn_readfirstlane(c_lab[u / kSteps]); };
-  // Packed mask words of step u (dense): this wave's 64 block rows.
-  auto issue_mask = [&](int pb, int t, int stage) {   // partial block pb, key group t
-    const uint32_t soff = static_cast<uint32_t>(((pb * kSteps + t) * kBQ + 64 * wave) * 4);
-    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (__attribute__((address_space(3))) char *)(m_st[stage] + 256 * wave)));
-    const uint32_t voff = static_cast<uint32_t>(4 * lane);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(m0), "v"(voff), "s"(m_res), "s"(soff) : "memory", "m0");
-#pragma clang diagnostic pop
-  };
   auto mask_words = [&](int stage, unsigned *mw) {
     if constexpr (DENSE) {
 #pragma unroll
@@ -1163,10 +1183,13 @@ void splash_fwd_wide(const FwdParams p) {
       int mn1 = DENSE ? __builtin_amdgcn_readfirstlane(c_mn[min(1, nb - 1)]) : 0;
       int lab0 = __builtin_amdgcn_readfirstlane(c_lab[0]);
       int lab1 = __builtin_amdgcn_readfirstlane(c_lab[min(1, nb - 1)]);
-      load_k(0, kv0, 0); load_m(0, mn0, 0);
-      load_k(1, kv0, 1); load_m(1, mn0, 1);
-      load_k(2, kv0, 2); load_m(2, mn0, 2); load_v(0, kv0, 0);
-      load_k(3, kv0, 3); load_m(3, mn0, 3); load_v(1, kv0, 1);
+      const bool early = s0 == 0 && attempt == 0 && kv0 == dn_first && (!has_bits || mn0 == mn_first);
+      if (!early) {
+        load_k(0, kv0, 0); load_m(0, mn0, 0);
+        load_k(1, kv0, 1); load_m(1, mn0, 1);
+        load_k(2, kv0, 2); load_m(2, mn0, 2); load_v(0, kv0, 0);
+        load_k(3, kv0, 3); load_m(3, mn0, 3); load_v(1, kv0, 1);
+      }
       wait_at_most<kMaxInFlight>(count(-3) + count(-2) + count(-1));
       lds_barrier();
       wide_qk<D>(k_st[0], qf, lane, half, sc_a);
