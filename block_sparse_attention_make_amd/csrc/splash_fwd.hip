@@ -634,6 +634,13 @@ __device__ __forceinline__ void qk_mfma(f32x16 &acc, const bf16x8 &a, const bf16
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(q));
 }
 
+// The first k-step of a tile with the accumulator started from `c` instead
+// of 0: with Q pre-scaled to base-2 units, c = -(the row's exponent base)
+// makes the matrix unit deliver the exponent itself.  `c` is only read.
+__device__ __forceinline__ void qk_mfma_c(f32x16 &acc, const bf16x8 &a, const bf16x8 &q, const f32x16 &c) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(a), "a"(q), "v"(c));
+}
+
 // Wait states covering the result latency of the last qk_mfma before its
 // accumulator is read by VALU instructions (16 passes, generously).
 __device__ __forceinline__ void qk_drain() {
@@ -867,6 +874,19 @@ void splash_fwd_wide(const FwdParams p) {
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) qpos_ld[qs] = p.q_seq[q_row0 + 32 * qs];
     }
+    // Without a soft cap Q is scaled once here by softmax_scale * log2(e), so
+    // every score comes out of the matrix unit in base-2 units and the
+    // softmax needs no multiply per score.  (One more bf16 rounding of each
+    // Q element: about 2^-9 relative, the size of the rounding P gets.)
+    if constexpr (!CAP) {
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            x[qs][ks][e] = static_cast<__bf16>(static_cast<float>(x[qs][ks][e]) * p.c2);
+    }
     // Q lives in AGPRs for the whole kernel: the QK instructions read it
     // from there, which leaves the VGPRs to the scores and P.
 #pragma unroll
@@ -891,7 +911,10 @@ void splash_fwd_wide(const FwdParams p) {
       hi[qs] = static_cast<int>(clamp64(h64 - p.kv_offset, -1, p.Skv));
     }
   }
-  const float c2e = CAP ? 1.f : p.c2;
+  // Scores as the QK instructions leave them are in base-2 units without a
+  // cap (Q is pre-scaled); with a cap they are raw and the cap takes p.c2.
+  constexpr float c2e = 1.f;
+  f32x16 cb[2];   // no cap: -(exponent base) per row, the first QK k-step's C
 
   // Compact one chunk of the block row's grid positions: keep label > 0.
   // Entry j + 1 is the block data_next points the pipeline at after entry j.
@@ -1011,7 +1034,14 @@ void splash_fwd_wide(const FwdParams p) {
     auto mfma_one = [&](int i, int sub) {
       const int qs = sub >> 1;
       if ((sub & 1) == 0) {
-        if (i < kKS) qk_mfma(sc_nxt[qs], ka[i], qf[qs][i], i == 0);
+        if (i < kKS) {
+          if constexpr (!CAP) {
+            if (i == 0) qk_mfma_c(sc_nxt[qs], ka[0], qf[qs][0], cb[qs]);
+            else qk_mfma(sc_nxt[qs], ka[i], qf[qs][i], false);
+          } else {
+            qk_mfma(sc_nxt[qs], ka[i], qf[qs][i], i == 0);
+          }
+        }
       } else if (i < kPVOps) {
         const int h = i / kDT, dt = i % kDT;
         o[dt][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pf_prv[qs][h], o[dt][qs], 0, 0, 0);
@@ -1023,7 +1053,6 @@ void splash_fwd_wide(const FwdParams p) {
     };
     float b2[2], sum[2] = {0.f, 0.f};
     const float kc2 = 2.f * kLog2e * p.c2;   // CAP: x -> 2 y log2 e
-    const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
     float eg[2][4];   // exponentials of slices i (even / odd), until packed
     auto exp_one = [&](int i, int k) {   // element 4(i%4) + k of row half i/4
       const int qs = i / 4;
@@ -1038,15 +1067,19 @@ void splash_fwd_wide(const FwdParams p) {
         const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + t), 1.f);
         eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(th, p.cap_out, __builtin_fmaf(x, 0x1p-100f, -b2[qs])));
       } else {
-        eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2e, -b2[qs]));
+        eg[i & 1][k] = __builtin_amdgcn_exp2f(x);   // already s * scale * log2(e) - base
       }
     };
     auto pack = [&](int i, int pr) {   // elements 2pr, 2pr+1 of slice i -> P, row sum
       const int qs = i / 4, v0 = 4 * (i % 4) + 2 * pr;
-      const bf16x2 pp = {static_cast<__bf16>(eg[i & 1][2 * pr]), static_cast<__bf16>(eg[i & 1][2 * pr + 1])};
+      const float e0 = eg[i & 1][2 * pr], e1 = eg[i & 1][2 * pr + 1];
+      const bf16x2 pp = {static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
       pf_cur[qs][v0 / 8][v0 % 8] = pp[0];
       pf_cur[qs][v0 / 8][v0 % 8 + 1] = pp[1];
-      sum[qs] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, sum[qs], false);
+      // Row sums of the float exponentials (round to nearest even makes the
+      // bf16 P that PV multiplies unbiased against them).  Plain adds: the
+      // bf16 dot product with ones stalled beside the matrix unit.
+      sum[qs] += e0 + e1;
       asm volatile("" : "+v"(sum[qs]));   // keep the sums in this slice
     };
 
@@ -1195,6 +1228,21 @@ void splash_fwd_wide(const FwdParams p) {
       wide_qk<D>(k_st[0], qf, lane, half, sc_a);
       finish(sc_a, lab0, 0, kv0 * kBK);
       if (__builtin_amdgcn_ballot_w64(rs.base[0] == -INFINITY || rs.base[1] == -INFINITY) != 0) set_base(sc_a);
+      if constexpr (!CAP) {
+        // The chunk's bases are fixed from here on: S(0) was formed from 0,
+        // later steps start their accumulators from -base.
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          const float b = rs.base[qs] == -INFINITY ? 0.f : rs.base[qs];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            sc_a[qs][v] -= b;
+            cb[qs][v] = -b;
+          }
+        }
+        // wait states between these VALU writes and the asm QK that reads cb
+        asm volatile("s_nop 4" ::: "memory");
+      }
 
       // Trip j runs the four steps u = 4j + t of block j.  Step u:
       //   top     wait for step u+1's K and mask words and step u-1's V
