@@ -568,7 +568,7 @@ extern "C" SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void 
 namespace {
 int64_t decode_ws_floats(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv, int64_t D) {
   const int64_t group = Hkv > 0 ? Hq / Hkv : 0;
-  return B * Hkv * decode_chunks(Skv) * group * (D + 2);
+  return B * Hkv * decode_chunks(B * Hkv, group, D, Skv) * group * (D + 2);
 }
 }  // namespace
 
@@ -601,8 +601,10 @@ extern "C" SPLASH_API splash_status splash_decode(const void *q, const void *k, 
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
     return fail(SPLASH_EUNSUPPORTED, "decode runs GQA groups of 1, 2, 4, 8 or 16 query heads");
   if (Skv == 0) return fail(SPLASH_EUNSUPPORTED, "decode needs at least one key");
-  if (B * Hkv > 0x7fffffffLL || decode_chunks(Skv) > 65535 || B * Hq > 0x7fffffffLL)
+  if (B * Hkv > 0x7fffffffLL || decode_chunks(B * Hkv, group, D, Skv) > 65535 || B * Hq > 0x7fffffffLL)
     return fail(SPLASH_EUNSUPPORTED, "grid too large");
+  if (Skv * D * 2 > 0x7fffffffLL)
+    return fail(SPLASH_EUNSUPPORTED, "the K (or V) cache of one head exceeds 2 GiB");
   if (!q || !k || !v || !out || !workspace) return fail(SPLASH_EINVAL, "NULL pointer");
   if (!aligned16({q, k, v, out, workspace})) return fail(SPLASH_EINVAL, "q, k, v, out and workspace must be 16-byte aligned");
   const int64_t floats = decode_ws_floats(B, Hq, Hkv, Skv, D);
@@ -620,7 +622,8 @@ extern "C" SPLASH_API splash_status splash_decode(const void *q, const void *k, 
   p.group = static_cast<int32_t>(group);
   p.D = static_cast<int32_t>(D);
   p.Skv = Skv;
-  p.n_chunks = static_cast<int32_t>(decode_chunks(Skv));
+  p.n_chunks = static_cast<int32_t>(decode_chunks(B * Hkv, group, D, Skv));
+  p.split_keys = decode_split_keys(B * Hkv, group, D, Skv);
   const float scale = resolve_scale(softmax_scale, D);
   const bool cap = std::isfinite(logits_soft_cap) && logits_soft_cap > 0.f;
   const double log2e = 1.4426950408889634;

@@ -11,9 +11,22 @@
 //      m = max m_c, l = sum l_c e^(m_c - m), out = sum o_c e^(m_c - m) / l,
 //      lse = m + log l (natural log).
 // HBM-bound: every K and V row of the cache is read once per kv head and
-// serves the whole GQA group, with 16-byte lane loads, 16 lanes per row.
+// serves the whole GQA group.
+//
+// Two partial kernels:
+//   * decode_stream (G * D <= 512: groups of up to 4 heads at D = 128, 8 at
+//     D = 64): a workgroup per (batch,
+//     kv head, key range of a few thousand keys) streams the range through a
+//     ring of four 32-key K/V stages in LDS, filled by direct-to-LDS loads
+//     three stages ahead, so the cache is read without pauses.  Each of its
+//     two waves keeps its own online softmax (running max, sum and output per
+//     head) over half of every stage's keys; the waves merge once at the end.
+//   * decode_partial (larger groups): a workgroup per 512-key chunk with the
+//     chunk's K and V rows in registers (the group's Q and outputs do not fit
+//     beside the streaming kernel's state).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "splash_kernel.h"
@@ -21,7 +34,10 @@
 namespace splash {
 namespace {
 
-constexpr int kChunk = 512;      // keys per partial workgroup
+constexpr int kChunk = 512;      // keys per partial workgroup (decode_partial)
+// decode_stream keeps G x D/4 outputs and G x D/8 Q words per lane: it serves
+// G * D <= 512 (groups of up to 4 heads at D = 128, 8 at D = 64).
+constexpr int kStreamMaxGD = 512;
 constexpr int kDThreads = 512;   // 8 waves; 512-key chunks measured 17 % faster than 256-key ones
 static_assert(kChunk == kDThreads, "the softmax phase gives each thread one key");
 constexpr float kLog2e = 1.4426950408889634f;
@@ -29,6 +45,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void unpack8(const u32x4 w, float (&x)[8]) {
 #pragma unroll
@@ -203,6 +221,289 @@ __global__ __launch_bounds__(kDThreads) void decode_partial(const DecodeParams p
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming partial kernel.
+constexpr int kSKeys = 32;               // keys per stage
+constexpr int kSStages = 4;              // ring of stages; loads run three ahead
+constexpr int kSWaves = 2;               // 16 keys of every stage per wave
+constexpr int kSThreads = 64 * kSWaves;
+constexpr float kBaseSlack = 32.f;       // see the exponent base in decode_stream
+
+// Buffer resource over `bytes` bytes at `base`; reads past the end return 0.
+__device__ __forceinline__ i32x4 stream_rsrc(const void *base, int64_t bytes) {
+  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+  i32x4 v;
+  __builtin_memcpy(&v, &r, sizeof(v));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  return v;
+}
+
+// Stage geometry: 32 key rows of D bf16, rows of 16-byte chunks, chunk c of
+// row r stored at chunk c ^ swz(r).  Lane (key kw, part pt) of a wave reads
+// the chunks of its quarter of a row; with the swizzle the 16 lanes of each
+// quarter-wave of a 16-byte LDS read hit 16 different bank groups.
+template <int D>
+struct SStage {
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kChunks = kRowBytes / 16;            // 16 (D = 128) or 8 (D = 64)
+  static constexpr int kBytes = kSKeys * kRowBytes;         // 8 KiB or 4 KiB
+  static constexpr int kSegsPerWave = kBytes / 1024 / kSWaves;   // 1 KiB loads per wave: 4 or 2
+  static constexpr int kRowsPerSeg = 1024 / kRowBytes;
+  __device__ static int swz(int row) {
+    if constexpr (D == 128) return row & 3;
+    else return (row >> 1) & 1;
+  }
+};
+
+// Direct-to-LDS loads of this wave's share of one stage: rows
+// [row0, row0 + 32) of a (batch, kv head) K or V array.  Lane l lands on
+// bytes 16 l of each 1 KiB segment; the swizzle is applied on the global side.
+// With the row counts above, the row a lane lands on has the same swizzle in
+// every segment, so one offset register and M0 value serve all segments (the
+// instruction offset moves both the LDS and the global address).  Issued from
+// inline assembly so the compiler does not order LDS reads of other stages
+// behind them; completion is awaited with s_waitcnt vmcnt before a barrier.
+template <int D>
+__device__ __forceinline__ void stream_stage(char *lds, i32x4 res, int64_t row0, int wave, int lane) {
+  using SG = SStage<D>;
+  const int row = lane / SG::kChunks;   // + 1 KiB segment * kRowsPerSeg, same swizzle
+  const uint32_t voff = static_cast<uint32_t>(row * SG::kRowBytes + ((lane % SG::kChunks) ^ SG::swz(row)) * 16);
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) char *)(lds + wave * SG::kSegsPerWave * 1024)));
+  const uint32_t soff = static_cast<uint32_t>(row0 * SG::kRowBytes) + wave * SG::kSegsPerWave * 1024;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (SG::kSegsPerWave == 4) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:3072 lds"
+        :: "s"(m0), "v"(voff), "s"(res), "s"(soff) : "memory", "m0");
+  } else {
+    static_assert(SG::kSegsPerWave == 2, "stage loads per wave");
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:1024 lds"
+        :: "s"(m0), "v"(voff), "s"(res), "s"(soff) : "memory", "m0");
+  }
+#pragma clang diagnostic pop
+}
+
+// Two bf16 from one 32-bit word (element 0 in the low half).  Through a copy:
+// hipcc lowered __builtin_bit_cast of an ext-vector element as element 0 of
+// the vector whatever the index.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
+  bf16x2 r;
+  __builtin_memcpy(&r, &w, sizeof(r));
+  return r;
+}
+
+// Sum over the four lanes of a quad (the four quarters of one key's row)
+// with DPP lane swaps: VALU moves, no LDS round trip.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));   // lanes ^ 1
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false));   // lanes ^ 2
+  return x;
+}
+
+// Wait until at most n of this wave's vector-memory loads are in flight.
+template <int N>
+__device__ __forceinline__ void stream_wait(int n) {
+  if constexpr (N == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= N) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    else stream_wait<N - 1>(n);
+  }
+}
+
+template <int D, int G, bool CAP>
+__global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams p) {
+  using SG = SStage<D>;
+  constexpr int kPart = D / 4;                 // elements of a row per lane (4 lanes per key)
+  constexpr int kPC = kPart / 8;               // 16-byte chunks per lane
+  constexpr int kLoadsPerStage = 2 * SG::kSegsPerWave;   // K and V, per wave
+  // One array, so the stages (the targets of the direct-to-LDS loads, whose
+  // LDS base comes from M0) sit in the first 64 KiB; the merge scalars after.
+  constexpr int kStBytes = 2 * kSStages * SG::kBytes;
+  static_assert(kStBytes <= 65536, "direct-to-LDS targets within the first 64 KiB");
+  constexpr int kOutBytes = kSWaves * (kSKeys / kSWaves) * G * D * 4;   // partial outputs at the end
+  constexpr int kArena = kStBytes > kOutBytes ? kStBytes : kOutBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kArena + 2 * kSWaves * G * 4];
+  char (*k_st)[SG::kBytes] = reinterpret_cast<char (*)[SG::kBytes]>(smem);
+  char (*v_st)[SG::kBytes] = reinterpret_cast<char (*)[SG::kBytes]>(smem + kSStages * SG::kBytes);
+  float (*mrg_m)[G] = reinterpret_cast<float (*)[G]>(smem + kArena);
+  float (*mrg_l)[G] = reinterpret_cast<float (*)[G]>(smem + kArena + kSWaves * G * 4);
+  static_assert(kSWaves * G * D * 4 <= kSStages * SG::kBytes, "the output merge reuses the K stages");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = lane >> 2, pt = lane & 3;     // key of the wave's 16, quarter of the row
+  const int unit = blockIdx.x;                 // (b, hkv)
+  const int split = blockIdx.y;
+  const int b = unit / p.Hkv, hkv = unit % p.Hkv;
+  const int64_t kb = static_cast<int64_t>(split) * p.split_keys;
+  const int64_t ke = min(kb + p.split_keys, p.Skv);
+  const int nst = static_cast<int>((ke - kb + kSKeys - 1) / kSKeys);   // >= 1
+
+  const int64_t kv_head = (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv;
+  const i32x4 k_res = stream_rsrc(static_cast<const __bf16 *>(p.k) + kv_head * D, p.Skv * SG::kRowBytes);
+  const i32x4 v_res = stream_rsrc(static_cast<const __bf16 *>(p.v) + kv_head * D, p.Skv * SG::kRowBytes);
+  auto issue = [&](int st) {   // stage st of this range into ring slot st % kSStages
+    stream_stage<D>(k_st[st % kSStages], k_res, kb + static_cast<int64_t>(st) * kSKeys, wave, lane);
+    stream_stage<D>(v_st[st % kSStages], v_res, kb + static_cast<int64_t>(st) * kSKeys, wave, lane);
+  };
+#pragma unroll
+  for (int st = 0; st < kSStages - 1; ++st)
+    if (st < nst) issue(st);
+
+  // this lane's quarter of the G query rows, as bf16 pairs
+  uint32_t qp[G][kPart / 2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const __bf16 *qr = static_cast<const __bf16 *>(p.q) + (static_cast<int64_t>(b) * p.Hq + hkv * G + g) * D + kPart * pt;
+#pragma unroll
+    for (int c = 0; c < kPC; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(qr + 8 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qp[g][4 * c + i] = w[i];
+    }
+  }
+
+  float m[G], l[G], o[G][kPart];   // per wave: running max (base 2, uniform), this lane's sums
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kPart; ++e) o[g][e] = 0.f;
+  }
+
+  const int row = kSKeys / kSWaves * wave + kw;   // this lane's key row within a stage
+  static_assert(kSKeys / kSWaves == 16, "a wave covers 16 keys x 4 quarters of a row");
+  const int sw = SG::swz(row);
+  for (int u = 0; u < nst; ++u) {
+    // stage u has landed in every wave; the slot stage u+3 refills was read
+    // in step u-1 by every wave
+    const int ahead = min(nst - 1 - u, kSStages - 2);   // stages issued after u
+    stream_wait<2 * kLoadsPerStage>(ahead * kLoadsPerStage);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (u + kSStages - 1 < nst) issue(u + kSStages - 1);
+
+    const char *kst = k_st[u % kSStages] + row * SG::kRowBytes;
+    const char *vst = v_st[u % kSStages] + row * SG::kRowBytes;
+    u32x4 kc[kPC], vc[kPC];
+#pragma unroll
+    for (int c = 0; c < kPC; ++c) {
+      kc[c] = *reinterpret_cast<const u32x4 *>(kst + ((kPC * pt + c) ^ sw) * 16);
+      vc[c] = *reinterpret_cast<const u32x4 *>(vst + ((kPC * pt + c) ^ sw) * 16);
+    }
+    const bool valid = kb + static_cast<int64_t>(u) * kSKeys + row < ke;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float acc0 = 0.f, acc1 = 0.f;   // two chains of dot products
+#pragma unroll
+      for (int c = 0; c < kPC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          acc0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kc[c][i]), as_bf16x2(qp[g][4 * c + i]), acc0, false);
+          acc1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kc[c][i + 1]), as_bf16x2(qp[g][4 * c + i + 1]), acc1,
+                                                 false);
+        }
+      const float acc = quad_sum(acc0 + acc1);
+      float s2;
+      if constexpr (CAP) {
+        const float xs = acc * p.c2;
+        const float e = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(xs));
+        const float th = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+        s2 = copysignf(th, xs) * p.cap_out;
+      } else {
+        s2 = acc * p.c2;
+      }
+      s2 = valid ? s2 : -INFINITY;
+      // The wave's exponent base m[g] is set by its first step with a valid
+      // key and moves only when a score exceeds it by more than 32 (base-2
+      // units), so exponentials stay below 2^32 and a step normally needs no
+      // cross-lane reduction.  Both tests are wave-uniform (ballots).
+      if (__builtin_amdgcn_ballot_w64(s2 > m[g] + kBaseSlack) != 0) {
+        float mx = s2;
+#pragma unroll
+        for (int x = 4; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x, 64));
+        mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));
+        const float a = __builtin_amdgcn_exp2f(m[g] - mx);   // 0 while m is -inf
+        l[g] *= a;
+#pragma unroll
+        for (int e = 0; e < kPart; ++e) o[g][e] *= a;
+        m[g] = mx;
+      }
+      const float pe = m[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s2 - m[g]);
+      l[g] += pe;
+#pragma unroll
+      for (int c = 0; c < kPC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[g][8 * c + 2 * i] += pe * __uint_as_float(vc[c][i] << 16);
+          o[g][8 * c + 2 * i + 1] += pe * __uint_as_float(vc[c][i] & 0xffff0000u);
+        }
+    }
+  }
+
+  // wave totals through LDS (the stages are free now): lane (kw, pt) stores
+  // its partial outputs at [wave][kw][g][quarter pt], then each output sums
+  // the 16 keys' partials of both waves.
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int x = 4; x < 64; x <<= 1) l[g] += __shfl_xor(l[g], x, 64);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages free
+  constexpr int kKw = kSKeys / kSWaves;   // 16 lanes (keys) per quarter
+  static_assert(kSWaves * kKw * G * D * 4 <= kArena, "partial outputs fit the arena");
+  float *o_lds = reinterpret_cast<float *>(smem);   // [kSWaves][kKw][G][D]
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < kPart; e += 4)
+      *reinterpret_cast<float4 *>(&o_lds[((wave * kKw + kw) * G + g) * D + kPart * pt + e]) =
+          make_float4(o[g][e], o[g][e + 1], o[g][e + 2], o[g][e + 3]);
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      mrg_m[wave][g] = m[g];
+      mrg_l[wave][g] = l[g];
+    }
+  }
+  __syncthreads();
+  const int64_t slot = static_cast<int64_t>(unit) * p.n_chunks + split;
+  for (int idx = tid; idx < G * D; idx += kSThreads) {
+    const int g = idx / D, d = idx % D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSWaves; ++w) mm = fmaxf(mm, mrg_m[w][g]);
+    float x = 0.f, lt = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kSWaves; ++w) {
+        const float a = mrg_m[w][g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrg_m[w][g] - mm);
+        float ow = 0.f;
+#pragma unroll
+        for (int j = 0; j < kKw; ++j) ow += o_lds[((w * kKw + j) * G + g) * D + d];
+        x += a * ow;
+        lt += a * mrg_l[w][g];
+      }
+    }
+    p.ws_o[(slot * G + g) * D + d] = x;
+    if (d == 0) {
+      p.ws_m[slot * G + g] = mm;
+      p.ws_l[slot * G + g] = lt;
+    }
+  }
+}
+
 // Merge of the chunks: one wave per (b, hq); lane i holds columns 2i, 2i+1
 // (D = 128) or column i (D = 64).
 template <int D, int G>
@@ -239,8 +540,13 @@ __global__ __launch_bounds__(64) void decode_merge(const DecodeParams p) {
 template <int D, int G>
 hipError_t go(const DecodeParams &p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(p.B * p.Hkv), static_cast<unsigned>(p.n_chunks));
-  if (p.cap) hipLaunchKernelGGL((decode_partial<D, G, true>), grid, dim3(kDThreads), 0, s, p);
-  else hipLaunchKernelGGL((decode_partial<D, G, false>), grid, dim3(kDThreads), 0, s, p);
+  if constexpr (G * D <= kStreamMaxGD) {
+    if (p.cap) hipLaunchKernelGGL((decode_stream<D, G, true>), grid, dim3(kSThreads), 0, s, p);
+    else hipLaunchKernelGGL((decode_stream<D, G, false>), grid, dim3(kSThreads), 0, s, p);
+  } else {
+    if (p.cap) hipLaunchKernelGGL((decode_partial<D, G, true>), grid, dim3(kDThreads), 0, s, p);
+    else hipLaunchKernelGGL((decode_partial<D, G, false>), grid, dim3(kDThreads), 0, s, p);
+  }
   hipLaunchKernelGGL((decode_merge<D, G>), dim3(static_cast<unsigned>(p.B * p.Hq)), dim3(64), 0, s, p);
   return hipGetLastError();
 }
@@ -258,7 +564,23 @@ hipError_t go_g(const DecodeParams &p, hipStream_t s) {
 
 }  // namespace
 
-int64_t decode_chunks(int64_t Skv) { return (Skv + kChunk - 1) / kChunk; }
+// Keys per partial workgroup.  Streaming kernel: whole 32-key stages, about
+// 512 workgroups over the launch (two per CU) when the cache is long enough,
+// and at least four stages per workgroup.  (1024 shorter ranges measured 9%
+// slower: each range ends with a merge of its waves.)  Larger groups: the 512-key chunks.
+int64_t decode_split_keys(int64_t units, int64_t group, int64_t D, int64_t Skv) {
+  if (group * D > kStreamMaxGD) return kChunk;
+  if (Skv <= 0 || units <= 0) return kSKeys;
+  const int64_t stages = (Skv + kSKeys - 1) / kSKeys;
+  int64_t splits = (512 + units - 1) / units;
+  splits = std::max<int64_t>(1, std::min(splits, (stages + 3) / 4));
+  return (stages + splits - 1) / splits * kSKeys;
+}
+
+int64_t decode_chunks(int64_t units, int64_t group, int64_t D, int64_t Skv) {
+  const int64_t k = decode_split_keys(units, group, D, Skv);
+  return (Skv + k - 1) / k;
+}
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   return p.D == 64 ? go_g<64>(p, stream) : go_g<128>(p, stream);

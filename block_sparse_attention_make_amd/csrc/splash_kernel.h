@@ -66,13 +66,15 @@ struct DecodeParams {
   float *lse;              // [B, Hq] or null
   int32_t B, Hq, Hkv, group, D;
   int64_t Skv;
-  int32_t n_chunks;
+  int32_t n_chunks;        // partial workgroups per (b, kv head)
+  int64_t split_keys;      // keys per partial workgroup (the last one may hold fewer)
   float c2, cap_out;       // as FwdParams
   int32_t cap;
   float *ws_o, *ws_m, *ws_l;   // [B * Hkv * n_chunks * group] (x D for ws_o)
 };
 
-int64_t decode_chunks(int64_t Skv);
+int64_t decode_split_keys(int64_t units, int64_t group, int64_t D, int64_t Skv);
+int64_t decode_chunks(int64_t units, int64_t group, int64_t D, int64_t Skv);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 
 }  // namespace splash

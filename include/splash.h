@@ -295,16 +295,18 @@ SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void *q, const v
  * MI355X: splash_fwd's attention with every key allowed,
  *   out_h = sum_j softmax_j(s_hj) v_j,  lse_h = log sum_j exp(s_hj),
  * s_hj = softmax_scale <q_h, k_j> (soft-capped if a cap is given), query head
- * h reading kv head h / (Hq / Hkv).  The keys are split into 512-key chunks
- * processed for a whole GQA group at once and merged by log-sum-exp.
+ * h reading kv head h / (Hq / Hkv).  The keys are split into ranges, each
+ * processed for a whole GQA group at once, and the ranges are merged by
+ * log-sum-exp.  Range sizes depend on B * Hkv, the group, D and Skv;
+ * splash_decode_workspace_size gives the matching scratch size.
  *
  * q: DEVICE bf16 [B, Hq, 1, D]; k, v: DEVICE bf16 [B, Hkv, Skv, D];
  * out: DEVICE bf16 [B, Hq, 1, D]; lse: DEVICE float32 [B, Hq] or NULL;
  * workspace: DEVICE scratch of at least splash_decode_workspace_size bytes,
  * overwritten.  All caller-owned, 16-byte aligned, valid until the kernels
  * end.  bf16 only; D == Dv in {64, 128}; Hq / Hkv in {1, 2, 4, 8, 16}; Skv >= 1
- * (else SPLASH_EUNSUPPORTED).  Asynchronous on hip_stream; allocates
- * nothing. */
+ * and Skv * D * 2 <= 2^31 - 1 bytes per head (else SPLASH_EUNSUPPORTED).
+ * Asynchronous on hip_stream; allocates nothing. */
 SPLASH_API splash_status splash_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv,
                                                       int64_t D, size_t *bytes);
 SPLASH_API splash_status splash_decode(const void *q, const void *k, const void *v, void *out, float *lse,

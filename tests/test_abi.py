@@ -158,6 +158,7 @@ def test_lse_merge_zero_rows_is_noop():
     (dict(ws=0), splash.EINVAL),
     (dict(ws_bytes=16), splash.EINVAL),              # too small
     (dict(q=8), splash.EINVAL),
+    (dict(Skv=1 << 23), splash.EUNSUPPORTED),        # one head's K cache of 2 GiB
 ])
 def test_decode_validation_errors_before_launch(over, status):
     lib = splash.load_library()
@@ -171,5 +172,14 @@ def test_decode_workspace_size():
     lib = splash.load_library()
     n = ctypes.c_size_t()
     assert lib.splash_decode_workspace_size(2, 8, 2, 1000, 128, ctypes.byref(n)) == splash.OK
-    assert n.value == 2 * 2 * 2 * 4 * (128 + 2) * 4      # 2 chunks of 512 keys, groups of 4
+    # groups of 4 at D = 128 stream 32-key stages: 4 (b, kv head) units x 32 stages -> 8 key
+    # ranges of 4 stages (128 keys) each (at least 4 stages per range), (D + 2) floats per range
+    # and query head
+    assert n.value == 2 * 2 * 8 * 4 * (128 + 2) * 4
+    # the bench's decode shape: 64 units x 1024 stages -> 8 ranges of 4096 keys (512 workgroups)
+    assert lib.splash_decode_workspace_size(8, 32, 8, 32768, 128, ctypes.byref(n)) == splash.OK
+    assert n.value == 8 * 8 * 8 * 4 * (128 + 2) * 4
+    # groups of 16 keep 512-key chunks: 2 chunks for 1000 keys
+    assert lib.splash_decode_workspace_size(1, 16, 1, 1000, 128, ctypes.byref(n)) == splash.OK
+    assert n.value == 1 * 1 * 2 * 16 * (128 + 2) * 4
     assert lib.splash_decode_workspace_size(1, 3, 2, 10, 64, ctypes.byref(n)) == splash.EINVAL

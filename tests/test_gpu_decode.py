@@ -26,6 +26,9 @@ CASES = [
     ("gqa16_short", 134, 1, 16, 1, 77, 128, None),
     ("d64_gqa2", 135, 3, 4, 2, 513, 64, None),
     ("one_key", 136, 1, 2, 1, 1, 128, None),
+    # 16 (b, kv head) units: 32 key ranges of 40 stages, the last one ragged
+    ("gqa4_many_stages", 137, 4, 16, 4, 40000, 128, None),
+    ("gqa8_d64_many_stages_cap", 138, 2, 16, 2, 30001, 64, 30.0),
 ]
 
 
