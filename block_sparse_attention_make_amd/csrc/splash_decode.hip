@@ -17,8 +17,8 @@
 //   * decode_stream (G * D <= 512: groups of up to 4 heads at D = 128, 8 at
 //     D = 64): a workgroup per (batch,
 //     kv head, key range of a few thousand keys) streams the range through a
-//     ring of four 32-key K/V stages in LDS, filled by direct-to-LDS loads
-//     three stages ahead, so the cache is read without pauses.  Each of its
+//     ring of five 32-key K/V stages in LDS, filled by direct-to-LDS loads
+//     four stages ahead, so the cache is read without pauses.  Each of its
 //     two waves keeps its own online softmax (running max, sum and output per
 //     head) over half of every stage's keys; the waves merge once at the end.
 //   * decode_partial (larger groups): a workgroup per 512-key chunk with the
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kDThreads) void decode_partial(const DecodeParams p
 // ---------------------------------------------------------------------------
 // Streaming partial kernel.
 constexpr int kSKeys = 32;               // keys per stage
-constexpr int kSStages = 4;              // ring of stages; loads run three ahead
+constexpr int kSStages = 5;              // ring of stages; loads run four ahead
 constexpr int kSWaves = 2;               // 16 keys of every stage per wave
 constexpr int kSThreads = 64 * kSWaves;
 constexpr float kBaseSlack = 32.f;       // see the exponent base in decode_stream
@@ -328,18 +328,19 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
   constexpr int kPart = D / 4;                 // elements of a row per lane (4 lanes per key)
   constexpr int kPC = kPart / 8;               // 16-byte chunks per lane
   constexpr int kLoadsPerStage = 2 * SG::kSegsPerWave;   // K and V, per wave
-  // One array, so the stages (the targets of the direct-to-LDS loads, whose
-  // LDS base comes from M0) sit in the first 64 KiB; the merge scalars after.
+  // One arena: the stages during the loop; the waves' partial outputs and
+  // the merge scalars after it.  80 KiB at D = 128, so two workgroups share
+  // a CU's 160 KiB.
   constexpr int kStBytes = 2 * kSStages * SG::kBytes;
-  static_assert(kStBytes <= 65536, "direct-to-LDS targets within the first 64 KiB");
   constexpr int kOutBytes = kSWaves * (kSKeys / kSWaves) * G * D * 4;   // partial outputs at the end
-  constexpr int kArena = kStBytes > kOutBytes ? kStBytes : kOutBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[kArena + 2 * kSWaves * G * 4];
+  constexpr int kMrgBytes = 2 * kSWaves * G * 4;
+  constexpr int kArena = kStBytes > kOutBytes + kMrgBytes ? kStBytes : kOutBytes + kMrgBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kArena];
   char (*k_st)[SG::kBytes] = reinterpret_cast<char (*)[SG::kBytes]>(smem);
   char (*v_st)[SG::kBytes] = reinterpret_cast<char (*)[SG::kBytes]>(smem + kSStages * SG::kBytes);
-  float (*mrg_m)[G] = reinterpret_cast<float (*)[G]>(smem + kArena);
-  float (*mrg_l)[G] = reinterpret_cast<float (*)[G]>(smem + kArena + kSWaves * G * 4);
-  static_assert(kSWaves * G * D * 4 <= kSStages * SG::kBytes, "the output merge reuses the K stages");
+  // (written after the loop, when the stages are free)
+  float (*mrg_m)[G] = reinterpret_cast<float (*)[G]>(smem + kOutBytes);
+  float (*mrg_l)[G] = reinterpret_cast<float (*)[G]>(smem + kOutBytes + kSWaves * G * 4);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
     // stage u has landed in every wave; the slot stage u+3 refills was read
     // in step u-1 by every wave
     const int ahead = min(nst - 1 - u, kSStages - 2);   // stages issued after u
-    stream_wait<2 * kLoadsPerStage>(ahead * kLoadsPerStage);
+    stream_wait<(kSStages - 2) * kLoadsPerStage>(ahead * kLoadsPerStage);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (u + kSStages - 1 < nst) issue(u + kSStages - 1);
 
