@@ -634,13 +634,6 @@ __device__ __forceinline__ void qk_mfma(f32x16 &acc, const bf16x8 &a, const bf16
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(q));
 }
 
-// The first k-step of a tile with the accumulator started from `c` instead
-// of 0: with Q pre-scaled to base-2 units, c = -(the row's exponent base)
-// makes the matrix unit deliver the exponent itself.  `c` is only read.
-__device__ __forceinline__ void qk_mfma_c(f32x16 &acc, const bf16x8 &a, const bf16x8 &q, const f32x16 &c) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(acc) : "v"(a), "a"(q), "v"(c));
-}
-
 // Wait states covering the result latency of the last qk_mfma before its
 // accumulator is read by VALU instructions (16 passes, generously).
 __device__ __forceinline__ void qk_drain() {
@@ -874,19 +867,6 @@ void splash_fwd_wide(const FwdParams p) {
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) qpos_ld[qs] = p.q_seq[q_row0 + 32 * qs];
     }
-    // Without a soft cap Q is scaled once here by softmax_scale * log2(e), so
-    // every score comes out of the matrix unit in base-2 units and the
-    // softmax needs no multiply per score.  (One more bf16 rounding of each
-    // Q element: about 2^-9 relative, the size of the rounding P gets.)
-    if constexpr (!CAP) {
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            x[qs][ks][e] = static_cast<__bf16>(static_cast<float>(x[qs][ks][e]) * p.c2);
-    }
     // Q lives in AGPRs for the whole kernel: the QK instructions read it
     // from there, which leaves the VGPRs to the scores and P.
 #pragma unroll
@@ -911,10 +891,12 @@ void splash_fwd_wide(const FwdParams p) {
       hi[qs] = static_cast<int>(clamp64(h64 - p.kv_offset, -1, p.Skv));
     }
   }
-  // Scores as the QK instructions leave them are in base-2 units without a
-  // cap (Q is pre-scaled); with a cap they are raw and the cap takes p.c2.
-  constexpr float c2e = 1.f;
-  f32x16 cb[2];   // no cap: -(exponent base) per row, the first QK k-step's C
+  // Scores leave the QK instructions as raw dot products.  Without a cap,
+  // c2e = softmax_scale * log2(e) turns them into base-2 logits; with a cap
+  // the cap takes p.c2 and the capped logits are already base-2.  (Q is not
+  // pre-scaled: a bf16 rounding of Q * scale errs by up to 2^-8 of a logit,
+  // which large logits along one dominant direction do not average away.)
+  const float c2e = CAP ? 1.f : p.c2;
 
   // Compact one chunk of the block row's grid positions: keep label > 0.
   // Entry j + 1 is the block data_next points the pipeline at after entry j.
@@ -1034,14 +1016,7 @@ void splash_fwd_wide(const FwdParams p) {
     auto mfma_one = [&](int i, int sub) {
       const int qs = sub >> 1;
       if ((sub & 1) == 0) {
-        if (i < kKS) {
-          if constexpr (!CAP) {
-            if (i == 0) qk_mfma_c(sc_nxt[qs], ka[0], qf[qs][0], cb[qs]);
-            else qk_mfma(sc_nxt[qs], ka[i], qf[qs][i], false);
-          } else {
-            qk_mfma(sc_nxt[qs], ka[i], qf[qs][i], i == 0);
-          }
-        }
+        if (i < kKS) qk_mfma(sc_nxt[qs], ka[i], qf[qs][i], i == 0);
       } else if (i < kPVOps) {
         const int h = i / kDT, dt = i % kDT;
         o[dt][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pf_prv[qs][h], o[dt][qs], 0, 0, 0);
@@ -1051,23 +1026,25 @@ void splash_fwd_wide(const FwdParams p) {
       if (i < kKS) ka[i] = read_k(i);
       if (i < kPVOps) va[i] = read_v(i);
     };
-    float b2[2], sum[2] = {0.f, 0.f};
-    const float kc2 = 2.f * kLog2e * p.c2;   // CAP: x -> 2 y log2 e
+    float b2[2], kr[2], sum[2] = {0.f, 0.f};   // kr (cap): cap log2(e) - base, per row
+    const float kc2 = 2.f * kLog2e * p.c2;   // cap: raw score -> 2 y log2(e), y = logit / cap
+    const float m2cap = -2.f * p.cap_out;
     float eg[2][4];   // exponentials of slices i (even / odd), until packed
     auto exp_one = [&](int i, int k) {   // element 4(i%4) + k of row half i/4
       const int qs = i / 4;
       const float x = sc_cur[qs][4 * (i % 4) + k];
       if constexpr (CAP) {
-        // Capped logit in base-2 units: with y = x c2,
-        // tanh y = 1 - 2 / (1 + e^{2y}), which reaches +-1 exactly at the
-        // float range's ends.  x 2^-100 lies far below the rounding of any
-        // finite logit but keeps a masked key (-inf) at -inf, without a
-        // select (which the compiler turns into a branch around the cap).
-        const float t = __builtin_amdgcn_exp2f(x * kc2);
-        const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + t), 1.f);
-        eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(th, p.cap_out, __builtin_fmaf(x, 0x1p-100f, -b2[qs])));
+        // Capped logit in base-2 units, cap log2(e) tanh y with y = logit / cap:
+        // with r = 1 / (1 + e^{2y}), tanh y = 1 - 2r, which reaches +-1
+        // exactly at the float range's ends, so the exponent is one FMA,
+        // r (-2 cap log2 e) + (cap log2 e - base).  x 2^-100 lies far below
+        // the rounding of any finite logit but keeps a masked key (-inf) at
+        // -inf, without a select (which the compiler turns into a branch
+        // around the cap).
+        const float r = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * kc2));
+        eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(r, m2cap, __builtin_fmaf(x, 0x1p-100f, kr[qs])));
       } else {
-        eg[i & 1][k] = __builtin_amdgcn_exp2f(x);   // already s * scale * log2(e) - base
+        eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2e, -b2[qs]));
       }
     };
     auto pack = [&](int i, int pr) {   // elements 2pr, 2pr+1 of slice i -> P, row sum
@@ -1087,7 +1064,10 @@ void splash_fwd_wide(const FwdParams p) {
     reads_slice(0);
     reads_slice(1);
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) b2[qs] = rs.base[qs] == -INFINITY ? 0.f : rs.base[qs];
+    for (int qs = 0; qs < 2; ++qs) {
+      b2[qs] = rs.base[qs] == -INFINITY ? 0.f : rs.base[qs];
+      kr[qs] = p.cap_out - b2[qs];
+    }
     __builtin_amdgcn_sched_barrier(0);
     // Each slice is four sub-slices of one matrix instruction each, with
     // about one matrix instruction's worth of other work beneath it (an
@@ -1228,21 +1208,6 @@ void splash_fwd_wide(const FwdParams p) {
       wide_qk<D>(k_st[0], qf, lane, half, sc_a);
       finish(sc_a, lab0, 0, kv0 * kBK);
       if (__builtin_amdgcn_ballot_w64(rs.base[0] == -INFINITY || rs.base[1] == -INFINITY) != 0) set_base(sc_a);
-      if constexpr (!CAP) {
-        // The chunk's bases are fixed from here on: S(0) was formed from 0,
-        // later steps start their accumulators from -base.
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-          const float b = rs.base[qs] == -INFINITY ? 0.f : rs.base[qs];
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            sc_a[qs][v] -= b;
-            cb[qs][v] = -b;
-          }
-        }
-        // wait states between these VALU writes and the asm QK that reads cb
-        asm volatile("s_nop 4" ::: "memory");
-      }
 
       // Trip j runs the four steps u = 4j + t of block j.  Step u:
       //   top     wait for step u+1's K and mask words and step u-1's V

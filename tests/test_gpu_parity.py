@@ -137,6 +137,18 @@ def test_scores_outgrowing_first_block_base(kind, kw, cap):
     compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], f"growing_{kind}")
 
 
+def test_large_logits_along_one_direction():
+    """Logits up to about 74 along one dominant query/key direction: the scale
+    must be applied to the float scores.  Rounding q * scale to bf16 first (an
+    error of up to 2^-8 of each logit, which one dominant direction does not
+    average away; here 29 * scale rounds 0.14% off) would put the lse about 0.1
+    off."""
+    q, k, v = _growing_scores(72, 1, 2, 512, 128, a=29.0, b=29.0)
+    o, l, _ = run_gpu(q, k, v, "causal")
+    o_ref, l_ref = oracle_full(q, k, v, "causal")
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], "large_logits_causal")
+
+
 def test_scores_outgrowing_base_dense_mask():
     q, k, v = _growing_scores(71, 1, 2, 512, 128)
     rng = np.random.default_rng(72)
