@@ -635,9 +635,10 @@ __device__ __forceinline__ void qk_mfma(f32x16 &acc, const bf16x8 &a, const bf16
 }
 
 // Wait states covering the result latency of the last qk_mfma before its
-// accumulator is read by VALU instructions (16 passes, generously).
+// accumulator is read by VALU instructions: 24, above the 19 a 16-pass XDL
+// result needs (the 32x32x16 bf16 instruction takes 8 passes).
 __device__ __forceinline__ void qk_drain() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 }
 
 // S^T for one 32-key step: sc[qs] holds, for this lane's row of half qs, keys
@@ -700,8 +701,11 @@ __device__ __forceinline__ void wide_cap_mask(const FwdParams &p, f32x16 *sc, in
         const unsigned w = mword[qs] >> (4 * half);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
+          // bit c sign-extended (0 or all ones) selects the score or -inf,
+          // bit by bit: a bitfield extract and a bitfield select
           const int c = 8 * (v / 4) + (v % 4);
-          sc[qs][v] = ((w >> c) & 1u) ? sc[qs][v] : -INFINITY;
+          const int m = __builtin_amdgcn_sbfe(static_cast<int>(w), c, 1);
+          sc[qs][v] = __int_as_float((m & __float_as_int(sc[qs][v])) | (~m & static_cast<int>(0xff800000u)));
         }
       }
     } else {
