@@ -712,12 +712,17 @@ __device__ __forceinline__ void wide_cap_mask(const FwdParams &p, f32x16 *sc, in
       const int kb = key0 + 4 * half;
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
-        const int rlo = min(max(lo[qs] - kb, -1), kSK);
-        const int rhi = min(max(hi[qs] - kb, -1), kSK);
+        // the row's allowed keys [lo, hi] as a word of this lane's keys
+        // (bit c <=> key kb + c), then the dense masks' two-instruction select
+        const int b0 = min(max(lo[qs] - kb, 0), kSK);       // first allowed bit
+        const int b1 = min(max(hi[qs] - kb + 1, 0), kSK);   // one past the last
+        const uint64_t span = b1 > b0 ? (uint64_t(1) << b1) - (uint64_t(1) << b0) : 0;
+        const int w = static_cast<int>(static_cast<uint32_t>(span));
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int c = 8 * (v / 4) + (v % 4);
-          sc[qs][v] = (c >= rlo && c <= rhi) ? sc[qs][v] : -INFINITY;
+          const int m = __builtin_amdgcn_sbfe(w, c, 1);
+          sc[qs][v] = __int_as_float((m & __float_as_int(sc[qs][v])) | (~m & static_cast<int>(0xff800000u)));
         }
       }
     }
