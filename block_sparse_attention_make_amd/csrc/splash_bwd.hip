@@ -324,6 +324,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
   // offset of each other, so their reads share address registers
   __shared__ __attribute__((aligned(1024))) char qdo_t[2][2][T::kBytes];
   __shared__ __attribute__((aligned(16))) float lse_s[2][kBlk], di_s[2][kBlk];
+  // computable masks: each row's allowed keys in this key block as a first key
+  // and a count (0 for none); dense masks: the packed words (all ones for
+  // full blocks)
   __shared__ __attribute__((aligned(16))) int lo_s[2][kBlk], hi_s[2][kBlk];
   __shared__ __attribute__((aligned(16))) unsigned mw_s[2][4 * kBlk];
 
@@ -384,7 +387,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
         lo -= kb0;
         hi -= kb0;
         sm.lo = static_cast<int>(lo < -1 ? -1 : (lo > kBlk ? kBlk : lo));
-        sm.hi = static_cast<int>(hi < -1 ? -1 : (hi > kBlk ? kBlk : hi));
+        const int hc = static_cast<int>(hi < -1 ? -1 : (hi > kBlk ? kBlk : hi));
+        sm.hi = hc >= sm.lo ? hc - sm.lo + 1 : 0;   // count of allowed keys from lo
       }
     }
     if constexpr (DENSE) {
@@ -406,10 +410,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
       }
     }
     if constexpr (DENSE) {
-      if (label == 1) {
-        mw_s[buf][tid] = sm.m0;
-        mw_s[buf][tid + kThreads] = sm.m1;
-      }
+      mw_s[buf][tid] = label == 1 ? sm.m0 : ~0u;   // full blocks: every key allowed
+      mw_s[buf][tid + kThreads] = label == 1 ? sm.m1 : ~0u;
     }
   };
   auto entry = [&](int gg, int ee, int &r, int &label) {
@@ -502,21 +504,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
           G.hi4 = *reinterpret_cast<const i32x4 *>(&hi_s[buf][qi0]);
         }
       };
-      const bool partial = label == 1;
       auto elem = [&](int qb, int v, const Grp &G) {
         const int k = v & 3;
         const float sv = sA[qb & 1][v], dpv = dpA[qb & 1][v];
         float s2, gf = 1.f;
         if constexpr (CAP) capped(sv, kc2, f.cap_out, s2, gf);
         else s2 = sv * f.c2;
-        // (bitwise &: short-circuit tests become branches)
-        bool in = true;
+        // The staged interval or words hold every key of a full block, and a
+        // row with no allowed key (lse -inf) has none in any block, so this
+        // one test covers labels 1 and 2 and empty rows.
+        bool in;
         if constexpr (DENSE) in = ((G.mw[k] >> (lane & 31)) & 1u) != 0u;
-        else in = (key_local >= G.lo4[k]) & (key_local <= G.hi4[k]);
-        const bool ok = (G.l4[k] != -INFINITY) & (!partial | in);
+        else in = static_cast<unsigned>(key_local - G.lo4[k]) < static_cast<unsigned>(G.hi4[k]);
         // select the exponent, not the exponential: a select between an
         // exponential and 0 becomes a branch around every exponential
-        const float pv = __builtin_amdgcn_exp2f(ok ? s2 - G.l4[k] : -INFINITY);
+        const float pv = __builtin_amdgcn_exp2f(in ? s2 - G.l4[k] : -INFINITY);
         const float dsv = pv * (dpv - G.d4[k]) * gf;
         pbB[qb & 1][v / 8][v % 8] = static_cast<__bf16>(pv);
         sbB[qb & 1][v / 8][v % 8] = static_cast<__bf16>(dsv);
