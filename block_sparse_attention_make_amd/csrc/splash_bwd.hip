@@ -683,23 +683,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
         mfma_v(dp, av, dob[ks], ks == 0);
       }
       mfma_drain(s, dp);
-      unsigned mword = 0u;
-      if constexpr (DENSE) {
-        if (label == 1) mword = mw_s[buf][kb4 * kBlk + 32 * wave + (lane & 31)];
+      // This lane's row's allowed keys among the 32 keys of kb4 as a word
+      // (bit c <=> key 32 kb4 + 4 half + c of the layout below), all ones in
+      // a full block.  A row with no allowed key has an empty word in every
+      // block it meets (label 2 blocks have none), so no lse test is needed.
+      unsigned word = ~0u;
+      if (label == 1) {
+        if constexpr (DENSE) {
+          word = mw_s[buf][kb4 * kBlk + 32 * wave + (lane & 31)] >> (4 * half);
+        } else {
+          const int kb = 32 * kb4 + 4 * half;
+          const int b0 = min(max(rlo - kb, 0), 32);
+          const int b1 = min(max(rhi - kb + 1, 0), 32);
+          word = b1 > b0 ? static_cast<unsigned>((uint64_t(1) << b1) - (uint64_t(1) << b0)) : 0u;
+        }
       }
       bf16x8 sb[2];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int kl = 32 * kb4 + 8 * (v / 4) + 4 * half + (v % 4);   // key within the block
+        const int c = 8 * (v / 4) + (v % 4);   // key 32 kb4 + 4 half + c of the block
         float s2, gf = 1.f;
         if constexpr (CAP) capped(s[v], kc2, f.cap_out, s2, gf);
         else s2 = s[v] * f.c2;
-        bool ok = lse2 != -INFINITY;
-        if (label == 1) {   // (bitwise &: short-circuit tests become branches)
-          if constexpr (DENSE) ok = ok & (((mword >> (kl & 31)) & 1u) != 0u);
-          else ok = ok & (kl >= rlo) & (kl <= rhi);
-        }
-        const float pv = __builtin_amdgcn_exp2f(ok ? s2 - lse2 : -INFINITY);   // (as in the dK/dV kernel)
+        // bit c sign-extended selects the exponent or -inf, bit by bit
+        const int m = __builtin_amdgcn_sbfe(static_cast<int>(word), c, 1);
+        const float x = __int_as_float((m & __float_as_int(s2 - lse2)) | (~m & static_cast<int>(0xff800000u)));
+        const float pv = __builtin_amdgcn_exp2f(x);
         sb[v / 8][v % 8] = static_cast<__bf16>(pv * (dp[v] - di) * gf);
       }
 #pragma unroll
