@@ -29,6 +29,8 @@ CASES = [
     # 16 (b, kv head) units: 32 key ranges of 40 stages, the last one ragged
     ("gqa4_many_stages", 137, 4, 16, 4, 40000, 128, None),
     ("gqa8_d64_many_stages_cap", 138, 2, 16, 2, 30001, 64, 30.0),
+    # 512 (b, kv head) units: one key range of 94 stages per unit
+    ("gqa2_d64_one_range_per_unit", 139, 32, 32, 16, 3000, 64, None),
 ]
 
 
