@@ -513,12 +513,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
         // The staged interval or words hold every key of a full block, and a
         // row with no allowed key (lse -inf) has none in any block, so this
         // one test covers labels 1 and 2 and empty rows.
-        bool in;
-        if constexpr (DENSE) in = ((G.mw[k] >> (lane & 31)) & 1u) != 0u;
-        else in = static_cast<unsigned>(key_local - G.lo4[k]) < static_cast<unsigned>(G.hi4[k]);
         // select the exponent, not the exponential: a select between an
         // exponential and 0 becomes a branch around every exponential
-        const float pv = __builtin_amdgcn_exp2f(in ? s2 - G.l4[k] : -INFINITY);
+        float x;
+        if constexpr (DENSE) {   // the key's bit sign-extended selects, bit by bit
+          const int m = __builtin_amdgcn_sbfe(static_cast<int>(G.mw[k]), lane & 31, 1);
+          x = __int_as_float((m & __float_as_int(s2 - G.l4[k])) | (~m & static_cast<int>(0xff800000u)));
+        } else {
+          const bool in = static_cast<unsigned>(key_local - G.lo4[k]) < static_cast<unsigned>(G.hi4[k]);
+          x = in ? s2 - G.l4[k] : -INFINITY;
+        }
+        const float pv = __builtin_amdgcn_exp2f(x);
         const float dsv = pv * (dpv - G.d4[k]) * gf;
         pbB[qb & 1][v / 8][v % 8] = static_cast<__bf16>(pv);
         sbB[qb & 1][v / 8][v % 8] = static_cast<__bf16>(dsv);
