@@ -14,8 +14,8 @@
 // serves the whole GQA group.
 //
 // Two partial kernels:
-//   * decode_stream (G * D <= 512: groups of up to 4 heads at D = 128, 8 at
-//     D = 64): a workgroup per (batch,
+//   * decode_stream (G * D <= 1024: groups of up to 8 heads at D = 128, 16
+//     at D = 64): a workgroup per (batch,
 //     kv head, key range of a few thousand keys) streams the range through a
 //     ring of five 32-key K/V stages in LDS, filled by direct-to-LDS loads
 //     four stages ahead, so the cache is read without pauses.  Each of its
@@ -35,9 +35,10 @@ namespace splash {
 namespace {
 
 constexpr int kChunk = 512;      // keys per partial workgroup (decode_partial)
-// decode_stream keeps G x D/4 outputs and G x D/8 Q words per lane: it serves
-// G * D <= 512 (groups of up to 4 heads at D = 128, 8 at D = 64).
-constexpr int kStreamMaxGD = 512;
+// decode_stream keeps G x D/L outputs and G x D/2L Q words per lane (L = 4 or
+// 8 lanes per key): it serves G * D <= 1024 (groups of up to 8 heads at
+// D = 128, 16 at D = 64).
+constexpr int kStreamMaxGD = 1024;
 constexpr int kDThreads = 512;   // 8 waves; 512-key chunks measured 17 % faster than 256-key ones
 static_assert(kChunk == kDThreads, "the softmax phase gives each thread one key");
 constexpr float kLog2e = 1.4426950408889634f;
@@ -303,11 +304,14 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
   return r;
 }
 
-// Sum over the four lanes of a quad (the four quarters of one key's row)
-// with DPP lane swaps: VALU moves, no LDS round trip.
-__device__ __forceinline__ float quad_sum(float x) {
+// Sum over the L lanes that hold the parts of one key's row (L = 4: a quad;
+// L = 8: two quads) with DPP lane moves: VALU only, no LDS round trip.
+template <int L>
+__device__ __forceinline__ float parts_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));   // lanes ^ 1
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false));   // lanes ^ 2
+  if constexpr (L == 8)   // row_half_mirror: lane i <-> 7 - i of each 8, the other quad
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));
   return x;
 }
 
@@ -325,14 +329,21 @@ __device__ __forceinline__ void stream_wait(int n) {
 template <int D, int G, bool CAP>
 __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams p) {
   using SG = SStage<D>;
-  constexpr int kPart = D / 4;                 // elements of a row per lane (4 lanes per key)
+  // L lanes share a key row: 4 while G * D <= 512, else 8 (half the Q words
+  // and outputs per lane); a wave covers 64 / L keys per pass and 16 keys
+  // of every stage in 16 L / 64 passes.
+  constexpr int L = G * D <= 512 ? 4 : 8;
+  constexpr int kKw = 64 / L;                  // keys per pass of a wave
+  constexpr int kPasses = kSKeys / kSWaves / kKw;
+  constexpr int kPart = D / L;                 // elements of a row per lane
   constexpr int kPC = kPart / 8;               // 16-byte chunks per lane
+  static_assert(kPC >= 1 && kPasses >= 1, "lane split");
   constexpr int kLoadsPerStage = 2 * SG::kSegsPerWave;   // K and V, per wave
   // One arena: the stages during the loop; the waves' partial outputs and
   // the merge scalars after it.  80 KiB at D = 128, so two workgroups share
   // a CU's 160 KiB.
   constexpr int kStBytes = 2 * kSStages * SG::kBytes;
-  constexpr int kOutBytes = kSWaves * (kSKeys / kSWaves) * G * D * 4;   // partial outputs at the end
+  constexpr int kOutBytes = kSWaves * kKw * G * D * 4;   // partial outputs at the end
   constexpr int kMrgBytes = 2 * kSWaves * G * 4;
   constexpr int kArena = kStBytes > kOutBytes + kMrgBytes ? kStBytes : kOutBytes + kMrgBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kArena];
@@ -344,7 +355,7 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kw = lane >> 2, pt = lane & 3;     // key of the wave's 16, quarter of the row
+  const int kw = lane / L, pt = lane % L;      // key of the pass, part of the row
   const int unit = blockIdx.x;                 // (b, hkv)
   const int split = blockIdx.y;
   const int b = unit / p.Hkv, hkv = unit % p.Hkv;
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
   for (int st = 0; st < kSStages - 1; ++st)
     if (st < nst) issue(st);
 
-  // this lane's quarter of the G query rows, as bf16 pairs
+  // this lane's part of the G query rows, as bf16 pairs
   uint32_t qp[G][kPart / 2];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -385,9 +396,6 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
     for (int e = 0; e < kPart; ++e) o[g][e] = 0.f;
   }
 
-  const int row = kSKeys / kSWaves * wave + kw;   // this lane's key row within a stage
-  static_assert(kSKeys / kSWaves == 16, "a wave covers 16 keys x 4 quarters of a row");
-  const int sw = SG::swz(row);
   for (int u = 0; u < nst; ++u) {
     // stage u has landed in every wave; the slot stage u+3 refills was read
     // in step u-1 by every wave
@@ -396,6 +404,10 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (u + kSStages - 1 < nst) issue(u + kSStages - 1);
 
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+    const int row = kSKeys / kSWaves * wave + kKw * pass + kw;   // this lane's key row of the stage
+    const int sw = SG::swz(row);
     const char *kst = k_st[u % kSStages] + row * SG::kRowBytes;
     const char *vst = v_st[u % kSStages] + row * SG::kRowBytes;
     u32x4 kc[kPC], vc[kPC];
@@ -416,7 +428,7 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
           acc1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kc[c][i + 1]), as_bf16x2(qp[g][4 * c + i + 1]), acc1,
                                                  false);
         }
-      const float acc = quad_sum(acc0 + acc1);
+      const float acc = parts_sum<L>(acc0 + acc1);
       float s2;
       if constexpr (CAP) {
         const float xs = acc * p.c2;
@@ -434,7 +446,7 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
       if (__builtin_amdgcn_ballot_w64(s2 > m[g] + kBaseSlack) != 0) {
         float mx = s2;
 #pragma unroll
-        for (int x = 4; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x, 64));
+        for (int x = L; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x, 64));
         mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));
         const float a = __builtin_amdgcn_exp2f(m[g] - mx);   // 0 while m is -inf
         l[g] *= a;
@@ -452,17 +464,17 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
           o[g][8 * c + 2 * i + 1] += pe * __uint_as_float(vc[c][i] & 0xffff0000u);
         }
     }
+    }   // pass
   }
 
   // wave totals through LDS (the stages are free now): lane (kw, pt) stores
-  // its partial outputs at [wave][kw][g][quarter pt], then each output sums
-  // the 16 keys' partials of both waves.
+  // its partial outputs at [wave][kw][g][part pt], then each output sums
+  // the kKw lanes' partials of both waves.
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int x = 4; x < 64; x <<= 1) l[g] += __shfl_xor(l[g], x, 64);
+    for (int x = L; x < 64; x <<= 1) l[g] += __shfl_xor(l[g], x, 64);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages free
-  constexpr int kKw = kSKeys / kSWaves;   // 16 lanes (keys) per quarter
   static_assert(kSWaves * kKw * G * D * 4 <= kArena, "partial outputs fit the arena");
   float *o_lds = reinterpret_cast<float *>(smem);   // [kSWaves][kKw][G][D]
 #pragma unroll

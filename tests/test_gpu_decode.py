@@ -31,6 +31,9 @@ CASES = [
     ("gqa8_d64_many_stages_cap", 138, 2, 16, 2, 30001, 64, 30.0),
     # 512 (b, kv head) units: one key range of 94 stages per unit
     ("gqa2_d64_one_range_per_unit", 139, 32, 32, 16, 3000, 64, None),
+    # groups with G * D > 512 stream with 8 lanes per key (two passes per stage)
+    ("gqa8_long_ragged", 140, 2, 16, 2, 20001, 128, None),
+    ("gqa16_d64_cap", 141, 2, 32, 2, 5000, 64, 30.0),
 ]
 
 
