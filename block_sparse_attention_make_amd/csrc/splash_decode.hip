@@ -4,26 +4,19 @@
 // TPU (EasyDeL BlockSparseAttn.forward_native); this is the MI355X-native
 // path for that case.  It is the forward's masked softmax attention with
 // every key allowed, split along the keys (flash decoding):
-//   1. partials: a workgroup per (batch, kv head, 512-key chunk) computes, for
-//      the G query heads of the kv head's GQA group at once, the chunk's
-//      scores, its max m_c, sum l_c and unnormalised output o_c;
-//   2. merge: a wave per (batch, query head) combines the chunks,
+//   1. partials (decode_stream): a workgroup per (batch, kv head, key range
+//      of a few thousand keys) computes, for the G query heads of the kv
+//      head's GQA group at once, the range's max m_c, sum l_c and
+//      unnormalised output o_c.  It streams the range through a ring of five
+//      32-key K/V stages in LDS, filled by direct-to-LDS loads four stages
+//      ahead, so the cache is read without pauses; each of its two waves
+//      keeps its own online softmax over half of every stage's keys, and the
+//      waves merge once at the end;
+//   2. merge: a wave per (batch, query head) combines the ranges,
 //      m = max m_c, l = sum l_c e^(m_c - m), out = sum o_c e^(m_c - m) / l,
 //      lse = m + log l (natural log).
 // HBM-bound: every K and V row of the cache is read once per kv head and
 // serves the whole GQA group.
-//
-// Two partial kernels:
-//   * decode_stream (G * D <= 1024: groups of up to 8 heads at D = 128, 16
-//     at D = 64): a workgroup per (batch,
-//     kv head, key range of a few thousand keys) streams the range through a
-//     ring of five 32-key K/V stages in LDS, filled by direct-to-LDS loads
-//     four stages ahead, so the cache is read without pauses.  Each of its
-//     two waves keeps its own online softmax (running max, sum and output per
-//     head) over half of every stage's keys; the waves merge once at the end.
-//   * decode_partial (larger groups): a workgroup per 512-key chunk with the
-//     chunk's K and V rows in registers (the group's Q and outputs do not fit
-//     beside the streaming kernel's state).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -34,193 +27,12 @@
 namespace splash {
 namespace {
 
-constexpr int kChunk = 512;      // keys per partial workgroup (decode_partial)
-// decode_stream keeps G x D/L outputs and G x D/2L Q words per lane (L = 4 or
-// 8 lanes per key): it serves G * D <= 1024 (groups of up to 8 heads at
-// D = 128, 16 at D = 64).
-constexpr int kStreamMaxGD = 1024;
-constexpr int kDThreads = 512;   // 8 waves; 512-key chunks measured 17 % faster than 256-key ones
-static_assert(kChunk == kDThreads, "the softmax phase gives each thread one key");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ void unpack8(const u32x4 w, float (&x)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
-// Partials.  Threads: kPerRow = D / 8 lanes per key row (8 elements each), so
-// a wave covers kRowsPerWave = 64 / kPerRow keys per pass.
-template <int D, int G, bool CAP>
-__global__ __launch_bounds__(kDThreads) void decode_partial(const DecodeParams p) {
-  constexpr int kPerRow = D / 8;
-  constexpr int kRowsPerWave = 64 / kPerRow;
-  constexpr int kWaves = kDThreads / 64;
-  __shared__ float s_lds[G][kChunk];        // scores (base-2 units), then exponentials
-  __shared__ float red[kWaves][G];
-  __shared__ float o_lds[kWaves][G][D];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int sub = lane / kPerRow;           // key row within the wave's pass
-  const int part = lane % kPerRow;          // 8-element slice of the row
-  const int unit = blockIdx.x;              // (b, hkv)
-  const int chunk = blockIdx.y;
-  const int b = unit / p.Hkv, hkv = unit % p.Hkv;
-  const int64_t key_begin = static_cast<int64_t>(chunk) * kChunk;
-  const int n_keys = static_cast<int>(min(static_cast<int64_t>(kChunk), p.Skv - key_begin));
-
-  // this lane's slice of the G query rows
-  float qv[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int hq = hkv * G + g;
-    const __bf16 *qr = static_cast<const __bf16 *>(p.q) + (static_cast<int64_t>(b) * p.Hq + hq) * D + 8 * part;
-    unpack8(*reinterpret_cast<const u32x4 *>(qr), qv[g]);
-  }
-  const int64_t kv_head = (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv;
-  const __bf16 *kbase = static_cast<const __bf16 *>(p.k) + (kv_head + key_begin) * D + 8 * part;
-  const __bf16 *vbase = static_cast<const __bf16 *>(p.v) + (kv_head + key_begin) * D + 8 * part;
-
-  // All of this lane's K rows are requested up front; its V rows once the
-  // scores are formed, so their latency overlaps the softmax phase (loading
-  // both at once costs occupancy and measured slower).
-  constexpr int kIters = kChunk / (kWaves * kRowsPerWave);
-  u32x4 kr[kIters], vr[kIters];
-  auto load_v = [&]() {
-#pragma unroll
-    for (int it = 0; it < kIters; ++it) {
-      const int key = wave * kRowsPerWave + it * kWaves * kRowsPerWave + sub;
-      vr[it] = key < n_keys ? *reinterpret_cast<const u32x4 *>(vbase + static_cast<int64_t>(key) * D) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int key = wave * kRowsPerWave + it * kWaves * kRowsPerWave + sub;
-    kr[it] = key < n_keys ? *reinterpret_cast<const u32x4 *>(kbase + static_cast<int64_t>(key) * D) : u32x4{0u, 0u, 0u, 0u};
-  }
-
-  // 1. scores
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int key = wave * kRowsPerWave + it * kWaves * kRowsPerWave + sub;
-    float kx[8];
-    unpack8(kr[it], kx);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc += qv[g][i] * kx[i];
-#pragma unroll
-      for (int m = kPerRow / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-      if (part == 0) {
-        float s2;
-        if constexpr (CAP) {
-          const float xs = acc * p.c2;
-          const float e = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(xs));
-          const float th = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
-          s2 = copysignf(th, xs) * p.cap_out;
-        } else {
-          s2 = acc * p.c2;
-        }
-        s_lds[g][key] = key < n_keys ? s2 : -INFINITY;
-      }
-    }
-  }
-  load_v();
-  __syncthreads();
-
-  // 2. per head: chunk max, exponentials, sum (thread t owns key t)
-  float mx[G], sm[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float x = s_lds[g][tid];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-    if (lane == 0) red[wave][g] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = red[0][g];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w][g]);
-    mx[g] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float e = mx[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_lds[g][tid] - mx[g]);
-    s_lds[g][tid] = e;
-    float x = e;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-    if (lane == 0) red[wave][g] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) l += red[w][g];
-    sm[g] = l;
-  }
-
-  // 3. unnormalised output: this lane's 8 columns, summed over its keys
-  float acc[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
-#pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int key = wave * kRowsPerWave + it * kWaves * kRowsPerWave + sub;
-    float vx[8];
-    unpack8(vr[it], vx);   // zeros past the chunk's end, whose exponentials are 0 too
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float pe = s_lds[g][key];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[g][i] += pe * vx[i];
-    }
-  }
-  // sum over the wave's key rows (lanes with the same slice), then over waves
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float x = acc[g][i];
-#pragma unroll
-      for (int m = kPerRow; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
-      acc[g][i] = x;
-    }
-  if (sub == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o_lds[wave][g][8 * part + i] = acc[g][i];
-  }
-  __syncthreads();
-  const int64_t slot = static_cast<int64_t>(unit) * p.n_chunks + chunk;
-  for (int idx = tid; idx < G * D; idx += kDThreads) {
-    const int g = idx / D, d = idx % D;
-    float x = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) x += o_lds[w][g][d];
-    p.ws_o[(slot * G + g) * D + d] = x;
-  }
-  if (tid < G) {
-    p.ws_m[slot * G + tid] = mx[tid];
-    p.ws_l[slot * G + tid] = sm[tid];
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Streaming partial kernel.
@@ -305,13 +117,16 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
 }
 
 // Sum over the L lanes that hold the parts of one key's row (L = 4: a quad;
-// L = 8: two quads) with DPP lane moves: VALU only, no LDS round trip.
+// 8: two quads; 16: a DPP row) with DPP lane moves: VALU only, no LDS round
+// trip.
 template <int L>
 __device__ __forceinline__ float parts_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));   // lanes ^ 1
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false));   // lanes ^ 2
-  if constexpr (L == 8)   // row_half_mirror: lane i <-> 7 - i of each 8, the other quad
+  if constexpr (L >= 8)   // row_half_mirror: lane i <-> 7 - i of each 8, the other quad
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));
+  if constexpr (L == 16)  // row_mirror: lane i <-> 15 - i of each 16, the other half-row
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false));
   return x;
 }
 
@@ -329,10 +144,10 @@ __device__ __forceinline__ void stream_wait(int n) {
 template <int D, int G, bool CAP>
 __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams p) {
   using SG = SStage<D>;
-  // L lanes share a key row: 4 while G * D <= 512, else 8 (half the Q words
-  // and outputs per lane); a wave covers 64 / L keys per pass and 16 keys
-  // of every stage in 16 L / 64 passes.
-  constexpr int L = G * D <= 512 ? 4 : 8;
+  // L lanes share a key row: 4 while G * D <= 512, 8 up to 1024, else 16,
+  // so a lane holds at most 128 outputs and 64 Q words; a wave covers 64 / L
+  // keys per pass and 16 keys of every stage in 16 L / 64 passes.
+  constexpr int L = G * D <= 512 ? 4 : G * D <= 1024 ? 8 : 16;
   constexpr int kKw = 64 / L;                  // keys per pass of a wave
   constexpr int kPasses = kSKeys / kSWaves / kKw;
   constexpr int kPart = D / L;                 // elements of a row per lane
@@ -553,13 +368,8 @@ __global__ __launch_bounds__(64) void decode_merge(const DecodeParams p) {
 template <int D, int G>
 hipError_t go(const DecodeParams &p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(p.B * p.Hkv), static_cast<unsigned>(p.n_chunks));
-  if constexpr (G * D <= kStreamMaxGD) {
-    if (p.cap) hipLaunchKernelGGL((decode_stream<D, G, true>), grid, dim3(kSThreads), 0, s, p);
-    else hipLaunchKernelGGL((decode_stream<D, G, false>), grid, dim3(kSThreads), 0, s, p);
-  } else {
-    if (p.cap) hipLaunchKernelGGL((decode_partial<D, G, true>), grid, dim3(kDThreads), 0, s, p);
-    else hipLaunchKernelGGL((decode_partial<D, G, false>), grid, dim3(kDThreads), 0, s, p);
-  }
+  if (p.cap) hipLaunchKernelGGL((decode_stream<D, G, true>), grid, dim3(kSThreads), 0, s, p);
+  else hipLaunchKernelGGL((decode_stream<D, G, false>), grid, dim3(kSThreads), 0, s, p);
   hipLaunchKernelGGL((decode_merge<D, G>), dim3(static_cast<unsigned>(p.B * p.Hq)), dim3(64), 0, s, p);
   return hipGetLastError();
 }
@@ -577,12 +387,13 @@ hipError_t go_g(const DecodeParams &p, hipStream_t s) {
 
 }  // namespace
 
-// Keys per partial workgroup.  Streaming kernel: whole 32-key stages, about
-// 512 workgroups over the launch (two per CU) when the cache is long enough,
-// and at least four stages per workgroup.  (1024 shorter ranges measured 9%
-// slower: each range ends with a merge of its waves.)  Larger groups: the 512-key chunks.
+// Keys per partial workgroup: whole 32-key stages, about 512 workgroups over
+// the launch (two per CU) when the cache is long enough, and at least four
+// stages per workgroup.  (1024 shorter ranges measured 9% slower: each range
+// ends with a merge of its waves.)  The same for every group size and D.
 int64_t decode_split_keys(int64_t units, int64_t group, int64_t D, int64_t Skv) {
-  if (group * D > kStreamMaxGD) return kChunk;
+  (void)group;
+  (void)D;
   if (Skv <= 0 || units <= 0) return kSKeys;
   const int64_t stages = (Skv + kSKeys - 1) / kSKeys;
   int64_t splits = (512 + units - 1) / units;

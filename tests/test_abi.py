@@ -179,7 +179,7 @@ def test_decode_workspace_size():
     # the bench's decode shape: 64 units x 1024 stages -> 8 ranges of 4096 keys (512 workgroups)
     assert lib.splash_decode_workspace_size(8, 32, 8, 32768, 128, ctypes.byref(n)) == splash.OK
     assert n.value == 8 * 8 * 8 * 4 * (128 + 2) * 4
-    # groups of 16 keep 512-key chunks: 2 chunks for 1000 keys
+    # groups of 16 at D = 128 (16 lanes per key): 1 unit x 32 stages -> 8 ranges of 4 stages
     assert lib.splash_decode_workspace_size(1, 16, 1, 1000, 128, ctypes.byref(n)) == splash.OK
-    assert n.value == 1 * 1 * 2 * 16 * (128 + 2) * 4
+    assert n.value == 1 * 1 * 8 * 16 * (128 + 2) * 4
     assert lib.splash_decode_workspace_size(1, 3, 2, 10, 64, ctypes.byref(n)) == splash.EINVAL

@@ -34,6 +34,8 @@ CASES = [
     # groups with G * D > 512 stream with 8 lanes per key (two passes per stage)
     ("gqa8_long_ragged", 140, 2, 16, 2, 20001, 128, None),
     ("gqa16_d64_cap", 141, 2, 32, 2, 5000, 64, 30.0),
+    # groups of 16 at D = 128: 16 lanes per key, four passes per stage
+    ("gqa16_long_cap", 142, 1, 32, 2, 9000, 128, 30.0),
 ]
 
 
