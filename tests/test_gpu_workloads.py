@@ -81,3 +81,70 @@ def test_device_mask_info_bit_exact(name):
             assert d is None, nm
             continue
         assert d.dtype == r.dtype and d.shape == r.shape and d.tobytes() == r.tobytes(), nm
+
+
+def test_decode_full_size_sampled_heads():
+    """decode_gqa_32k (B = 8, Hq = 32, Hkv = 8, 32,768 cached keys, D = 128), called as the
+    decode benchmark calls it: every output finite, and a seeded sample of (b, query head)
+    rows, plus both corners, against the fp64 oracle with every key allowed."""
+    from block_sparse_attention_make_amd import splash_decode
+    w = synthetic.DECODE_WORKLOADS["decode_gqa_32k"]
+    q, k, v = synthetic.make_qkv(w.seed, w.B, w.Hq, w.Hkv, 1, w.Skv, w.D, w.Dv)
+    dev = torch.device("cuda:0")
+    out, lse = splash_decode(q.to(dev), k.to(dev), v.to(dev))
+    torch.cuda.synchronize()
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+    rng = np.random.default_rng(2000 + w.seed)
+    picks = [(int(rng.integers(w.B)), int(rng.integers(w.Hq)), 0) for _ in range(40)]
+    picks += [(0, 0, 0), (w.B - 1, w.Hq - 1, 0)]
+    allowed = np.ones((1, w.Skv), dtype=bool)
+    o_ref, l_ref = oatt.attention_sampled(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                          lambda h, rows: allowed, picks)
+    err_o = float(np.abs(np.stack([o[b, h, i] for b, h, i in picks]) - o_ref).max())
+    err_l = float(np.abs(np.array([l[b, h] for b, h, _ in picks]) - l_ref).max())
+    print(f"{w.name}: {len(picks)} sampled heads max|dO|={err_o:.3e} max|dlse|={err_l:.3e}", flush=True)
+    assert err_o <= TOL[torch.bfloat16] and err_l <= TOL[torch.bfloat16]
+
+
+def test_bwd_full_size_sampled():
+    """causal_mha_8k backward (B = 1, 16 heads, S = 8192, D = 128), with the output gradient
+    the backward benchmark draws (torch generator seed 11): every gradient finite; dq, dk and
+    dv of two whole heads, and dq of sampled rows of the other heads, against the fp64 oracle.
+    Tolerance: 2e-2 of the larger of 1 and the reference's max-abs, as for the small cases."""
+    from block_sparse_attention_make_amd import make_mask_info, splash_bwd, splash_fwd
+    w = synthetic.WORKLOADS["causal_mha_8k"]
+    q, k, v, _ = synthetic.make_inputs(w)
+    dev = torch.device("cuda:0")
+    mi = make_mask_info("causal", w.Sq, w.Skv)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out, lse = splash_fwd(qd, kd, vd, mi)
+    g = torch.Generator().manual_seed(11)
+    do = torch.randn(out.shape, generator=g).to(q.dtype)
+    dq, dk, dv = splash_bwd(qd, kd, vd, out, lse, do.to(dev), mi)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy() for t in (dq, dk, dv)]
+    for name, t in zip(("dq", "dk", "dv"), got):
+        assert np.isfinite(t).all(), name
+    q64, k64, v64, do64 = (t.double().numpy() for t in (q, k, v, do))
+    fn = mask_rows_fn("causal", w.Skv)
+
+    def check(name, a, ref):
+        scale = max(1.0, float(np.abs(ref).max()))
+        err = float(np.abs(a - ref).max())
+        print(f"{w.name} {name}: max|d|={err:.3e} ref max={scale:.3e}", flush=True)
+        assert err <= 2e-2 * scale, (name, err, scale)
+
+    rng = np.random.default_rng(3000 + w.seed)
+    heads = [0, int(rng.integers(1, w.Hq))]
+    for h in heads:
+        sl = slice(h, h + 1)   # MHA: query head h reads kv head h
+        rq, rk, rv = oatt.attention_bwd(q64[:, sl], k64[:, sl], v64[:, sl], do64[:, sl], fn)
+        check(f"head {h} dq", got[0][:, sl], rq)
+        check(f"head {h} dk", got[1][:, sl], rk)
+        check(f"head {h} dv", got[2][:, sl], rv)
+    rows = [(int(rng.integers(w.Hq)), int(rng.integers(w.Sq))) for _ in range(24)] + [(w.Hq - 1, w.Sq - 1)]
+    for h, i in rows:
+        rq, _, _ = oatt.attention_bwd_rows(q64[0, h, [i]], k64[0, h], v64[0, h], do64[0, h, [i]],
+                                           fn(h, np.array([i])))
+        check(f"dq row ({h}, {i})", got[0][0, h, [i]], rq)
