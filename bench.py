@@ -201,7 +201,7 @@ def bench_decode(args):
         "kernel_ms_median": round(float(np.median(kern)), 5),
         "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (kav * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(kv_bytes / (kav * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                     "traffic": None, "kernel": "decode_stream + decode_merge", "bytes_per_launch": kv_bytes,
+                     "traffic": None, "kernel": "decode_mfma + decode_merge", "bytes_per_launch": kv_bytes,
                      "kernel_ms_avg": round(kav, 5)},
         "cpu_baseline": None,
     }

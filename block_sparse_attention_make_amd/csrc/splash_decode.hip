@@ -4,7 +4,7 @@
 // TPU (EasyDeL BlockSparseAttn.forward_native); this is the MI355X-native
 // path for that case.  It is the forward's masked softmax attention with
 // every key allowed, split along the keys (flash decoding):
-//   1. partials (decode_stream): a workgroup per (batch, kv head, key range
+//   1. partials (decode_mfma): a workgroup per (batch, kv head, key range
 //      of a few thousand keys) computes, for the G query heads of the kv
 //      head's GQA group at once, the range's max m_c, sum l_c and
 //      unnormalised output o_c.  It streams the range through a ring of five
@@ -33,6 +33,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Streaming partial kernel.
@@ -40,7 +43,7 @@ constexpr int kSKeys = 32;               // keys per stage
 constexpr int kSStages = 5;              // ring of stages; loads run four ahead
 constexpr int kSWaves = 2;               // 16 keys of every stage per wave
 constexpr int kSThreads = 64 * kSWaves;
-constexpr float kBaseSlack = 32.f;       // see the exponent base in decode_stream
+constexpr float kBaseSlack = 32.f;       // headroom of the exponent base (base 2)
 
 // Buffer resource over `bytes` bytes at `base`; reads past the end return 0.
 __device__ __forceinline__ i32x4 stream_rsrc(const void *base, int64_t bytes) {
@@ -54,9 +57,9 @@ __device__ __forceinline__ i32x4 stream_rsrc(const void *base, int64_t bytes) {
 }
 
 // Stage geometry: 32 key rows of D bf16, rows of 16-byte chunks, chunk c of
-// row r stored at chunk c ^ swz(r).  Lane (key kw, part pt) of a wave reads
-// the chunks of its quarter of a row; with the swizzle the 16 lanes of each
-// quarter-wave of a 16-byte LDS read hit 16 different bank groups.
+// row r stored at chunk c ^ swz(r), so the 16 rows one K operand read spans
+// (one chunk each) and the rows of a transposing V read spread over
+// several bank groups instead of one.
 template <int D>
 struct SStage {
   static constexpr int kRowBytes = 2 * D;
@@ -107,29 +110,6 @@ __device__ __forceinline__ void stream_stage(char *lds, i32x4 res, int64_t row0,
 #pragma clang diagnostic pop
 }
 
-// Two bf16 from one 32-bit word (element 0 in the low half).  Through a copy:
-// hipcc lowered __builtin_bit_cast of an ext-vector element as element 0 of
-// the vector whatever the index.
-__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
-  bf16x2 r;
-  __builtin_memcpy(&r, &w, sizeof(r));
-  return r;
-}
-
-// Sum over the L lanes that hold the parts of one key's row (L = 4: a quad;
-// 8: two quads; 16: a DPP row) with DPP lane moves: VALU only, no LDS round
-// trip.
-template <int L>
-__device__ __forceinline__ float parts_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xb1, 0xf, 0xf, false));   // lanes ^ 1
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4e, 0xf, 0xf, false));   // lanes ^ 2
-  if constexpr (L >= 8)   // row_half_mirror: lane i <-> 7 - i of each 8, the other quad
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));
-  if constexpr (L == 16)  // row_mirror: lane i <-> 15 - i of each 16, the other half-row
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false));
-  return x;
-}
-
 // Wait until at most n of this wave's vector-memory loads are in flight.
 template <int N>
 __device__ __forceinline__ void stream_wait(int n) {
@@ -141,36 +121,39 @@ __device__ __forceinline__ void stream_wait(int n) {
   }
 }
 
+// Partial kernel: a workgroup of two waves per (b, kv head, key range), for
+// every group size up to 16.  A wave takes 16 keys of every stage; the dot
+// products and the output accumulation run on 16x16 MFMAs.
+//  - Scores, transposed: S^T (16 keys x 16 heads) = K Q^T with D / 32
+//    16x16x32 bf16 products.  K rows come from LDS (one 16-byte read per
+//    product); Q^T stays in registers, its rows past G zero.  Lane l then
+//    holds head l % 16 and keys 4 (l / 16) + 0..3.
+//  - Output, transposed: O^T (D x 16 heads) += V^T P^T with D / 16 16x16x16
+//    products.  P^T is the lane's four weights rounded to bf16, already in
+//    the operand layout; V^T comes from the row-major V stage through the
+//    transposing LDS read ds_read_b64_tr_b16 (lane l gets column l % 16 of
+//    a 4 x 16 block of rows 4 (l / 16) + 0..3).
+// Every register of a lane belongs to one head, so a rescale is lane-local.
 template <int D, int G, bool CAP>
-__global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams p) {
+__global__ __launch_bounds__(kSThreads, 1) void decode_mfma(const DecodeParams p) {
   using SG = SStage<D>;
-  // L lanes share a key row: 4 while G * D <= 512, 8 up to 1024, else 16,
-  // so a lane holds at most 128 outputs and 64 Q words; a wave covers 64 / L
-  // keys per pass and 16 keys of every stage in 16 L / 64 passes.
-  constexpr int L = G * D <= 512 ? 4 : G * D <= 1024 ? 8 : 16;
-  constexpr int kKw = 64 / L;                  // keys per pass of a wave
-  constexpr int kPasses = kSKeys / kSWaves / kKw;
-  constexpr int kPart = D / L;                 // elements of a row per lane
-  constexpr int kPC = kPart / 8;               // 16-byte chunks per lane
-  static_assert(kPC >= 1 && kPasses >= 1, "lane split");
-  constexpr int kLoadsPerStage = 2 * SG::kSegsPerWave;   // K and V, per wave
-  // One arena: the stages during the loop; the waves' partial outputs and
-  // the merge scalars after it.  80 KiB at D = 128, so two workgroups share
-  // a CU's 160 KiB.
+  constexpr int kKC = D / 32;                  // QK products per stage and wave
+  constexpr int kDT = D / 16;                  // PV products (output tiles)
+  constexpr int kLoadsPerStage = 2 * SG::kSegsPerWave;
   constexpr int kStBytes = 2 * kSStages * SG::kBytes;
-  constexpr int kOutBytes = kSWaves * kKw * G * D * 4;   // partial outputs at the end
+  constexpr int kOutBytes = kSWaves * G * D * 4;
   constexpr int kMrgBytes = 2 * kSWaves * G * 4;
   constexpr int kArena = kStBytes > kOutBytes + kMrgBytes ? kStBytes : kOutBytes + kMrgBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kArena];
   char (*k_st)[SG::kBytes] = reinterpret_cast<char (*)[SG::kBytes]>(smem);
   char (*v_st)[SG::kBytes] = reinterpret_cast<char (*)[SG::kBytes]>(smem + kSStages * SG::kBytes);
-  // (written after the loop, when the stages are free)
   float (*mrg_m)[G] = reinterpret_cast<float (*)[G]>(smem + kOutBytes);
   float (*mrg_l)[G] = reinterpret_cast<float (*)[G]>(smem + kOutBytes + kSWaves * G * 4);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kw = lane / L, pt = lane % L;      // key of the pass, part of the row
+  const int h = lane & 15, grp = lane >> 4;    // head; group of four keys
+  const bool hv = h < G;
   const int unit = blockIdx.x;                 // (b, hkv)
   const int split = blockIdx.y;
   const int b = unit / p.Hkv, hkv = unit % p.Hkv;
@@ -181,7 +164,7 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
   const int64_t kv_head = (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv;
   const i32x4 k_res = stream_rsrc(static_cast<const __bf16 *>(p.k) + kv_head * D, p.Skv * SG::kRowBytes);
   const i32x4 v_res = stream_rsrc(static_cast<const __bf16 *>(p.v) + kv_head * D, p.Skv * SG::kRowBytes);
-  auto issue = [&](int st) {   // stage st of this range into ring slot st % kSStages
+  auto issue = [&](int st) {
     stream_stage<D>(k_st[st % kSStages], k_res, kb + static_cast<int64_t>(st) * kSKeys, wave, lane);
     stream_stage<D>(v_st[st % kSStages], v_res, kb + static_cast<int64_t>(st) * kSKeys, wave, lane);
   };
@@ -189,120 +172,113 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
   for (int st = 0; st < kSStages - 1; ++st)
     if (st < nst) issue(st);
 
-  // this lane's part of the G query rows, as bf16 pairs
-  uint32_t qp[G][kPart / 2];
+  // Q^T operand: head h, dims 32 kk + 8 grp + 0..7
+  bf16x8 qb[kKC];
+  {
+    const __bf16 *qr = static_cast<const __bf16 *>(p.q) + (static_cast<int64_t>(b) * p.Hq + hkv * G + (hv ? h : 0)) * D;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const __bf16 *qr = static_cast<const __bf16 *>(p.q) + (static_cast<int64_t>(b) * p.Hq + hkv * G + g) * D + kPart * pt;
+    for (int kk = 0; kk < kKC; ++kk) {
+      u32x4 w = *reinterpret_cast<const u32x4 *>(qr + 32 * kk + 8 * grp);
+      if (!hv) w = u32x4{0u, 0u, 0u, 0u};
+      __builtin_memcpy(&qb[kk], &w, sizeof(w));
+    }
+  }
+  // byte offsets in a stage: the K operand row 16 wave + h, chunk 4 kk + grp;
+  // the transposing V read of rows 16 wave + 4 grp + h / 4, columns
+  // 16 dt + 4 (h % 4) + 0..3
+  int koff[kKC], voff[kDT];
+  {
+    const int kr = 16 * wave + h;
 #pragma unroll
-    for (int c = 0; c < kPC; ++c) {
-      const u32x4 w = *reinterpret_cast<const u32x4 *>(qr + 8 * c);
+    for (int kk = 0; kk < kKC; ++kk) koff[kk] = kr * SG::kRowBytes + (((4 * kk + grp) ^ SG::swz(kr)) * 16);
+    const int vr = 16 * wave + 4 * grp + (h >> 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qp[g][4 * c + i] = w[i];
+    for (int dt = 0; dt < kDT; ++dt) {
+      const int col = 16 * dt + 4 * (h & 3);
+      voff[dt] = vr * SG::kRowBytes + (((col >> 3) ^ SG::swz(vr)) * 16) + (col & 7) * 2;
     }
   }
 
-  float m[G], l[G], o[G][kPart];   // per wave: running max (base 2, uniform), this lane's sums
+  float m = -INFINITY, lsum = 0.f;   // head h's base (base 2) and this lane's share of its sum
+  f32x4 o[kDT];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < kPart; ++e) o[g][e] = 0.f;
-  }
+  for (int dt = 0; dt < kDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int u = 0; u < nst; ++u) {
-    // stage u has landed in every wave; the slot stage u+3 refills was read
-    // in step u-1 by every wave
-    const int ahead = min(nst - 1 - u, kSStages - 2);   // stages issued after u
+    const int ahead = min(nst - 1 - u, kSStages - 2);
     stream_wait<(kSStages - 2) * kLoadsPerStage>(ahead * kLoadsPerStage);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (u + kSStages - 1 < nst) issue(u + kSStages - 1);
+    const char *ks = k_st[u % kSStages];
+    const char *vs = v_st[u % kSStages];
 
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int pass = 0; pass < kPasses; ++pass) {
-    const int row = kSKeys / kSWaves * wave + kKw * pass + kw;   // this lane's key row of the stage
-    const int sw = SG::swz(row);
-    const char *kst = k_st[u % kSStages] + row * SG::kRowBytes;
-    const char *vst = v_st[u % kSStages] + row * SG::kRowBytes;
-    u32x4 kc[kPC], vc[kPC];
-#pragma unroll
-    for (int c = 0; c < kPC; ++c) {
-      kc[c] = *reinterpret_cast<const u32x4 *>(kst + ((kPC * pt + c) ^ sw) * 16);
-      vc[c] = *reinterpret_cast<const u32x4 *>(vst + ((kPC * pt + c) ^ sw) * 16);
+    for (int kk = 0; kk < kKC; ++kk) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + koff[kk]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[kk], sacc, 0, 0, 0);
     }
-    const bool valid = kb + static_cast<int64_t>(u) * kSKeys + row < ke;
+    const int64_t key0 = kb + static_cast<int64_t>(u) * kSKeys + 16 * wave + 4 * grp;
+    float s2[4];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float acc0 = 0.f, acc1 = 0.f;   // two chains of dot products
-#pragma unroll
-      for (int c = 0; c < kPC; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          acc0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kc[c][i]), as_bf16x2(qp[g][4 * c + i]), acc0, false);
-          acc1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kc[c][i + 1]), as_bf16x2(qp[g][4 * c + i + 1]), acc1,
-                                                 false);
-        }
-      const float acc = parts_sum<L>(acc0 + acc1);
-      float s2;
+    for (int j = 0; j < 4; ++j) {
+      float x;
       if constexpr (CAP) {
-        const float xs = acc * p.c2;
+        const float xs = sacc[j] * p.c2;
         const float e = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(xs));
         const float th = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
-        s2 = copysignf(th, xs) * p.cap_out;
+        x = copysignf(th, xs) * p.cap_out;
       } else {
-        s2 = acc * p.c2;
+        x = sacc[j] * p.c2;
       }
-      s2 = valid ? s2 : -INFINITY;
-      // The wave's exponent base m[g] is set by its first step with a valid
-      // key and moves only when a score exceeds it by more than 32 (base-2
-      // units), so exponentials stay below 2^32 and a step normally needs no
-      // cross-lane reduction.  Both tests are wave-uniform (ballots).
-      if (__builtin_amdgcn_ballot_w64(s2 > m[g] + kBaseSlack) != 0) {
-        float mx = s2;
-#pragma unroll
-        for (int x = L; x < 64; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x, 64));
-        mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));
-        const float a = __builtin_amdgcn_exp2f(m[g] - mx);   // 0 while m is -inf
-        l[g] *= a;
-#pragma unroll
-        for (int e = 0; e < kPart; ++e) o[g][e] *= a;
-        m[g] = mx;
-      }
-      const float pe = m[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s2 - m[g]);
-      l[g] += pe;
-#pragma unroll
-      for (int c = 0; c < kPC; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[g][8 * c + 2 * i] += pe * __uint_as_float(vc[c][i] << 16);
-          o[g][8 * c + 2 * i + 1] += pe * __uint_as_float(vc[c][i] & 0xffff0000u);
-        }
+      s2[j] = hv && key0 + j < ke ? x : -INFINITY;
+      mx = fmaxf(mx, s2[j]);
     }
-    }   // pass
+    // Head h's exponent base is set by its first valid scores and moves,
+    // with a rescale, only when a score exceeds it by more than 32 (base-2
+    // units): weights stay below 2^32 and a step normally needs no
+    // cross-lane max.  The test is a wave-wide ballot; the four lanes of a
+    // head agree on the base.
+    if (__builtin_amdgcn_ballot_w64(mx > m + kBaseSlack) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+      lsum *= a;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) o[dt] *= a;
+      m = mn;
+    }
+    float pe[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pe[j] = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s2[j] - m);
+    lsum += (pe[0] + pe[1]) + (pe[2] + pe[3]);
+    const bf16x2 p01 = {static_cast<__bf16>(pe[0]), static_cast<__bf16>(pe[1])};
+    const bf16x2 p23 = {static_cast<__bf16>(pe[2]), static_cast<__bf16>(pe[3])};
+    const bf16x2 pp[2] = {p01, p23};
+    s16x4 pb;
+    __builtin_memcpy(&pb, pp, sizeof(pb));
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4 __attribute__((address_space(3))) *)(vs + voff[dt]));
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dt], 0, 0, 0);
+    }
   }
 
-  // wave totals through LDS (the stages are free now): lane (kw, pt) stores
-  // its partial outputs at [wave][kw][g][part pt], then each output sums
-  // the kKw lanes' partials of both waves.
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int x = L; x < 64; x <<= 1) l[g] += __shfl_xor(l[g], x, 64);
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stages free
-  static_assert(kSWaves * kKw * G * D * 4 <= kArena, "partial outputs fit the arena");
-  float *o_lds = reinterpret_cast<float *>(smem);   // [kSWaves][kKw][G][D]
+  float *o_lds = reinterpret_cast<float *>(smem);   // [kSWaves][G][D]
+  if (hv) {
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < kPart; e += 4)
-      *reinterpret_cast<float4 *>(&o_lds[((wave * kKw + kw) * G + g) * D + kPart * pt + e]) =
-          make_float4(o[g][e], o[g][e + 1], o[g][e + 2], o[g][e + 3]);
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      mrg_m[wave][g] = m[g];
-      mrg_l[wave][g] = l[g];
+    for (int dt = 0; dt < kDT; ++dt)
+      *reinterpret_cast<float4 *>(&o_lds[(wave * G + h) * D + 16 * dt + 4 * grp]) =
+          make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (grp == 0) {
+      mrg_m[wave][h] = m;
+      mrg_l[wave][h] = lsum;
     }
   }
   __syncthreads();
@@ -317,10 +293,7 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_stream(const DecodeParams
 #pragma unroll
       for (int w = 0; w < kSWaves; ++w) {
         const float a = mrg_m[w][g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrg_m[w][g] - mm);
-        float ow = 0.f;
-#pragma unroll
-        for (int j = 0; j < kKw; ++j) ow += o_lds[((w * kKw + j) * G + g) * D + d];
-        x += a * ow;
+        x += a * o_lds[(w * G + g) * D + d];
         lt += a * mrg_l[w][g];
       }
     }
@@ -368,8 +341,8 @@ __global__ __launch_bounds__(64) void decode_merge(const DecodeParams p) {
 template <int D, int G>
 hipError_t go(const DecodeParams &p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(p.B * p.Hkv), static_cast<unsigned>(p.n_chunks));
-  if (p.cap) hipLaunchKernelGGL((decode_stream<D, G, true>), grid, dim3(kSThreads), 0, s, p);
-  else hipLaunchKernelGGL((decode_stream<D, G, false>), grid, dim3(kSThreads), 0, s, p);
+  if (p.cap) hipLaunchKernelGGL((decode_mfma<D, G, true>), grid, dim3(kSThreads), 0, s, p);
+  else hipLaunchKernelGGL((decode_mfma<D, G, false>), grid, dim3(kSThreads), 0, s, p);
   hipLaunchKernelGGL((decode_merge<D, G>), dim3(static_cast<unsigned>(p.B * p.Hq)), dim3(64), 0, s, p);
   return hipGetLastError();
 }
