@@ -36,6 +36,8 @@ CASES = [
     ("gqa16_d64_cap", 141, 2, 32, 2, 5000, 64, 30.0),
     # groups of 16 at D = 128: 16 lanes per key, four passes per stage
     ("gqa16_long_cap", 142, 1, 32, 2, 9000, 128, 30.0),
+    # 33 key ranges of 128 keys for one (b, kv head): the last range holds one key
+    ("last_range_one_key", 143, 1, 4, 1, 4097, 128, None),
 ]
 
 
@@ -50,3 +52,29 @@ def test_decode_parity(case):
     o_ref, l_ref = oatt.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),
                                   lambda h, rows: allowed, soft_cap=cap)
     compare(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref[..., 0], TOL[torch.bfloat16], name)
+
+
+@pytest.mark.parametrize("G,D,cap", [(4, 128, None), (16, 64, None), (8, 128, 30.0)])
+def test_decode_scores_growing_and_shrinking_along_the_cache(G, D, cap):
+    """k_j carries b (j / Skv) along one direction and the query heads +-a along it, so
+    half of the heads' logits grow along the cache (to about 85, about 122 in base-2
+    units) and half shrink: the exponent base of a growing head has to move several
+    times by more than its 32-unit headroom, each time rescaling the partial sums."""
+    B, Hkv, Skv = 1, 2, 6001
+    Hq = G * Hkv
+    q, k, v = synthetic.make_qkv(150 + G, B, Hq, Hkv, 1, Skv, D, D)
+    t = torch.arange(Skv, dtype=torch.float32) / Skv
+    q = 0.05 * q.float()
+    k = 0.05 * k.float()
+    sign = torch.tensor([1.0 if h % 2 == 0 else -1.0 for h in range(Hq)])
+    q[:, :, 0, 0] += 31.0 * sign
+    k[..., 0] += 31.0 * t
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    dev = torch.device("cuda:0")
+    out, lse = splash_decode(q.to(dev), k.to(dev), v.to(dev), logits_soft_cap=cap)
+    torch.cuda.synchronize()
+    allowed = np.ones((1, Skv), dtype=bool)
+    o_ref, l_ref = oatt.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                  lambda h, rows: allowed, soft_cap=cap)
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref[..., 0], TOL[torch.bfloat16],
+            f"growing_G{G}_D{D}")
