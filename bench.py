@@ -101,6 +101,81 @@ def mfma_probe(torch):
     return {"tflops": round(flops / (a.elapsed_time(b) * 1e-3) / 1e12, 1), "cus": blocks}
 
 
+def read_probe(torch, nbytes):
+    """HBM read GB/s the GPU sustains on a plain grid-stride read of one
+    nbytes device buffer (as many bytes as a memory-bound kernel streams per
+    launch), 32 workgroups per CU, 1 s warm, median of 10 timed launches;
+    None if the probe library is absent."""
+    import ctypes
+    import numpy as np
+    path = os.path.join(ROOT, "block_sparse_attention_make_amd", "lib", "libsplash_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.splash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    blocks = 32 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda:0")
+
+    def one():
+        if lib.splash_probe_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(),
+                                 ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("read probe launch failed")
+
+    t0 = time.time()
+    while time.time() - t0 < 1.0:
+        one()
+        torch.cuda.synchronize()
+    ts = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        one()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return {"gbps": round(nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1), "bytes": nbytes}
+
+
+def cpu_baseline_decode(w, q, k, v, budget_s=12.0):
+    """The fp64 oracle, as it stands, on (b, query head) rows of the decode
+    workload in order, until about budget_s seconds of CPU work; its rate in
+    the GPU's unit: the workload's K/V bytes (bf16, each kv head once) times
+    the fraction of its query rows done, per second."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as oatt
+
+    group = w.Hq // w.Hkv
+    allowed = np.ones((1, w.Skv), dtype=bool)
+    row_bytes = w.Skv * (w.D + w.Dv) * 2
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        kn = k[b].double().numpy()
+        vn = v[b].double().numpy()
+        for h in range(w.Hq):
+            oatt.attention_rows(q[b, h].double().numpy(), kn[h // group], vn[h // group], allowed)
+            done += 1
+            if time.perf_counter() - t0 > budget_s and done >= 2:
+                break
+        if time.perf_counter() - t0 > budget_s and done >= 2:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": done * row_bytes / group / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle on {done} of {w.B * w.Hq} (b, query head) rows in {dt:.1f} s; bytes counted "
+                   f"as the GPU's: the workload's bf16 K/V bytes times the fraction of query rows done"),
+    }
+
+
 def flops_per_block(w):
     return 2 * w.block * w.block * (w.D + w.Dv)
 
@@ -205,6 +280,11 @@ def bench_decode(args):
                      "kernel_ms_avg": round(kav, 5)},
         "cpu_baseline": None,
     }
+    probe = read_probe(torch, kv_bytes)
+    if probe is not None:
+        res["hbm_read_probe"] = {**probe, "frac_of_probe": round(res["roofline"]["achieved"] / probe["gbps"], 4)}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(w, q, k, v)
     print(json.dumps(res), flush=True)
 
 

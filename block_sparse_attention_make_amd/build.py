@@ -1,6 +1,6 @@
 """Build libsplash.so (HIP kernels for gfx950 + host mask compiler + C ABI)
-and libsplash_probe.so (an MFMA throughput probe the benchmark reports beside
-the nominal peak; not part of the attention path).
+and libsplash_probe.so (MFMA-throughput and HBM-read probes the benchmark reports
+beside the nominal peaks; not part of the attention path).
 
 Run `python -m block_sparse_attention_make_amd.build` (or call build()).  The
 library lands in block_sparse_attention_make_amd/lib/, next to the binding

@@ -1,4 +1,4 @@
-// Measurement helper, not part of the attention path: the bf16 MFMA
+// Measurement helpers, not part of the attention path.  First, the bf16 MFMA
 // throughput this GPU sustains, to put the kernels' MFMA rates against the
 // chip's own ceiling (clock under load included) beside the nominal peak.
 // Every wave keeps four independent 32x32x16 bf16 accumulator chains busy
@@ -36,5 +36,37 @@ extern "C" __attribute__((visibility("default"))) int splash_probe_mfma(int bloc
                                                                        void *stream) {
   if (blocks <= 0 || iters <= 0 || !sink) return 1;
   hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+// The HBM read rate this GPU sustains, for the memory-bound kernels: a
+// grid-stride read of n 16-byte words with four independent non-temporal
+// loads in flight per lane, XOR-folded into sink[blocks * 256] so the loads
+// are not dropped.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *__restrict__ src, int64_t n, unsigned *sink) {
+  const int64_t nt = static_cast<int64_t>(gridDim.x) * 256;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t me = i;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * nt < n; i += 4 * nt) {
+    const u32x4 x0 = __builtin_nontemporal_load(src + i);
+    const u32x4 x1 = __builtin_nontemporal_load(src + i + nt);
+    const u32x4 x2 = __builtin_nontemporal_load(src + i + 2 * nt);
+    const u32x4 x3 = __builtin_nontemporal_load(src + i + 3 * nt);
+    acc ^= (x0 ^ x1) ^ (x2 ^ x3);
+  }
+  for (; i < n; i += nt) acc ^= __builtin_nontemporal_load(src + i);
+  sink[me] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// Reads `bytes` (a multiple of 16) at the 16-byte aligned `src` with `blocks`
+// workgroups of 256 lanes into sink[blocks * 256].
+extern "C" __attribute__((visibility("default"))) int splash_probe_read(const void *src, int64_t bytes, int blocks,
+                                                                       unsigned *sink, void *stream) {
+  if (!src || !sink || blocks <= 0 || bytes <= 0 || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15)) return 1;
+  hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4 *>(src), bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
