@@ -49,16 +49,17 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_make_amd", "csrc", "splash_fwd.hip")
+DECODE_SRC = os.path.join(ROOT, "block_sparse_attention_make_amd", "csrc", "splash_decode.hip")
 
 
-def kernel_sha():
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_sha(src=KERNEL_SRC):
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, src=KERNEL_SRC):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current source of the kernel (src); else None."""
     path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -67,7 +68,7 @@ def measured_traffic(workload):
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("kernel_source_sha256") != kernel_sha():
+    if kv.get("kernel_source_sha256") != kernel_sha(src):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -276,7 +277,8 @@ def bench_decode(args):
         "kernel_ms_median": round(float(np.median(kern)), 5),
         "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (kav * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(kv_bytes / (kav * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                     "traffic": None, "kernel": "decode_mfma + decode_merge", "bytes_per_launch": kv_bytes,
+                     "traffic": measured_traffic(w.name, DECODE_SRC), "kernel": "decode_mfma + decode_merge",
+                     "bytes_per_launch": kv_bytes,
                      "kernel_ms_avg": round(kav, 5)},
         "cpu_baseline": None,
     }
