@@ -78,3 +78,20 @@ def test_decode_scores_growing_and_shrinking_along_the_cache(G, D, cap):
                                   lambda h, rows: allowed, soft_cap=cap)
     compare(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref[..., 0], TOL[torch.bfloat16],
             f"growing_G{G}_D{D}")
+
+
+def test_decode_reused_workspace_gives_identical_results():
+    """The workspace is scratch that every call overwrites: one buffer used first for a
+    longer cache with a larger group, then for the case under test, gives bit-identical
+    out and lse to a call on a fresh NaN-filled buffer."""
+    dev = torch.device("cuda:0")
+    ws = torch.full((4 << 20,), float("nan"), dtype=torch.float32, device=dev)
+    qa, ka, va = (t.to(dev) for t in synthetic.make_qkv(160, 2, 32, 2, 1, 20000, 128, 128))
+    splash_decode(qa, ka, va, workspace=ws)
+    q, k, v = (t.to(dev) for t in synthetic.make_qkv(161, 1, 8, 2, 1, 3001, 128, 128))
+    o1, l1 = splash_decode(q, k, v, workspace=ws)
+    fresh = torch.full((4 << 20,), float("nan"), dtype=torch.float32, device=dev)
+    o2, l2 = splash_decode(q, k, v, workspace=fresh)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.isfinite(o1.float()).all() and torch.isfinite(l1).all()
