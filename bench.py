@@ -167,14 +167,48 @@ def cpu_baseline_decode(w, q, k, v, budget_s=12.0):
             break
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    model, usable = host_cpu()
     return {
         "value": done * row_bytes / group / dt / 1e9,
         "unit": "GB/s",
         "cores": int(threads),
+        "cpu_model": model,
+        "host_cores_usable": usable,
         "kind": "oracle",
         "sample": (f"fp64 oracle on {done} of {w.B * w.Hq} (b, query head) rows in {dt:.1f} s; bytes counted "
                    f"as the GPU's: the workload's bf16 K/V bytes times the fraction of query rows done"),
     }
+
+
+def host_cpu():
+    """Model name and usable core count of the host the oracle runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return model, usable
+
+
+def prewarm(step, torch, seconds):
+    """Run step() back to back for `seconds` of wall time, synchronising every
+    few launches: the GPU's clock ramps up over the first 0.1-1 s of load, so
+    a count of warm-up launches alone can leave the timed launches on a cold
+    clock.  Returns the seconds spent."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    return time.perf_counter() - t0
 
 
 def flops_per_block(w):
@@ -219,10 +253,13 @@ def cpu_baseline(w, q, k, v, dense, block_mask, budget_s=12.0):
             break
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    model, usable = host_cpu()
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": model,
+        "host_cores_usable": usable,
         "kind": "oracle",
         "sample": (f"fp64 oracle on {rows_done} of {w.B * w.Hq * nq} query blocks (128 rows each, "
                    f"batch 0, longest block rows first, round-robin over heads) in {dt:.1f} s; "
@@ -252,6 +289,7 @@ def bench_decode(args):
 
     def step():
         splash_decode(qd, kd, vd, out=out, lse=lse, workspace=ws, stream=stream)
+    prewarm_s = prewarm(step, torch, args.prewarm_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -274,6 +312,7 @@ def bench_decode(args):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "kv_len": w.Skv,
                    "head_dim": w.D, "pass": "decode", "parallelism": "single-gpu"},
+        "prewarm_s": round(prewarm_s, 2),
         "kernel_ms_median": round(float(np.median(kern)), 5),
         "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (kav * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(kv_bytes / (kav * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
@@ -296,6 +335,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # The GPU's clock settles only after ~100 ms of sustained load, so the default warm-up is long.
     ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--prewarm-s", type=float, default=2.0,
+                    help="seconds of back-to-back steps before the counted warm-up, so the clock has settled")
     ap.add_argument("--workload", default="causal_mha_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -406,6 +447,7 @@ def main():
             splash_fwd(qd, kd, vd, mi, logits_soft_cap=w.soft_cap, out=out, lse=lse, stream=stream,
                        softmax_aux=aux)
 
+    prewarm_s = prewarm(step, torch, args.prewarm_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -482,6 +524,7 @@ def main():
                    "soft_cap": w.soft_cap, "parallelism": "single-gpu",
                    "sinks_per_kv_head": args.sinks, "kv_shards": P,
                    "mask_block": [args.block_q, args.block_kv], "pass": "backward" if args.backward else "forward"},
+        "prewarm_s": round(prewarm_s, 2),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "dense_equiv_tflops": round(flops_dense / (ms_per_step * 1e-3) / 1e12, 2),
         "blocks_skipped": blocks_total - blocks_computed,

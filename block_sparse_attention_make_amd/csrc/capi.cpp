@@ -341,6 +341,9 @@ extern "C" SPLASH_API splash_status splash_mask_info_read_device(const splash_ma
 
 namespace {
 
+// Largest byte count one buffer resource (32-bit size field) covers.
+constexpr int64_t kMaxHeadBytes = 0x7fffffffLL;
+
 // Checks shared by the forward and the backward entry points.
 splash_status validate_call(const splash_mask_info *mi, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
                             int64_t Skv, int64_t D, int64_t Dv, int32_t dtype, float softmax_scale) {
@@ -363,6 +366,18 @@ splash_status validate_call(const splash_mask_info *mi, int64_t B, int64_t Hq, i
   const int64_t n_wg = B * Hq * (Sq / 128);
   if (n_wg > 0x7fffffffLL || B * Hq > 0x7fffffffLL || B * Hkv * (Skv / 128) > 0x7fffffffLL)
     return fail(SPLASH_EUNSUPPORTED, "grid too large");
+  // The kernels address one head's q, k, v, out (and dout) through buffer
+  // resources whose size field and stage offsets are 32-bit: a head larger
+  // than 2^31 - 1 bytes would read zeros past that point instead of its data.
+  const int64_t esize = dtype == SPLASH_BF16 ? 2 : 4;
+  if (Skv * D * esize > kMaxHeadBytes || Skv * Dv * esize > kMaxHeadBytes || Sq * D * esize > kMaxHeadBytes ||
+      Sq * Dv * esize > kMaxHeadBytes)
+    return fail(SPLASH_EUNSUPPORTED, "one head of q, k, v or out exceeds 2^31 - 1 bytes");
+  // Dense masks: the partial blocks, packed to one bit per element, are read
+  // through one buffer resource as well.
+  const HostArray &pm = mi->arr[SPLASH_MI_PARTIAL_BLOCKS];
+  if (pm.present && pm.ndim == 3 && pm.shape[0] * pm.shape[1] * pm.shape[2] / 8 > kMaxHeadBytes)
+    return fail(SPLASH_EUNSUPPORTED, "the packed partial mask blocks exceed 2^31 - 1 bytes");
   return SPLASH_OK;
 }
 

@@ -13,27 +13,23 @@
 //     recomputed from q_sequence and the key position, dense masks read the
 //     partial block mask_next points at;
 //   * data_next names the key/value block to fetch at each position.
-// The softmax is the flash online softmax: a running max and running sum per
-// query row, the accumulator rescaled whenever the max moves, one division by
-// the final sum at the end, and the log-sum-exp kept as the per-row residual.
+// The softmax is the flash online softmax: a per-row running max and running
+// sum, one division by the final sum at the end, and the log-sum-exp kept as
+// the per-row residual.
 //
-// MI355X mapping.  Four 64-lane waves per workgroup, each owning 32 query
-// rows.  Scores are formed transposed, S^T = K Q^T, with the 32x32x16 bf16
-// MFMA (32x32x2 f32 for float inputs): Q stays in registers as the B operand
-// and K streams from LDS as the A operand.  In that output layout every lane
-// holds one query row (lane % 32) and 16 of its keys per 32-key tile, so a
-// row max or row sum is a per-lane reduction plus one v_permlane32_swap with
-// the partner lane (lane ^ 32).  The output is accumulated transposed too,
-// O^T = V^T P^T: P goes straight from the score registers into the B
-// operand, and V^T comes out of the row-major V tile with the gfx950
-// transposing LDS read ds_read_b64_tr_b16, so neither P nor V is shuffled.
-// K and V tiles (128 x D) are staged through LDS with XOR-swizzled 16-byte
-// chunks so that the staging writes, the K operand reads and the transposing
-// V reads are bank-conflict free.
+// Two kernels, one per input type:
+//   * splash_fwd_wide (bfloat16): two 64-lane waves per 128-row block, 64
+//     query rows per wave, K/V streamed through LDS by direct-to-LDS loads in
+//     32-key stages, software-pipelined QK / softmax / PV over 32x32x16 bf16
+//     MFMAs;
+//   * splash_fwd_f32 (float32): four waves of 32 rows over 128-key tiles with
+//     the 32x32x2 f32 MFMA.
+// Both form the scores transposed, S^T = K Q^T, so that a lane holds one
+// query row and row reductions stay inside a lane pair, and accumulate
+// O^T = V^T P^T with P taken straight from the score registers.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <type_traits>
 
 #include "splash_kernel.h"
 
@@ -109,37 +105,30 @@ __device__ __forceinline__ int load_index(const void *p, int bytes, int64_t i) {
   return static_cast<const int32_t *>(p)[i];
 }
 
-// Tile geometry and swizzles.  A tile is 128 rows of D elements; a row is
-// split into 16-byte chunks whose index is XORed with swz(row).
-template <typename T, int D>
+// Tile geometry and swizzles of the float32 kernel.  A tile is 128 rows of
+// D floats; a row is split into 16-byte chunks whose index is XORed with
+// swz(row).
+template <int D>
 struct Tile {
-  static constexpr int kRowBytes = D * static_cast<int>(sizeof(T));
+  static constexpr int kRowBytes = D * 4;
   static constexpr int kChunks = kRowBytes / 16;
   static constexpr int kBytes = kBK * kRowBytes;
-  // K tile: the A-operand read has 16 consecutive lanes on 16 consecutive
-  // rows at one chunk.
+  // K tile: the A-operand read has 32 lanes on 32 consecutive rows at one
+  // chunk.
   __device__ static int swz_k(int row) {
     if constexpr (kChunks >= 16) return row & 15;
     else return (row >> 1) & 7;
   }
-  // V tile: the transposing read has 32 lanes on 4 consecutive rows x 4
-  // chunks (bf16); the f32 read has 32 lanes on one row.
-  __device__ static int swz_v(int row) {
-    if constexpr (sizeof(T) == 2) {
-      if constexpr (kChunks >= 16) return (row & 3) << 2;
-      else return ((row >> 1) & 1) << 2;
-    } else {
-      return row & 15;
-    }
-  }
+  // V tile: the operand read has 32 lanes on one row.
+  __device__ static int swz_v(int row) { return row & 15; }
 };
 
 // Copy one 128 x D tile from global memory (rows contiguous, D elements each)
 // into a swizzled LDS tile.  Each lane moves 16-byte chunks; 16 lanes cover
 // one 256-byte span of a row, so the global reads are fully coalesced.
-template <typename T, int D, bool IS_V>
-__device__ __forceinline__ void stage_tile(char *lds, const T *g, int tid) {
-  using TL = Tile<T, D>;
+template <int D, bool IS_V>
+__device__ __forceinline__ void stage_tile(char *lds, const float *g, int tid) {
+  using TL = Tile<D>;
   constexpr int kPerThread = kBK * TL::kChunks / kThreads;
   u32x4 buf[kPerThread];
 #pragma unroll
@@ -158,11 +147,23 @@ __device__ __forceinline__ void stage_tile(char *lds, const T *g, int tid) {
   }
 }
 
-template <typename T, int D, bool CAP, bool DENSE>
-__global__ __launch_bounds__(kThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1)
-void splash_fwd_kernel(const FwdParams p) {
-  using TL = Tile<T, D>;
-  constexpr bool kBf16 = sizeof(T) == 2;
+// ===========================================================================
+// float32 kernel.  Four 64-lane waves per workgroup, each owning 32 query
+// rows.  Scores are formed transposed, S^T = K Q^T, with the 32x32x2 f32
+// MFMA: Q stays in registers as the B operand and K streams from LDS as the A
+// operand.  In that output layout every lane holds one query row (lane % 32)
+// and 16 of its keys per 32-key tile, so a row max or row sum is a per-lane
+// reduction plus one v_permlane32_swap with the partner lane (lane ^ 32).
+// The output is accumulated transposed too, O^T = V^T P^T, with P taken
+// straight from the score registers.  K and V tiles (128 x D) are staged
+// through VGPRs into LDS with XOR-swizzled 16-byte chunks, so the staging
+// writes and both operand reads are bank-conflict free.  The softmax keeps
+// the exact running max: the accumulator is rescaled whenever a row's max
+// moves.
+template <int D, bool CAP, bool DENSE>
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1)
+void splash_fwd_f32(const FwdParams p) {
+  using TL = Tile<D>;
   constexpr int kDT = D / 32;  // 32-wide output tiles along Dv
 
   __shared__ __attribute__((aligned(16))) char smem[2 * TL::kBytes];
@@ -198,26 +199,18 @@ void splash_fwd_kernel(const FwdParams p) {
   const int hm = p.hm == 1 ? 0 : hq;
 
   const int64_t q_row = static_cast<int64_t>(r) * kBQ + lrow;
-  const T *qg = static_cast<const T *>(p.q) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
-  const T *kg = static_cast<const T *>(p.k) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
-  const T *vg = static_cast<const T *>(p.v) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
+  const float *qg = static_cast<const float *>(p.q) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
+  const float *kg = static_cast<const float *>(p.k) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
+  const float *vg = static_cast<const float *>(p.v) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
 
   // ---- Q fragment (B operand of S^T = K Q^T), resident for the whole row ----
-  // bf16: k-step ks covers d = 16 ks + 8 half + 0..7.  f32: the lane's half
-  // owns d in [half D/2, (half+1) D/2) and k-step ks takes one of them.
-  constexpr int kQRegs = kBf16 ? D / 16 : D / 2;
-  using QFrag = typename std::conditional<kBf16, bf16x8, float>::type;
-  QFrag qf[kQRegs];
-  if constexpr (kBf16) {
+  // The lane's half owns d in [half D/2, (half+1) D/2) and k-step ks takes one of them.
+  constexpr int kQRegs = D / 2;
+  float qf[kQRegs];
 #pragma unroll
-    for (int ks = 0; ks < kQRegs; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8 *>(qg + 16 * ks + 8 * half);
-  } else {
-#pragma unroll
-    for (int i = 0; i < kQRegs / 4; ++i) {
-      const float4 x = *reinterpret_cast<const float4 *>(qg + half * (D / 2) + 4 * i);
-      qf[4 * i + 0] = x.x; qf[4 * i + 1] = x.y; qf[4 * i + 2] = x.z; qf[4 * i + 3] = x.w;
-    }
+  for (int i = 0; i < kQRegs / 4; ++i) {
+    const float4 x = *reinterpret_cast<const float4 *>(qg + half * (D / 2) + 4 * i);
+    qf[4 * i + 0] = x.x; qf[4 * i + 1] = x.y; qf[4 * i + 2] = x.z; qf[4 * i + 3] = x.w;
   }
 
   // ---- per-row mask interval for computable masks --------------------------
@@ -279,8 +272,8 @@ void splash_fwd_kernel(const FwdParams p) {
 
       // ---- stage K and V of block kvb ----
       __syncthreads();
-      stage_tile<T, D, false>(lds_k, kg + static_cast<int64_t>(kvb) * kBK * D, tid);
-      stage_tile<T, D, true>(lds_v, vg + static_cast<int64_t>(kvb) * kBK * D, tid);
+      stage_tile<D, false>(lds_k, kg + static_cast<int64_t>(kvb) * kBK * D, tid);
+      stage_tile<D, true>(lds_v, vg + static_cast<int64_t>(kvb) * kBK * D, tid);
       __syncthreads();
 
       // ---- S^T = K Q^T: four 32-key tiles ----
@@ -289,31 +282,19 @@ void splash_fwd_kernel(const FwdParams p) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) sc[t][v] = 0.f;
-      if constexpr (kBf16) {
 #pragma unroll
-        for (int ks = 0; ks < kQRegs; ++ks)
+      for (int i = 0; i < kQRegs / 4; ++i)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int row = 32 * t + (lane & 31);
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                lds_k + row * TL::kRowBytes + (((2 * ks + half) ^ TL::swz_k(row)) * 16));
-            sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sc[t], 0, 0, 0);
-          }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kQRegs / 4; ++i)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int row = 32 * t + (lane & 31);
-            const int c = (half * (D / 2) + 4 * i) / 4;
-            const float4 a = *reinterpret_cast<const float4 *>(
-                lds_k + row * TL::kRowBytes + ((c ^ TL::swz_k(row)) * 16));
-            sc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qf[4 * i + 0], sc[t], 0, 0, 0);
-            sc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qf[4 * i + 1], sc[t], 0, 0, 0);
-            sc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qf[4 * i + 2], sc[t], 0, 0, 0);
-            sc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qf[4 * i + 3], sc[t], 0, 0, 0);
-          }
-      }
+        for (int t = 0; t < 4; ++t) {
+          const int row = 32 * t + (lane & 31);
+          const int c = (half * (D / 2) + 4 * i) / 4;
+          const float4 a = *reinterpret_cast<const float4 *>(
+              lds_k + row * TL::kRowBytes + ((c ^ TL::swz_k(row)) * 16));
+          sc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qf[4 * i + 0], sc[t], 0, 0, 0);
+          sc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qf[4 * i + 1], sc[t], 0, 0, 0);
+          sc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qf[4 * i + 2], sc[t], 0, 0, 0);
+          sc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qf[4 * i + 3], sc[t], 0, 0, 0);
+        }
 
       // Lane holds, for query lrow, keys kvb*128 + 32t + 8(v/4) + 4*half + v%4.
       float c2e = c2;
@@ -384,56 +365,20 @@ void splash_fwd_kernel(const FwdParams p) {
       }
 
       // ---- O^T += V^T P^T ----
-      if constexpr (kBf16) {
-        bf16x8 pf[4][2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+        for (int v = 0; v < 16; ++v) {
+          const int key = 32 * t + 8 * (v / 4) + 4 * half + (v % 4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pf[t][h][e] = static_cast<__bf16>(sc[t][8 * h + e]);
-        // Lane supplies V[key][dv] for dv = 32 dt + lane%32 and the 8 keys
-        // 32t + 16h + 4 half + {0..3, 8..11}: two transposing reads, each lane
-        // addressing row 32t + 16h + 4 half + (lane%16)/4 (+8) at column
-        // 32 dt + 16 ((lane/16)%2) + 4 (lane%4).
-        const int trow = 4 * half + ((lane & 15) >> 2);
-        const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int dt = 0; dt < kDT; ++dt) {
-              const int row0 = 32 * t + 16 * h + trow;
-              const int col = 32 * dt + tcol;
-              const int c = col >> 3, within = (col & 7) * 2;
-              const char *a0 = lds_v + row0 * TL::kRowBytes + ((c ^ TL::swz_v(row0)) * 16) + within;
-              const char *a1 = lds_v + (row0 + 8) * TL::kRowBytes + ((c ^ TL::swz_v(row0 + 8)) * 16) + within;
-              const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (s16x4 __attribute__((address_space(3))) *)(a0));
-              const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (s16x4 __attribute__((address_space(3))) *)(a1));
-              const s16x4 both[2] = {lo4, hi4};
-              bf16x8 a;
-              __builtin_memcpy(&a, both, 16);
-              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[t][h], o[dt], 0, 0, 0);
-            }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = 32 * t + 8 * (v / 4) + 4 * half + (v % 4);
-#pragma unroll
-            for (int dt = 0; dt < kDT; ++dt) {
-              const int col = 32 * dt + (lane & 31);
-              const int c = col >> 2;
-              const float a = *reinterpret_cast<const float *>(
-                  lds_v + key * TL::kRowBytes + ((c ^ TL::swz_v(key)) * 16) + (col & 3) * 4);
-              o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sc[t][v], o[dt], 0, 0, 0);
-            }
+          for (int dt = 0; dt < kDT; ++dt) {
+            const int col = 32 * dt + (lane & 31);
+            const int c = col >> 2;
+            const float a = *reinterpret_cast<const float *>(
+                lds_v + key * TL::kRowBytes + ((c ^ TL::swz_v(key)) * 16) + (col & 3) * 4);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sc[t][v], o[dt], 0, 0, 0);
           }
-      }
+        }
     }
   }
 
@@ -444,23 +389,16 @@ void splash_fwd_kernel(const FwdParams p) {
     const float m_fin = m_run == -INFINITY ? 0.f : m_run;
     row_finish(l_tot, m_fin * (CAP ? 1.f : c2), sink_lse2(p, hq), inv, lse_row);
   }
-  T *og = static_cast<T *>(p.out) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
+  float *og = static_cast<float *>(p.out) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int col = 32 * dt + 8 * g + 4 * half;
-      if constexpr (kBf16) {
-        union { __bf16 h[4]; u32x2 u; } pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk.h[e] = static_cast<__bf16>(o[dt][4 * g + e] * inv);
-        *reinterpret_cast<u32x2 *>(og + col) = pk.u;
-      } else {
-        float4 x;
-        x.x = o[dt][4 * g + 0] * inv; x.y = o[dt][4 * g + 1] * inv;
-        x.z = o[dt][4 * g + 2] * inv; x.w = o[dt][4 * g + 3] * inv;
-        *reinterpret_cast<float4 *>(og + col) = x;
-      }
+      float4 x;
+      x.x = o[dt][4 * g + 0] * inv; x.y = o[dt][4 * g + 1] * inv;
+      x.z = o[dt][4 * g + 2] * inv; x.w = o[dt][4 * g + 3] * inv;
+      *reinterpret_cast<float4 *>(og + col) = x;
     }
   if (p.lse && half == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] = lse_row;
 }
@@ -1350,30 +1288,31 @@ hipError_t launch_wide(const FwdParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, int D, bool CAP, bool DENSE>
-hipError_t launch_one(const FwdParams &p, hipStream_t stream) {
+template <int D, bool CAP, bool DENSE>
+hipError_t launch_f32(const FwdParams &p, hipStream_t stream) {
   const int64_t blocks = p.B * p.Hq * p.nq;
-  hipLaunchKernelGGL((splash_fwd_kernel<T, D, CAP, DENSE>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((splash_fwd_f32<D, CAP, DENSE>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t launch_d(const FwdParams &p, hipStream_t stream) {
-  if constexpr (sizeof(T) == 2) {
-    if (p.cap) return p.dense ? launch_wide<D, true, true>(p, stream) : launch_wide<D, true, false>(p, stream);
-    return p.dense ? launch_wide<D, false, true>(p, stream) : launch_wide<D, false, false>(p, stream);
-  } else {
-    if (p.cap) return p.dense ? launch_one<T, D, true, true>(p, stream) : launch_one<T, D, true, false>(p, stream);
-    return p.dense ? launch_one<T, D, false, true>(p, stream) : launch_one<T, D, false, false>(p, stream);
-  }
+template <int D>
+hipError_t launch_bf16(const FwdParams &p, hipStream_t stream) {
+  if (p.cap) return p.dense ? launch_wide<D, true, true>(p, stream) : launch_wide<D, true, false>(p, stream);
+  return p.dense ? launch_wide<D, false, true>(p, stream) : launch_wide<D, false, false>(p, stream);
+}
+
+template <int D>
+hipError_t launch_float(const FwdParams &p, hipStream_t stream) {
+  if (p.cap) return p.dense ? launch_f32<D, true, true>(p, stream) : launch_f32<D, true, false>(p, stream);
+  return p.dense ? launch_f32<D, false, true>(p, stream) : launch_f32<D, false, false>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams &p, int dtype, hipStream_t stream) {
-  if (dtype == 0) return p.D == 64 ? launch_d<__bf16, 64>(p, stream) : launch_d<__bf16, 128>(p, stream);
-  return p.D == 64 ? launch_d<float, 64>(p, stream) : launch_d<float, 128>(p, stream);
+  if (dtype == 0) return p.D == 64 ? launch_bf16<64>(p, stream) : launch_bf16<128>(p, stream);
+  return p.D == 64 ? launch_float<64>(p, stream) : launch_float<128>(p, stream);
 }
 
 }  // namespace splash

@@ -213,6 +213,19 @@ def make_mask_info(kind, q_len, kv_len, left=None, right=None, chunk=None, dense
     return MaskInfo(h.value, lib, kind, int(q_len), local_kv, int(block_q), int(block_kv), d.num_heads)
 
 
+def _check_buffer(name, t, shape, dtype, device):
+    """A caller-supplied output or workspace tensor: the kernels write
+    exactly `shape` elements of `dtype` at its data pointer, so anything else
+    would be written out of bounds or misread."""
+    if t is None:
+        return
+    if not (t.is_cuda and t.device == device):
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
 def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
                out=None, lse=None, return_lse=True, stream=None, softmax_aux=None):
     """Splash-attention forward on GPU torch tensors (contiguous BHSD).
@@ -235,6 +248,8 @@ def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
     Hkv, Skv, Dv = k.shape[1], k.shape[2], v.shape[3]
     if k.shape[0] != B or v.shape[:3] != k.shape[:3] or k.shape[3] != D:
         raise ValueError("k / v shapes do not match q")
+    _check_buffer("out", out, (B, Hq, Sq, Dv), q.dtype, q.device)
+    _check_buffer("lse", lse, (B, Hq, Sq), torch.float32, q.device)
     if out is None:
         out = torch.empty((B, Hq, Sq, Dv), dtype=q.dtype, device=q.device)
     if return_lse and lse is None:
@@ -279,6 +294,10 @@ def lse_merge(out_a, lse_a, out_b, lse_b, out=None, lse=None, out_dtype=None, st
         raise ValueError("lse must be float32")
     if out is None:
         out = torch.empty(out_a.shape, dtype=out_dtype or out_a.dtype, device=out_a.device)
+    _check_buffer("out", out, out_a.shape, out.dtype if out is not None else None, out_a.device)
+    if out is not None and out.dtype not in dts:
+        raise ValueError("out must be bfloat16 or float32")
+    _check_buffer("lse", lse, lse_a.shape, torch.float32, out_a.device)
     if lse is None:
         lse = torch.empty(lse_a.shape, dtype=torch.float32, device=out_a.device)
     if stream is None:
@@ -339,6 +358,10 @@ def splash_bwd(q, k, v, out, lse, dout, mask_info, softmax_scale=None, logits_so
     Hkv, Skv, Dv = k.shape[1], k.shape[2], v.shape[3]
     if out.shape != (B, Hq, Sq, Dv) or dout.shape != out.shape or lse.shape != (B, Hq, Sq):
         raise ValueError("out / dout / lse shapes do not match q")
+    _check_buffer("dq", dq, q.shape, q.dtype, q.device)
+    _check_buffer("dk", dk, k.shape, k.dtype, q.device)
+    _check_buffer("dv", dv, v.shape, v.dtype, q.device)
+    _check_buffer("delta", delta, (B, Hq, Sq), torch.float32, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -413,6 +436,12 @@ def splash_decode(q, k, v, softmax_scale=None, logits_soft_cap=None, out=None, l
         raise ValueError("decode takes one query per head (q_len == 1)")
     nbytes = ctypes.c_size_t()
     _check(lib, lib.splash_decode_workspace_size(B, Hq, Hkv, Skv, D, ctypes.byref(nbytes)))
+    _check_buffer("out", out, (B, Hq, 1, Dv), q.dtype, q.device)
+    _check_buffer("lse", lse, (B, Hq), torch.float32, q.device)
+    if workspace is not None and not (workspace.is_cuda and workspace.device == q.device
+                                      and workspace.is_contiguous()
+                                      and workspace.numel() * workspace.element_size() >= nbytes.value):
+        raise ValueError(f"workspace must be a contiguous GPU tensor of at least {nbytes.value} bytes on {q.device}")
     if workspace is None:
         workspace = torch.empty(max(1, nbytes.value // 4), dtype=torch.float32, device=q.device)
     if out is None:

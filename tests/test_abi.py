@@ -183,3 +183,36 @@ def test_decode_workspace_size():
     assert lib.splash_decode_workspace_size(1, 16, 1, 1000, 128, ctypes.byref(n)) == splash.OK
     assert n.value == 1 * 1 * 8 * 16 * (128 + 2) * 4
     assert lib.splash_decode_workspace_size(1, 3, 2, 10, 64, ctypes.byref(n)) == splash.EINVAL
+
+
+@pytest.mark.parametrize("dtype,skv", [(splash.BF16, 8 * 1024 * 1024 + 128), (splash.F32, 4 * 1024 * 1024 + 128)])
+def test_fwd_and_bwd_reject_heads_beyond_32bit_buffers(dtype, skv):
+    """One head of k / v larger than 2^31 - 1 bytes cannot be addressed by the
+    kernels' 32-bit buffer resources: refused before anything runs."""
+    lib = splash.load_library()
+    mi = splash.make_mask_info("causal", 128, skv)
+    st = lib.splash_fwd(*_fwd_args(mi, Hq=1, Hkv=1, dtype=dtype))
+    assert st == splash.EUNSUPPORTED and "2^31" in lib.splash_last_error().decode()
+    a = _fwd_args(mi, Hq=1, Hkv=1, dtype=dtype)
+    assert lib.splash_fwd_sinks(*a[:-1], None, 0, 0, None) == splash.EUNSUPPORTED
+    if dtype == splash.BF16:
+        st = lib.splash_bwd(mi.handle, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1, 1, 1, 128, skv, 128, 128,
+                            splash.BF16, math.nan, 0.0, None)
+        assert st == splash.EUNSUPPORTED and "2^31" in lib.splash_last_error().decode()
+    # one block short of the limit passes validation (and then stops at the NULL lse-free no-op: B = 0)
+    mi_ok = splash.make_mask_info("causal", 128, skv - 256)
+    assert lib.splash_fwd(*_fwd_args(mi_ok, Hq=1, Hkv=1, dtype=dtype, B=0)) == splash.OK
+
+
+def test_binding_checks_caller_buffers():
+    """Outputs the caller passes must have the shape and dtype the kernel
+    writes; the check runs before any GPU work (CPU tensors are refused too)."""
+    import torch
+    x = torch.zeros((1, 2, 128, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        splash._check_buffer("out", x, (1, 2, 128, 128), torch.bfloat16, torch.device("cuda:0"))
+    with pytest.raises(ValueError):
+        splash._check_buffer("lse", torch.zeros(4), (1, 2, 128), torch.float32, torch.device("cpu"))
+    with pytest.raises(ValueError):
+        splash._check_buffer("out", x[:, :, :, :64], (1, 2, 128, 64), torch.bfloat16, torch.device("cpu"))
+    splash._check_buffer("out", None, (1,), torch.float32, torch.device("cpu"))

@@ -1,10 +1,13 @@
 """GPU parity of the backward (splash_bwd) against the fp64 oracle's
 attention_bwd (itself pinned against torch autograd and central differences).
 
-Tolerance: max-abs error of each gradient at most 2e-2 of the larger of 1 and
-the reference's max-abs -- the forward's bf16 bar, taken relative to the
-gradient's scale (bf16 inputs; p and ds enter the matrix products in bf16,
-fp32 accumulation)."""
+Tolerance: max-abs error of each gradient at most 1e-2 of the larger of 1 and
+the reference's max-abs (GRAD_TOL).  The gradients are written in bf16 (a
+relative rounding of up to 2^-9, 0.2 %) and p and ds enter the matrix
+products rounded to bf16 (another 0.2 % per term, fp32 accumulation), so a
+correct kernel sits near 0.4 % of the scale; measured maxima are 0.375 % in
+these cases and 0.54 % in the smoke case's dq.  A dropped term, a wrong
+scale or a missed block moves a gradient by far more."""
 import numpy as np
 import pytest
 import torch
@@ -16,6 +19,7 @@ from tests.gpu_cases import mask_rows_fn
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
+GRAD_TOL = 1e-2
 
 
 @pytest.fixture(autouse=True)
@@ -30,7 +34,7 @@ def _check(name, got, ref):
     scale = max(1.0, float(np.abs(ref).max()))
     err = float(np.abs(got - ref).max())
     print(f"{name}: max|d|={err:.3e} ref max={scale:.3e}", flush=True)
-    assert err <= 2e-2 * scale, (name, err, scale)
+    assert err <= GRAD_TOL * scale, (name, err, scale)
 
 
 def _run(seed, B, Hq, Hkv, Sq, Skv, D, kind, cap=None, dense=None, **mk):
@@ -62,6 +66,8 @@ CASES = [
     ("local_d64_cap", 106, 1, 2, 1, 512, 512, 64, dict(kind="local", left=None, right=100), 3.0),
     ("rect_sq_lt_skv", 107, 1, 2, 2, 256, 640, 128, dict(kind="causal"), None),
     ("rect_sq_gt_skv", 108, 1, 2, 2, 640, 256, 128, dict(kind="causal"), None),
+    # 258 key blocks per row (more than one 256-slot metadata chunk; int16 data_next)
+    ("rows_258_blocks", 109, 1, 2, 1, 256, 33024, 128, dict(kind="local", left=None, right=None), None),
 ]
 
 

@@ -380,3 +380,31 @@ def test_bwd_finite_differences():
             num[idx] = (lp - lm) / (2 * eps)
         np.testing.assert_allclose(grad, num, rtol=0, atol=1e-8)
     assert np.all(dq[0, 0, 2] == 0)
+
+
+@pytest.mark.parametrize("kind,kw,cap", [
+    ("causal", {}, None),
+    ("local", dict(left=70, right=20), None),
+    ("chunked", dict(chunk=96), 5.0),
+    ("dense", {}, None),
+])
+def test_block_row_oracle_equals_plain_oracle(kind, kw, cap):
+    """The GPU tests' whole-output reference (the oracle called per group of
+    query rows on the span of keys those rows may see) equals the oracle over
+    all keys: a masked key contributes nothing.  Rectangular shapes, GQA, a
+    row with no allowed key and a key range no row sees are included."""
+    from block_sparse_attention_make_amd import synthetic
+    from tests.gpu_cases import oracle_by_block_rows, oracle_full
+    q, k, v = synthetic.make_qkv(77, 2, 4, 2, 300, 420, 32, 16)
+    dense = None
+    if kind == "dense":
+        rng = np.random.default_rng(78)
+        dense = synthetic.random_dense_mask(rng, 4, 300, 420, 0.1)
+        dense[:, 17] = False
+        dense[:, :, 400:] = False
+    o, l = oracle_by_block_rows(q, k, v, kind, dense=dense, cap=cap, rows_per_call=64, **kw)
+    o2, l2 = oracle_full(q, k, v, kind, dense=dense, cap=cap, **kw)
+    assert np.array_equal(np.isfinite(l), np.isfinite(l2))
+    assert np.abs(o - o2).max() < 1e-12
+    fin = np.isfinite(l2)
+    assert np.abs(l[fin] - l2[fin]).max() < 1e-12
