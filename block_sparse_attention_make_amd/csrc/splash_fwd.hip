@@ -231,6 +231,7 @@ void splash_fwd_f32(const FwdParams p) {
   // ---- running softmax state ----------------------------------------------
   const float c2 = p.c2;                   // score multiplier into base-2 units
   float m_run = -INFINITY;                 // running max (raw score units, or capped base-2 units)
+  float mb_run = -INFINITY;                // the same in base-2 units, as the exponentials used it
   float l_run = 0.f;                       // this lane's share of the running sum
   f32x16 o[kDT];
 #pragma unroll
@@ -344,8 +345,17 @@ void splash_fwd_f32(const FwdParams p) {
       mx = pair_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float mb = m_use * c2e;
-      const float alpha = __builtin_amdgcn_exp2f(m_run * c2e - mb);
+      float mb = m_use * c2e;
+      // The base must be the same rounded float everywhere it is used: the
+      // exponentials, alpha and the lse.  HIP contracts a*b+c into an FMA
+      // across statements, which would fuse this product into
+      // mb_run - mb and leave its rounding error in alpha: alpha one ulp off
+      // 1 at every step of an unmoved max, a drift of the running sum and
+      // the accumulator of about 1e-7 per block (2e-5 in lse after 258
+      // blocks).  The empty asm makes mb an opaque, already rounded value.
+      asm volatile("" : "+v"(mb));
+      const float alpha = __builtin_amdgcn_exp2f(mb_run - mb);
+      mb_run = mb;
       float rs = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -385,10 +395,7 @@ void splash_fwd_f32(const FwdParams p) {
   // ---- epilogue: O / l, lse ----
   const float l_tot = pair_sum(l_run);
   float inv, lse_row;
-  {
-    const float m_fin = m_run == -INFINITY ? 0.f : m_run;
-    row_finish(l_tot, m_fin * (CAP ? 1.f : c2), sink_lse2(p, hq), inv, lse_row);
-  }
+  row_finish(l_tot, mb_run == -INFINITY ? 0.f : mb_run, sink_lse2(p, hq), inv, lse_row);
   float *og = static_cast<float *>(p.out) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
