@@ -10,4 +10,5 @@ compiler and the C ABI of include/splash.h) is loaded on first use and must
 have been built with `python -m block_sparse_attention_make_amd.build`.
 """
 from .splash import (MaskInfo, SplashError, load_library, lse_merge, make_mask_info,  # noqa: F401
-                     splash_attention, splash_bwd, splash_decode, splash_fwd, splash_fwd_kv_sharded)
+                     splash_attention, splash_bwd, splash_decode, splash_decode_static, splash_fwd,
+                     splash_fwd_kv_sharded)

@@ -597,11 +597,14 @@ extern "C" SPLASH_API splash_status splash_decode_workspace_size(int64_t B, int6
   return SPLASH_OK;
 }
 
-extern "C" SPLASH_API splash_status splash_decode(const void *q, const void *k, const void *v, void *out, float *lse,
-                                                  void *workspace, size_t workspace_bytes, int64_t B, int64_t Hq,
-                                                  int64_t Hkv, int64_t Skv, int64_t D, int64_t Dv, int32_t dtype,
-                                                  float softmax_scale, float logits_soft_cap, void *hip_stream) {
-  clear_error();
+namespace {
+
+// Size and argument checks of both decode entry points (pointers and the
+// workspace aside).  Returns SPLASH_OK with *noop set when there is nothing
+// to compute.
+splash_status decode_validate(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv, int64_t D, int64_t Dv, int32_t dtype,
+                              float softmax_scale, bool *noop) {
+  *noop = false;
   if (B < 0 || Hq < 0 || Hkv < 0 || Skv < 0 || D <= 0 || Dv <= 0)
     return fail(SPLASH_EINVAL, "negative size or non-positive head dim");
   if (dtype != SPLASH_BF16 && dtype != SPLASH_F32) return fail(SPLASH_EINVAL, "unknown dtype");
@@ -611,20 +614,27 @@ extern "C" SPLASH_API splash_status splash_decode(const void *q, const void *k, 
   if (D != Dv || (D != 64 && D != 128)) return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
   if (!(std::isnan(softmax_scale) || (std::isfinite(softmax_scale) && softmax_scale > 0.f)))
     return fail(SPLASH_EINVAL, "softmax_scale must be NaN (default) or finite and > 0");
-  if (B == 0 || Hq == 0) return SPLASH_OK;
+  if (B == 0 || Hq == 0) {
+    *noop = true;
+    return SPLASH_OK;
+  }
   const int64_t group = Hq / Hkv;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
     return fail(SPLASH_EUNSUPPORTED, "decode runs GQA groups of 1, 2, 4, 8 or 16 query heads");
   if (Skv == 0) return fail(SPLASH_EUNSUPPORTED, "decode needs at least one key");
   if (B * Hkv > 0x7fffffffLL || decode_chunks(B * Hkv, group, D, Skv) > 65535 || B * Hq > 0x7fffffffLL)
     return fail(SPLASH_EUNSUPPORTED, "grid too large");
-  if (Skv * D * 2 > 0x7fffffffLL)
+  if (Skv * D * 2 > kMaxHeadBytes)
     return fail(SPLASH_EUNSUPPORTED, "the K (or V) cache of one head exceeds 2 GiB");
-  if (!q || !k || !v || !out || !workspace) return fail(SPLASH_EINVAL, "NULL pointer");
-  if (!aligned16({q, k, v, out, workspace})) return fail(SPLASH_EINVAL, "q, k, v, out and workspace must be 16-byte aligned");
-  const int64_t floats = decode_ws_floats(B, Hq, Hkv, Skv, D);
-  if (workspace_bytes < static_cast<size_t>(floats) * sizeof(float))
-    return fail(SPLASH_EINVAL, "workspace smaller than splash_decode_workspace_size");
+  return SPLASH_OK;
+}
+
+// Launch of both decode entry points: the partial and merge kernels with
+// their scratch at `workspace` (already checked to be large enough).
+splash_status decode_launch(const void *q, const void *k, const void *v, void *out, float *lse, void *workspace,
+                            int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv, int64_t D, float softmax_scale,
+                            float logits_soft_cap, void *hip_stream) {
+  const int64_t group = Hq / Hkv;
   DecodeParams p{};
   p.q = q;
   p.k = k;
@@ -652,4 +662,44 @@ extern "C" SPLASH_API splash_status splash_decode(const void *q, const void *k, 
   hipError_t e = launch_decode(p, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return SPLASH_OK;
+}
+
+}  // namespace
+
+extern "C" SPLASH_API splash_status splash_decode(const void *q, const void *k, const void *v, void *out, float *lse,
+                                                  void *workspace, size_t workspace_bytes, int64_t B, int64_t Hq,
+                                                  int64_t Hkv, int64_t Skv, int64_t D, int64_t Dv, int32_t dtype,
+                                                  float softmax_scale, float logits_soft_cap, void *hip_stream) {
+  clear_error();
+  bool noop = false;
+  splash_status st = decode_validate(B, Hq, Hkv, Skv, D, Dv, dtype, softmax_scale, &noop);
+  if (st != SPLASH_OK || noop) return st;
+  if (!q || !k || !v || !out || !workspace) return fail(SPLASH_EINVAL, "NULL pointer");
+  if (!aligned16({q, k, v, out, workspace})) return fail(SPLASH_EINVAL, "q, k, v, out and workspace must be 16-byte aligned");
+  const int64_t floats = decode_ws_floats(B, Hq, Hkv, Skv, D);
+  if (workspace_bytes < static_cast<size_t>(floats) * sizeof(float))
+    return fail(SPLASH_EINVAL, "workspace smaller than splash_decode_workspace_size");
+  return decode_launch(q, k, v, out, lse, workspace, B, Hq, Hkv, Skv, D, softmax_scale, logits_soft_cap, hip_stream);
+}
+
+extern "C" SPLASH_API splash_status splash_decode_static(const void *q, const void *k, const void *v, void *out,
+                                                         float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv,
+                                                         int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
+                                                         float logits_soft_cap, void *hip_stream) {
+  clear_error();
+  bool noop = false;
+  splash_status st = decode_validate(B, Hq, Hkv, Skv, D, Dv, dtype, softmax_scale, &noop);
+  if (st != SPLASH_OK || noop) return st;
+  if (!q || !k || !v || !out) return fail(SPLASH_EINVAL, "NULL pointer");
+  if (!aligned16({q, k, v, out})) return fail(SPLASH_EINVAL, "q, k, v and out must be 16-byte aligned");
+  const size_t need = static_cast<size_t>(decode_ws_floats(B, Hq, Hkv, Skv, D)) * sizeof(float);
+  if (need > kDecodeStaticScratchBytes)
+    return fail(SPLASH_EUNSUPPORTED, "this decode needs " + std::to_string(need) +
+                                         " bytes of scratch; the library's static scratch holds " +
+                                         std::to_string(kDecodeStaticScratchBytes) +
+                                         " (use splash_decode with a workspace)");
+  void *scratch = nullptr;
+  const hipError_t e = decode_static_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "looking up the static decode scratch");
+  return decode_launch(q, k, v, out, lse, scratch, B, Hq, Hkv, Skv, D, softmax_scale, logits_soft_cap, hip_stream);
 }

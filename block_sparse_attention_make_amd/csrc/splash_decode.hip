@@ -21,6 +21,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "splash_kernel.h"
 
@@ -381,6 +382,37 @@ int64_t decode_chunks(int64_t units, int64_t group, int64_t D, int64_t Skv) {
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
   return p.D == 64 ? go_g<64>(p, stream) : go_g<128>(p, stream);
+}
+
+// Scratch of the allocation-free decode entry point: the per-range partial
+// max, sum and output that splash_decode keeps in its caller's workspace.
+// Each GPU the library runs on holds its own copy for the life of the
+// process.  In host code `scratch` names a host-side stand-in, not device
+// memory, so its device address is looked up once per device and only that
+// address is handed to kernels.
+static __device__ __align__(256) float scratch[kDecodeStaticScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t decode_static_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace splash

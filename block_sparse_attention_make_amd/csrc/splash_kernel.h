@@ -77,4 +77,10 @@ int64_t decode_split_keys(int64_t units, int64_t group, int64_t D, int64_t Skv);
 int64_t decode_chunks(int64_t units, int64_t group, int64_t D, int64_t Skv);
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 
+// The allocation-free decode's scratch: a file-scope device array of this
+// many bytes, one per GPU.  decode_static_scratch returns its device address
+// on the current device (looked up on the first call per device).
+constexpr size_t kDecodeStaticScratchBytes = size_t(16) << 20;
+hipError_t decode_static_scratch(void **ptr);
+
 }  // namespace splash

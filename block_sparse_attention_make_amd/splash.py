@@ -83,6 +83,9 @@ def load_library(path=None):
     lib.splash_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, i64, i64, i64, i64, i64, i64, i32,
                                   ctypes.c_float, ctypes.c_float, vp]
     lib.splash_decode.restype = ctypes.c_int
+    lib.splash_decode_static.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, ctypes.c_float,
+                                         ctypes.c_float, vp]
+    lib.splash_decode_static.restype = ctypes.c_int
     lib.splash_last_error.argtypes = []
     lib.splash_last_error.restype = ctypes.c_char_p
     if path is None:
@@ -456,5 +459,36 @@ def splash_decode(q, k, v, softmax_scale=None, logits_soft_cap=None, out=None, l
         st = lib.splash_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                B, Hq, Hkv, Skv, D, Dv, BF16, scale, cap, ctypes.c_void_p(stream.cuda_stream))
+    _check(lib, st)
+    return out, lse
+
+
+def splash_decode_static(q, k, v, softmax_scale=None, logits_soft_cap=None, out=None, lse=None, stream=None):
+    """splash_decode without a workspace: the library keeps the partials in
+    its own per-GPU static scratch (16 MiB), so the call itself allocates
+    nothing beyond out / lse when those are not given.  Calls that overlap
+    on one GPU race; calls ordered on one stream are safe."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not (t.is_cuda and t.is_contiguous() and t.dim() == 4 and t.dtype == torch.bfloat16):
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if Sq != 1:
+        raise ValueError("decode takes one query per head (q_len == 1)")
+    _check_buffer("out", out, (B, Hq, 1, Dv), q.dtype, q.device)
+    _check_buffer("lse", lse, (B, Hq), torch.float32, q.device)
+    if out is None:
+        out = torch.empty((B, Hq, 1, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    scale = math.nan if softmax_scale is None else float(softmax_scale)
+    cap = 0.0 if logits_soft_cap is None else float(logits_soft_cap)
+    with torch.cuda.device(q.device):
+        st = lib.splash_decode_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                      B, Hq, Hkv, Skv, D, Dv, BF16, scale, cap, ctypes.c_void_p(stream.cuda_stream))
     _check(lib, st)
     return out, lse

@@ -314,6 +314,24 @@ SPLASH_API splash_status splash_decode(const void *q, const void *k, const void 
                                        int64_t Hkv, int64_t Skv, int64_t D, int64_t Dv, int32_t dtype,
                                        float softmax_scale, float logits_soft_cap, void *hip_stream);
 
+/* splash_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels, results and errors as splash_decode, without the
+ * workspace: the per-range partials live in a file-scope device array of the
+ * library, 16 MiB (16777216 bytes) on each GPU it runs on, held until the
+ * process ends; its device address is looked up on the first call on each
+ * device.  A call whose partials need more than that (see
+ * splash_decode_workspace_size) returns SPLASH_EUNSUPPORTED before anything
+ * runs.  The call allocates nothing, on the device or the host.  Every call
+ * on one GPU shares that GPU's array, which keeps the last call's partials
+ * (no part of it needs to start at zero): calls that overlap on one GPU --
+ * on different streams, or from several threads without ordering -- race
+ * and give wrong results; calls ordered on one stream are safe. */
+SPLASH_API splash_status splash_decode_static(const void *q, const void *k, const void *v, void *out, float *lse,
+                                              int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv, int64_t D, int64_t Dv,
+                                              int32_t dtype, float softmax_scale, float logits_soft_cap,
+                                              void *hip_stream);
+
 /* Message of the last failed call on this thread ("" if none).  The string
  * stays valid until the next library call on this thread. */
 SPLASH_API const char *splash_last_error(void);

@@ -21,7 +21,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "splash_bwd", "splash_decode", "splash_decode_workspace_size", "splash_fwd", "splash_fwd_sinks",
+        "splash_bwd", "splash_decode", "splash_decode_static", "splash_decode_workspace_size", "splash_fwd",
+        "splash_fwd_sinks",
         "splash_last_error", "splash_lse_merge",
         "splash_make_mask_info", "splash_make_mask_info_kv_slice", "splash_mask_info_destroy",
         "splash_mask_info_read_device", "splash_mask_info_upload", "splash_mask_info_view"])
@@ -216,3 +217,23 @@ def test_binding_checks_caller_buffers():
     with pytest.raises(ValueError):
         splash._check_buffer("out", x[:, :, :, :64], (1, 2, 128, 64), torch.bfloat16, torch.device("cpu"))
     splash._check_buffer("out", None, (1,), torch.float32, torch.device("cpu"))
+
+
+def test_static_decode_rejects_more_than_its_scratch_before_running():
+    """splash_decode_static keeps its partials in a 16 MiB static array: a
+    decode whose partials need more is refused before any GPU call, and the
+    other argument errors match splash_decode's."""
+    lib = splash.load_library()
+    n = ctypes.c_size_t()
+    # 4096 x 16 query heads of D = 128, one range each: 4096 * 16 * 130 * 4 bytes = 34 MB of partials
+    assert lib.splash_decode_workspace_size(4096, 16, 1, 1000, 128, ctypes.byref(n)) == splash.OK
+    assert n.value > 16 << 20
+    a = dict(q=16, k=16, v=16, out=16, lse=None, B=4096, Hq=16, Hkv=1, Skv=1000, D=128, Dv=128,
+             dtype=splash.BF16, scale=math.nan, cap=0.0, stream=None)
+    st = lib.splash_decode_static(*a.values())
+    assert st == splash.EUNSUPPORTED and "scratch" in lib.splash_last_error().decode()
+    for over, status in ((dict(dtype=splash.F32), splash.EUNSUPPORTED), (dict(Hq=3, Hkv=2), splash.EINVAL),
+                         (dict(q=0), splash.EINVAL), (dict(q=8), splash.EINVAL), (dict(D=96, Dv=96), splash.EUNSUPPORTED)):
+        b = dict(a, B=1, **over)
+        assert lib.splash_decode_static(*b.values()) == status, (over, lib.splash_last_error())
+    assert lib.splash_decode_static(*dict(a, B=0, q=0, k=0, v=0, out=0).values()) == splash.OK
