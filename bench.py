@@ -344,6 +344,8 @@ def main():
     ap.add_argument("--kv-shards", type=int, default=1, help="time the key/value-sharded path")
     ap.add_argument("--backward", action="store_true", help="time splash_bwd")
     ap.add_argument("--decode", action="store_true", help="time splash_decode on a decode workload")
+    ap.add_argument("--kv-splits", default="auto",
+                    help="key splits per block row: auto (the library's plan) or 1..8")
     ap.add_argument("--block-q", type=int, default=128, help="mask block rows (a multiple of 128)")
     ap.add_argument("--block-kv", type=int, default=128, help="mask block columns (a multiple of 128)")
     ap.add_argument("--cold", action="store_true",
@@ -403,8 +405,18 @@ def main():
         flops_exec = blocks_computed * 7 * 2 * w.block * w.block * w.D
         flops_dense = w.B * w.Hq * w.Sq * w.Skv * 5 * 2 * w.D
 
+    from block_sparse_attention_make_amd.splash import plan_kv_splits
+    splits = (plan_kv_splits(mi, w.B, w.Hq, 0 if w.dtype == "bf16" else 1) if args.kv_splits == "auto"
+              else int(args.kv_splits))
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty((w.B, w.Hq, w.Sq, w.Dv), dtype=q.dtype, device=dev)
+    split_ws = None
+    if splits > 1:
+        import ctypes
+        from block_sparse_attention_make_amd.splash import load_library
+        nb = ctypes.c_size_t()
+        load_library().splash_fwd_workspace_size(w.B, w.Hq, w.Sq, w.Dv, splits, ctypes.byref(nb))
+        split_ws = torch.empty(max(1, nb.value // 4), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     aux = None
@@ -445,7 +457,7 @@ def main():
             splash_fwd_kv_sharded(qd, ks, vs, shard_mis, logits_soft_cap=w.soft_cap, stream=stream)
         else:
             splash_fwd(qd, kd, vd, mi, logits_soft_cap=w.soft_cap, out=out, lse=lse, stream=stream,
-                       softmax_aux=aux)
+                       softmax_aux=aux, kv_splits=splits, workspace=split_ws)
 
     prewarm_s = prewarm(step, torch, args.prewarm_s)
     for _ in range(args.warmup):
@@ -522,7 +534,7 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "seq_len": w.Sq, "head_dim": w.D, "mask": m.kind, "block": w.block,
                    "soft_cap": w.soft_cap, "parallelism": "single-gpu",
-                   "sinks_per_kv_head": args.sinks, "kv_shards": P,
+                   "sinks_per_kv_head": args.sinks, "kv_shards": P, "kv_splits": splits,
                    "mask_block": [args.block_q, args.block_kv], "pass": "backward" if args.backward else "forward"},
         "prewarm_s": round(prewarm_s, 2),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -540,6 +552,8 @@ def main():
                      "kernel_ms_avg": round(kern_avg, 5)},
         "cpu_baseline": None,
     }
+    if splits > 1 and not args.backward and P == 1:
+        res["roofline"]["kernel"] = "splash_fwd_wide (key splits) + merge_splits"
     if args.backward:
         res["roofline"]["kernel"] = "bwd_delta + bwd_dkdv + bwd_dq (executed products: 7 per block)"
         res["roofline"]["flops_per_launch"] = flops_exec

@@ -63,6 +63,14 @@ void free_copy(DeviceCopy &dc) {
   }
   dc.has_cols = false;
   dc.col_w = 0;
+  for (int32_t **t : {&dc.walk_kv, &dc.walk_mn}) {
+    if (*t) (void)hipFree(*t);
+    *t = nullptr;
+  }
+  for (int32_t *&t : dc.items) {
+    if (t) (void)hipFree(t);
+    t = nullptr;
+  }
   dc.device = -1;
   if (prev >= 0) (void)hipSetDevice(prev);
 }
@@ -153,6 +161,87 @@ hipError_t upload_vec(const std::vector<T> &v, T **dst) {
   return e;
 }
 
+// Grid geometry the forward kernels walk: the MaskInfo's own, or its kernel
+// view for blocks larger than 128 x 128.
+struct Walk {
+  int64_t nq, width;
+  bool view;
+};
+Walk walk_of(const splash_mask_info *mi) {
+  if (mi->block_q != 128 || mi->block_kv != 128) return {mi->q_len / 128, std::max<int64_t>(1, mi->width * (mi->block_kv / 128)), true};
+  return {mi->nq, mi->width, false};
+}
+
+// The non-empty grid positions of every block row of the walk geometry, in
+// order: (data_next, label, mask_next) and each row's first entry.
+struct WalkLists {
+  std::vector<int32_t> kv, mn;      // kv: data_next | label << 28
+  std::vector<int64_t> row_off;     // [Hm * nq + 1]
+};
+WalkLists build_walk(const splash_mask_info *mi) {
+  const Walk wk = walk_of(mi);
+  const int64_t hm = mi->num_heads;
+  const HostArray &bm = mi->arr[SPLASH_MI_BLOCK_MASK], &dn = mi->arr[SPLASH_MI_DATA_NEXT];
+  const HostArray &mn = mi->arr[SPLASH_MI_MASK_NEXT];
+  WalkLists w;
+  w.row_off.assign(static_cast<size_t>(hm * wk.nq + 1), 0);
+  for (int64_t h = 0; h < hm; ++h)
+    for (int64_t r = 0; r < wk.nq; ++r) {
+      for (int64_t sl = 0; sl < wk.width; ++sl) {
+        const int64_t at = (h * wk.nq + r) * wk.width + sl;
+        const int64_t label = wk.view ? mi->kview.bm[at] : host_index(bm, at);
+        if (label <= 0) continue;
+        const int64_t c = wk.view ? mi->kview.dn[at] : host_index(dn, at);
+        const int64_t m = wk.view ? mi->kview.mn[at] : (mn.present ? host_index(mn, at) : 0);
+        w.kv.push_back(static_cast<int32_t>(c | (label << 28)));
+        w.mn.push_back(static_cast<int32_t>(label == 1 ? m : 0));
+      }
+      w.row_off[h * wk.nq + r + 1] = static_cast<int64_t>(w.kv.size());
+    }
+  return w;
+}
+
+// The item table for S key splits (see DeviceCopy::items), uploaded to the
+// device copy `dc`.  Called under the MaskInfo's lock, after the device copy
+// (and the kernel view, if any) exists.
+splash_status ensure_items(splash_mask_info *mi, DeviceCopy &dc, int S, const WalkLists *lists = nullptr) {
+  if (dc.items[S]) return SPLASH_OK;
+  WalkLists own;
+  if (!lists) {
+    own = build_walk(mi);
+    lists = &own;
+  }
+  const Walk wk = walk_of(mi);
+  const int64_t hm = mi->num_heads;
+  const std::vector<int32_t> &order = wk.view ? mi->kview.row_order : mi->row_order;
+  std::vector<int32_t> table(static_cast<size_t>(std::max<int64_t>(1, hm * wk.nq * S) * 8), 0);
+  for (int64_t h = 0; h < hm; ++h)
+    for (int64_t i = 0; i < wk.nq; ++i) {
+      const int64_t r = order.empty() ? i : order[static_cast<size_t>(i)];
+      const int64_t r0 = lists->row_off[h * wk.nq + r], n = lists->row_off[h * wk.nq + r + 1] - r0;
+      for (int s = 0; s < S; ++s) {
+        const int64_t a = n * s / S, e = n * (s + 1) / S;
+        int32_t *it = table.data() + ((h * wk.nq + i) * S + s) * 8;
+        it[0] = static_cast<int32_t>(r);
+        it[1] = static_cast<int32_t>(r0 + a);
+        it[2] = static_cast<int32_t>(e - a);
+        // first block of the range, or of the row, or block 0: the prologue
+        // starts its loads there, so it must name a real block
+        const int64_t f = a < n ? r0 + a : (n > 0 ? r0 : -1);
+        it[3] = f >= 0 ? (lists->kv[static_cast<size_t>(f)] & 0x0fffffff) : 0;
+        it[4] = f >= 0 ? lists->mn[static_cast<size_t>(f)] : 0;
+      }
+    }
+  int32_t *d = nullptr;
+  hipError_t e = upload_vec(table, &d);
+  if (e != hipSuccess) {
+    if (d) (void)hipFree(d);
+    return hip_fail(e, "uploading the forward's item table");
+  }
+  dc.items[S] = d;
+  return SPLASH_OK;
+}
+
 // Device copy for the current device, uploading it if needed.
 splash_status ensure_device_copy(splash_mask_info *mi, DeviceCopy **out) {
   int dev = -1;
@@ -217,6 +306,26 @@ splash_status ensure_device_copy(splash_mask_info *mi, DeviceCopy **out) {
       return hip_fail(e, "uploading the kernel view");
     }
     fresh.kbits_bytes = static_cast<int64_t>(kv.bits.size() * sizeof(uint32_t));
+  }
+  {
+    WalkLists lists;
+    try {
+      lists = build_walk(mi);
+    } catch (const std::bad_alloc &) {
+      free_copy(fresh);
+      return fail(SPLASH_ENOMEM, "out of host memory for the forward's walk lists");
+    }
+    e = upload_vec(lists.kv, &fresh.walk_kv);
+    if (e == hipSuccess && mi->kind == SPLASH_MASK_DENSE) e = upload_vec(lists.mn, &fresh.walk_mn);
+    if (e != hipSuccess) {
+      free_copy(fresh);
+      return hip_fail(e, "uploading the forward's walk lists");
+    }
+    const splash_status st = ensure_items(mi, fresh, 1, &lists);
+    if (st != SPLASH_OK) {
+      free_copy(fresh);
+      return st;
+    }
   }
   dc = fresh;
   *out = &dc;
@@ -295,6 +404,7 @@ splash_status ensure_cols(splash_mask_info *mi, DeviceCopy &dc) {
   dc.has_cols = true;
   return SPLASH_OK;
 }
+
 
 }  // namespace
 }  // namespace splash
@@ -391,6 +501,7 @@ FwdParams make_params(const splash_mask_info *mi, const DeviceCopy *dc, const vo
                       const void *v, void *out, float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
                       int64_t Skv, int64_t D, float scale, float logits_soft_cap) {
   FwdParams p{};
+  p.kv_splits = 1;
   p.q = q;
   p.k = k;
   p.v = v;
@@ -414,6 +525,9 @@ FwdParams make_params(const splash_mask_info *mi, const DeviceCopy *dc, const vo
   p.pmb_bits_bytes = dc->mask_bits_bytes;
   p.q_seq = static_cast<const int32_t *>(dc->ptr[SPLASH_MI_Q_SEQUENCE]);
   p.row_order = dc->row_order;
+  p.walk_kv = dc->walk_kv;
+  p.walk_mn = dc->walk_mn;
+  p.items = dc->items[1];
   p.bm_bytes = mi->arr[SPLASH_MI_BLOCK_MASK].elem_bits / 8;
   p.dn_bytes = mi->arr[SPLASH_MI_DATA_NEXT].elem_bits / 8;
   p.mn_bytes = mi->arr[SPLASH_MI_MASK_NEXT].present ? mi->arr[SPLASH_MI_MASK_NEXT].elem_bits / 8 : 4;
@@ -448,14 +562,32 @@ float resolve_scale(float softmax_scale, int64_t D) {
   return std::isnan(softmax_scale) ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D))) : softmax_scale;
 }
 
+// Bytes of the split-key workspace: normalised partial outputs and lses,
+// float32, [S, B, Hq, Sq, Dv] then [S, B, Hq, Sq].
+int64_t split_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t Dv, int64_t S) {
+  return S > 1 ? S * B * Hq * Sq * (Dv + 1) * 4 : 0;
+}
+
 splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const void *v, void *out,
                        float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                        int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
                        float logits_soft_cap, const float *aux, int32_t aux_heads,
-                       int32_t num_sinks, void *hip_stream) {
+                       int32_t num_sinks, int32_t kv_splits, void *workspace, size_t workspace_bytes,
+                       void *hip_stream) {
   // ---- validation: nothing below launches or allocates until all passes ----
   splash_status st = validate_call(mi, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale);
   if (st != SPLASH_OK) return st;
+  if (kv_splits < 1 || kv_splits > DeviceCopy::kMaxSplits)
+    return fail(SPLASH_EINVAL, "kv_splits must be in 1..8");
+  if (kv_splits > 1 && dtype != SPLASH_BF16)
+    return fail(SPLASH_EUNSUPPORTED, "key splits run on the bf16 kernel only");
+  if (B * Hq * (Sq / 128) * kv_splits > 0x7fffffffLL) return fail(SPLASH_EUNSUPPORTED, "grid too large");
+  if (kv_splits > 1 && B > 0 && Hq > 0 && Sq > 0) {
+    const int64_t need = split_workspace_bytes(B, Hq, Sq, Dv, kv_splits);
+    if (!workspace || workspace_bytes < static_cast<size_t>(need))
+      return fail(SPLASH_EINVAL, "workspace missing or smaller than splash_fwd_workspace_size");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(SPLASH_EINVAL, "workspace must be 16-byte aligned");
+  }
   if (num_sinks < 0) return fail(SPLASH_EINVAL, "num_sinks must be >= 0");
   if (num_sinks > 0) {
     if (!aux) return fail(SPLASH_EINVAL, "softmax_aux is NULL with num_sinks > 0");
@@ -471,12 +603,23 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
   DeviceCopy *dc = nullptr;
   st = ensure_device_copy(mi, &dc);
   if (st != SPLASH_OK) return st;
+  if (kv_splits > 1) {
+    std::lock_guard<std::mutex> lock(mi->mu);
+    st = ensure_items(mi, *dc, kv_splits);
+    if (st != SPLASH_OK) return st;
+  }
 
   FwdParams p = make_params(mi, dc, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, resolve_scale(softmax_scale, D),
                             logits_soft_cap);
   p.aux = num_sinks > 0 ? aux : nullptr;
   p.aux_heads = num_sinks > 0 ? aux_heads : 0;
   p.num_sinks = num_sinks;
+  p.kv_splits = kv_splits;
+  p.items = dc->items[kv_splits];
+  if (kv_splits > 1) {
+    p.part_o = static_cast<float *>(workspace);
+    p.part_lse = p.part_o + kv_splits * B * Hq * Sq * Dv;
+  }
 
   hipError_t e = launch_fwd(p, dtype, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
@@ -493,7 +636,7 @@ extern "C" SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void 
                                                void *hip_stream) {
   clear_error();
   return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale,
-                  logits_soft_cap, nullptr, 0, 0, hip_stream);
+                  logits_soft_cap, nullptr, 0, 0, 1, nullptr, 0, hip_stream);
 }
 
 extern "C" SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const void *q, const void *k,
@@ -505,7 +648,58 @@ extern "C" SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const
                                                      int32_t num_sinks, void *hip_stream) {
   clear_error();
   return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale,
-                  logits_soft_cap, softmax_aux, aux_heads, num_sinks, hip_stream);
+                  logits_soft_cap, softmax_aux, aux_heads, num_sinks, 1, nullptr, 0, hip_stream);
+}
+
+extern "C" SPLASH_API splash_status splash_fwd_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t Dv,
+                                                              int32_t kv_splits, size_t *bytes) {
+  clear_error();
+  if (!bytes) return fail(SPLASH_EINVAL, "bytes is NULL");
+  if (B < 0 || Hq < 0 || Sq < 0 || Dv <= 0) return fail(SPLASH_EINVAL, "negative size or non-positive head dim");
+  if (kv_splits < 1 || kv_splits > DeviceCopy::kMaxSplits) return fail(SPLASH_EINVAL, "kv_splits must be in 1..8");
+  *bytes = static_cast<size_t>(split_workspace_bytes(B, Hq, Sq, Dv, kv_splits));
+  return SPLASH_OK;
+}
+
+extern "C" SPLASH_API splash_status splash_fwd_plan(const splash_mask_info *mi, int64_t B, int64_t Hq, int32_t dtype,
+                                                    int32_t *kv_splits) {
+  clear_error();
+  if (!mi || !kv_splits) return fail(SPLASH_EINVAL, "NULL argument");
+  if (B < 0 || Hq < 0) return fail(SPLASH_EINVAL, "negative size");
+  if (dtype != SPLASH_BF16 && dtype != SPLASH_F32) return fail(SPLASH_EINVAL, "unknown dtype");
+  *kv_splits = 1;
+  if (dtype != SPLASH_BF16 || B == 0 || Hq == 0) return SPLASH_OK;
+  int dev = -1, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "querying the device's compute units");
+  const Walk wk = walk_of(mi);
+  const int64_t n_wg = B * Hq * wk.nq;
+  const int64_t slots = 2 * static_cast<int64_t>(cus);   // the bf16 kernel runs two workgroups per CU
+  if (n_wg == 0 || n_wg >= slots) return SPLASH_OK;
+  // non-empty 128 x 128 blocks per block row, on average
+  const HostArray &bm = mi->arr[SPLASH_MI_BLOCK_MASK];
+  int64_t nonempty = 0;
+  for (int64_t i = 0; i < bm.numel(); ++i) nonempty += host_index(bm, i) > 0 ? 1 : 0;
+  nonempty *= (mi->block_q / 128) * (mi->block_kv / 128);
+  const int64_t rows = std::max<int64_t>(1, mi->num_heads * wk.nq);
+  const int64_t per_row = nonempty / rows;
+  int64_t S = (slots + n_wg - 1) / n_wg;
+  S = std::min<int64_t>(S, std::max<int64_t>(1, per_row / 2));   // at least two blocks per split
+  *kv_splits = static_cast<int32_t>(std::min<int64_t>(S, DeviceCopy::kMaxSplits));
+  return SPLASH_OK;
+}
+
+extern "C" SPLASH_API splash_status splash_fwd_split(splash_mask_info *mi, const void *q, const void *k,
+                                                     const void *v, void *out, float *lse, int64_t B, int64_t Hq,
+                                                     int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D, int64_t Dv,
+                                                     int32_t dtype, float softmax_scale, float logits_soft_cap,
+                                                     const float *softmax_aux, int32_t aux_heads, int32_t num_sinks,
+                                                     int32_t kv_splits, void *workspace, size_t workspace_bytes,
+                                                     void *hip_stream) {
+  clear_error();
+  return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale, logits_soft_cap,
+                  softmax_aux, aux_heads, num_sinks, kv_splits, workspace, workspace_bytes, hip_stream);
 }
 
 extern "C" SPLASH_API splash_status splash_lse_merge(const void *out_a, const float *lse_a, int32_t dtype_a,

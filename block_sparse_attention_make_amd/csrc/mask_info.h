@@ -52,6 +52,18 @@ struct DeviceCopy {
   int32_t *col_n = nullptr, *col_ent = nullptr, *col_mn = nullptr;
   int32_t *col_order = nullptr;   // key blocks by descending list length (over mask heads)
   int32_t col_w = 0;
+  // The bf16 forward's walk of the MaskInfo.  walk_kv / walk_mn: for every
+  // block row of every mask head, in order, the row's non-empty grid
+  // positions as data_next | label << 28 and mask_next (dense masks only),
+  // int32.  items[S]: per mask head and launch rank (block rows longest
+  // first, each followed by its S key splits) eight int32: block row, first
+  // walk entry, entry count, and the data_next and mask_next of the first
+  // entry (the split's non-empty positions divided into S ranges of about
+  // equal count).  items[1] is made at upload, items[S > 1] on the first
+  // call with S splits.
+  static constexpr int kMaxSplits = 8;
+  int32_t *walk_kv = nullptr, *walk_mn = nullptr;
+  int32_t *items[kMaxSplits + 1] = {};
 };
 
 // A MaskInfo with mask blocks of bq x bk (multiples of 128) as the kernels

@@ -46,6 +46,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// The two 4-element halves of a transposing LDS read joined into one MFMA
+// operand, in registers.  (Copying them through a local array made the
+// compiler place that array in LDS, one slot per thread, which needs the
+// workgroup size from the dispatch packet in host memory: microseconds of
+// latency at the start of every workgroup.)
+__device__ __forceinline__ bf16x8 join_tr_halves(s16x4 lo4, s16x4 hi4) {
+  const s16x8 c = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -113,9 +124,7 @@ __device__ __forceinline__ bf16x8 read_tr(const char *lds, int r0, int h, int dt
   const char *a1 = lds + (row0 + 8) * T::kRowBytes + ((c ^ T::swz(row0 + 8)) * 16) + within;
   const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a0));
   const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a1));
-  const s16x4 both[2] = {lo4, hi4};
-  bf16x8 r;
-  __builtin_memcpy(&r, both, 16);
+  const bf16x8 r = join_tr_halves(lo4, hi4);
   return r;
 }
 
@@ -142,9 +151,7 @@ struct TrRead {
     const char *base = lds + (r0 + 16 * h) * T::kRowBytes;
     const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(base + off_lo[dt]));
     const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(base + off_hi[dt]));
-    const s16x4 both[2] = {lo4, hi4};
-    bf16x8 r;
-    __builtin_memcpy(&r, both, 16);
+    const bf16x8 r = join_tr_halves(lo4, hi4);
     return r;
   }
 };
@@ -233,11 +240,17 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // Buffer resource over `bytes` bytes at `base`; uniform, kept in SGPRs.
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, int64_t bytes) {
   const int n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes);
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+  // The four descriptor words, built directly: base address (48 bits, stride
+  // 0), the byte count, and the data-format word.  (Going through the
+  // opaque resource type and a memcpy left a private copy that the compiler
+  // placed in LDS per thread, which reads the workgroup size from the
+  // dispatch packet in host memory at every workgroup's start.)
+  const uint64_t a = reinterpret_cast<uintptr_t>(base);
   i32x4 v;
-  __builtin_memcpy(&v, &r, sizeof(v));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  v[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  v[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu));
+  v[2] = __builtin_amdgcn_readfirstlane(n);
+  v[3] = 0x00020000;
   return v;
 }
 

@@ -49,11 +49,17 @@ constexpr float kBaseSlack = 32.f;       // headroom of the exponent base (base 
 // Buffer resource over `bytes` bytes at `base`; reads past the end return 0.
 __device__ __forceinline__ i32x4 stream_rsrc(const void *base, int64_t bytes) {
   const int n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes);
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+  // The four descriptor words, built directly: base address (48 bits, stride
+  // 0), the byte count, and the data-format word.  (Going through the
+  // opaque resource type and a memcpy left a private copy that the compiler
+  // placed in LDS per thread, which reads the workgroup size from the
+  // dispatch packet in host memory at every workgroup's start.)
+  const uint64_t a = reinterpret_cast<uintptr_t>(base);
   i32x4 v;
-  __builtin_memcpy(&v, &r, sizeof(v));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  v[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  v[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu));
+  v[2] = __builtin_amdgcn_readfirstlane(n);
+  v[3] = 0x00020000;
   return v;
 }
 

@@ -83,6 +83,17 @@ __device__ __forceinline__ void row_finish(float l_tot, float base2, float sl2, 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// The two 4-element halves of a transposing LDS read joined into one MFMA
+// operand, in registers.  (Copying them through a local array made the
+// compiler place that array in LDS, one slot per thread, which needs the
+// workgroup size from the dispatch packet in host memory: microseconds of
+// latency at the start of every workgroup.)
+__device__ __forceinline__ bf16x8 join_tr_halves(s16x4 lo4, s16x4 hi4) {
+  const s16x8 c = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
@@ -436,7 +447,6 @@ constexpr int kWThreads = 64 * kWWaves;
 constexpr int kSK = 32;            // keys per pipeline step
 constexpr int kSteps = kBK / kSK;  // steps per mask block
 constexpr int kStages = 4;         // LDS stages for K and for V
-constexpr int kWMeta = 256;        // grid positions compacted at a time
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -445,11 +455,17 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Uniform by construction; readfirstlane keeps it in SGPRs.
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, int64_t bytes) {
   const int n = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes);
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+  // The four descriptor words, built directly: base address (48 bits, stride
+  // 0), the byte count, and the data-format word.  (Going through the
+  // opaque resource type and a memcpy left a private copy that the compiler
+  // placed in LDS per thread, which reads the workgroup size from the
+  // dispatch packet in host memory at every workgroup's start.)
+  const uint64_t a = reinterpret_cast<uintptr_t>(base);
   i32x4 v;
-  __builtin_memcpy(&v, &r, sizeof(v));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  v[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  v[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu));
+  v[2] = __builtin_amdgcn_readfirstlane(n);
+  v[3] = 0x00020000;
   return v;
 }
 
@@ -626,7 +642,7 @@ struct RowState {
 // of the row (bit c <=> key c of the step).
 template <bool CAP, bool DENSE, bool MASK>
 __device__ __forceinline__ void wide_cap_mask(const FwdParams &p, f32x16 *sc, int key0, int half, const int *lo,
-                                              const int *hi, const unsigned *mword) {
+                                              const int *hi, const unsigned *mword, unsigned *seen) {
   if constexpr (CAP) {
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs)
@@ -644,6 +660,7 @@ __device__ __forceinline__ void wide_cap_mask(const FwdParams &p, f32x16 *sc, in
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
         const unsigned w = mword[qs] >> (4 * half);
+        seen[qs] |= w & 0x0f0f0f0fu;   // this lane's keys: bits 8 (v / 4) + v % 4
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           // bit c sign-extended (0 or all ones) selects the score or -inf,
@@ -663,6 +680,7 @@ __device__ __forceinline__ void wide_cap_mask(const FwdParams &p, f32x16 *sc, in
         const int b1 = min(max(hi[qs] - kb + 1, 0), kSK);   // one past the last
         const uint64_t span = b1 > b0 ? (uint64_t(1) << b1) - (uint64_t(1) << b0) : 0;
         const int w = static_cast<int>(static_cast<uint32_t>(span));
+        seen[qs] |= static_cast<unsigned>(w) & 0x0f0f0f0fu;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int c = 8 * (v / 4) + (v % 4);
@@ -694,9 +712,7 @@ __device__ __forceinline__ void wide_pv(const char *vs_lds, const bf16x8 (*pf)[2
       const char *a1 = vs_lds + (row0 + 8) * SG::kRowBytes + ((c ^ SG::swz_v(row0 + 8)) * 16) + within;
       const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a0));
       const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a1));
-      const s16x4 both[2] = {lo4, hi4};
-      bf16x8 a;
-      __builtin_memcpy(&a, both, 16);
+      const bf16x8 a = join_tr_halves(lo4, hi4);
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs)
         o[dt][qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qs][h], o[dt][qs], 0, 0, 0);
@@ -727,8 +743,7 @@ void splash_fwd_wide(const FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char k_st[kStages][SG::kBytes];
   __shared__ __attribute__((aligned(1024))) char v_st[kStages][SG::kBytes];
   __shared__ __attribute__((aligned(16))) char m_st[DENSE ? kStages : 1][kMaskBytes];
-  __shared__ int c_kvb[kWMeta], c_lab[kWMeta], c_mn[kWMeta];
-  __shared__ int wave_count[kWWaves];
+  __shared__ int wg_any[kWWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -748,11 +763,29 @@ void splash_fwd_wide(const FwdParams p) {
     bh = pid % nbh;
     rank = pid / nbh;
   }
-  const int r = p.row_order[rank];
+  // With split keys, rank counts (row, split) pairs: the splits of a row
+  // follow one another in launch order.
+  const int n_split = p.kv_splits;
+  const int split = rank % n_split;
   const int b = bh / static_cast<int>(p.Hq);
   const int hq = bh % static_cast<int>(p.Hq);
   const int hkv = hq / p.group;
   const int hm = p.hm == 1 ? 0 : hq;
+  // The workgroup's item and walk: one scalar load names the block row, the
+  // range of its walk entries (the row's non-empty grid positions in order,
+  // or this split's share of them) and the first entry's block, so the
+  // first key/value loads can go out at once.  The tables are read-only for
+  // the kernel's lifetime, so they are read through the constant address
+  // space (scalar loads, counted with the LDS operations, not with the
+  // key/value loads whose counts the pipeline waits on).
+  typedef const __attribute__((address_space(4))) int32_t *cptr;
+  const cptr items = (cptr)(p.items);
+  const cptr walk_kv = (cptr)(p.walk_kv);
+  const cptr walk_mn = (cptr)(DENSE ? p.walk_mn : p.walk_kv);
+  const int64_t item_at = ((static_cast<int64_t>(hm) * p.nq) * n_split + rank) * 8;
+  const int r = items[item_at + 0];
+  const int w_off = items[item_at + 1];
+  const int w_len = items[item_at + 2];
   const int row_in_block0 = 64 * wave + (lane & 31);      // qs = 0; qs = 1 adds 32
   const int64_t q_row0 = static_cast<int64_t>(r) * kBQ + row_in_block0;
 
@@ -763,7 +796,6 @@ void splash_fwd_wide(const FwdParams p) {
   const bool has_bits = DENSE && p.pmb_bits != nullptr;
   const i32x4 m_res = make_rsrc(has_bits ? static_cast<const void *>(p.pmb_bits) : p.k,
                                 has_bits ? p.pmb_bits_bytes : 0);
-  const int64_t meta_base = (static_cast<int64_t>(hm) * p.nq + r) * p.width;
 
   // Packed mask words of step t of partial block pb (dense masks): this
   // wave's 64 block rows, into mask stage `stage`.
@@ -779,15 +811,11 @@ void splash_fwd_wide(const FwdParams p) {
 #pragma clang diagnostic pop
   };
 
-  // The first chunk's prologue loads (K of its block's four steps, their
-  // mask words, V of the first two) go out before the Q loads and the
-  // chunk's compaction, so the three latencies overlap: data_next at the
-  // row's first grid position is the column of the row's first non-empty
-  // block (and mask_next the first partial block's mask), which is where
-  // the pipeline starts.  (A row whose first chunk is empty loads an unused
-  // block; the chunk loop checks the block before relying on these loads.)
-  const int dn_first = __builtin_amdgcn_readfirstlane(load_index(p.dn, p.dn_bytes, meta_base));
-  const int mn_first = has_bits ? __builtin_amdgcn_readfirstlane(load_index(p.mn, p.mn_bytes, meta_base)) : 0;
+  // The prologue loads of the first block (K of its four steps, their mask
+  // words, V of the first two) go out before the Q loads, so the two
+  // latencies overlap.  (A split with no block loads a block it never uses.)
+  const int dn_first = items[item_at + 3];
+  const int mn_first = has_bits ? items[item_at + 4] : 0;
 #pragma unroll
   for (int t = 0; t < kSteps; ++t) {
     issue_stage<D, false>(k_st[t], k_res, static_cast<int64_t>(dn_first) * kBK + kSK * t, wave, lane);
@@ -852,49 +880,10 @@ void splash_fwd_wide(const FwdParams p) {
   // which large logits along one dominant direction do not average away.)
   const float c2e = CAP ? 1.f : p.c2;
 
-  // Compact one chunk of the block row's grid positions: keep label > 0.
-  // Entry j + 1 is the block data_next points the pipeline at after entry j.
-  // Returns the number kept (uniform).
-  auto compact = [&](int s0) -> int {
-    const int n_meta = min(kWMeta, p.width - s0);
-    __syncthreads();
-    int lab[kWMeta / kWThreads], kv_t[kWMeta / kWThreads], mn_t[kWMeta / kWThreads];
-    int tot = 0;
-#pragma unroll
-    for (int i = 0; i < kWMeta / kWThreads; ++i) {
-      const int s = tid + kWThreads * i;
-      lab[i] = 0; kv_t[i] = 0; mn_t[i] = 0;
-      if (s < n_meta) {
-        lab[i] = load_index(p.bm, p.bm_bytes, meta_base + s0 + s);
-        kv_t[i] = load_index(p.dn, p.dn_bytes, meta_base + s0 + s);
-        if constexpr (DENSE) mn_t[i] = load_index(p.mn, p.mn_bytes, meta_base + s0 + s);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kWMeta / kWThreads; ++i) {
-      const uint64_t keep = __builtin_amdgcn_ballot_w64(lab[i] > 0);
-      if (lane == 0) wave_count[wave] = __builtin_popcountll(keep);
-      __syncthreads();
-      int off = tot;
-#pragma unroll
-      for (int w = 0; w < kWWaves; ++w) {
-        off += w < wave ? wave_count[w] : 0;
-        tot += wave_count[w];
-      }
-      if (lab[i] > 0) {
-        const int at = off + __builtin_popcountll(keep & ((uint64_t(1) << lane) - 1));
-        c_kvb[at] = kv_t[i];
-        c_lab[at] = lab[i];
-        if constexpr (DENSE) c_mn[at] = mn_t[i];
-      }
-      __syncthreads();
-    }
-    return __builtin_amdgcn_readfirstlane(tot);
-  };
-  auto key0 = [&](int u) -> int {
-    return __builtin_amdgcn_readfirstlane(c_kvb[u / kSteps]) * kBK + kSK * (u % kSteps);
-  };
-  auto label = [&](int u) -> int { return __builtin_amdgcn_readfirstlane(c_lab[u / kSteps]); };
+  // Walk entry j of this workgroup: key/value block, label, partial block.
+  auto ent_kv = [&](int j) -> int { return walk_kv[w_off + j] & 0x0fffffff; };
+  auto ent_lab = [&](int j) -> int { return static_cast<int>(static_cast<uint32_t>(walk_kv[w_off + j]) >> 28); };
+  auto ent_mn = [&](int j) -> int { return DENSE ? walk_mn[w_off + j] : 0; };
   auto mask_words = [&](int stage, unsigned *mw) {
     if constexpr (DENSE) {
 #pragma unroll
@@ -906,6 +895,11 @@ void splash_fwd_wide(const FwdParams p) {
   f32x16 o[kDT][2];        // O^T accumulators
   RowState rs;
   float base_init[2] = {-INFINITY, -INFINITY};
+  // Whether each row met an allowed key: any full block, or a set bit in a
+  // partial block's mask words (this lane's keys).  A row that met none has
+  // a zero sum and needs no recompute.
+  bool any_full = false;
+  unsigned key_bits[2] = {0u, 0u};
 
   // Exponent base of rows that have none yet: the max of the chunk's first
   // step (after cap and mask; the cap is monotonic, so capping the max gives
@@ -959,9 +953,7 @@ void splash_fwd_wide(const FwdParams p) {
       const char *a1 = vst + (row0 + 8) * SG::kRowBytes + ((c ^ SG::swz_v(row0 + 8)) * 16) + within;
       const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a0));
       const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)(a1));
-      const s16x4 both[2] = {lo4, hi4};
-      bf16x8 r;
-      __builtin_memcpy(&r, both, 16);
+      const bf16x8 r = join_tr_halves(lo4, hi4);
       return r;
     };
     bf16x8 ka[kKS], va[kPVOps];
@@ -1068,10 +1060,12 @@ void splash_fwd_wide(const FwdParams p) {
         for (int v = 0; v < 16; ++v) o[dt][qs][v] = 0.f;
     }
     rs.over = false;
+    any_full = false;
+    key_bits[0] = key_bits[1] = 0u;
 
-    for (int s0 = 0; s0 < p.width; s0 += kWMeta) {
-      const int nb = compact(s0);
-      if (nb == 0) continue;
+    do {
+      const int nb = w_len;
+      if (nb == 0) break;
       const int N = kSteps * nb;   // pipeline steps
 
       // Loads of (virtual) iteration w, counted per wave: K(w+4) with, for
@@ -1138,19 +1132,17 @@ void splash_fwd_wide(const FwdParams p) {
           qk_drain();   // the scores were formed by the step that just ended
           unsigned mw[2] = {0u, 0u};
           mask_words(stage, mw);
-          wide_cap_mask<false, DENSE, true>(p, sc, key0, half, lo, hi, mw);
+          wide_cap_mask<false, DENSE, true>(p, sc, key0, half, lo, hi, mw, key_bits);
+        } else {
+          any_full = true;
         }
       };
 
       // prologue: loads of virtual iterations -4..-1 (K(0..3), mask words of
       // steps 0..3, V(0..1), all in block 0), then S(0)
-      int kv0 = __builtin_amdgcn_readfirstlane(c_kvb[0]);
-      int mn0 = DENSE ? __builtin_amdgcn_readfirstlane(c_mn[0]) : 0;
-      int kv1 = __builtin_amdgcn_readfirstlane(c_kvb[min(1, nb - 1)]);
-      int mn1 = DENSE ? __builtin_amdgcn_readfirstlane(c_mn[min(1, nb - 1)]) : 0;
-      int lab0 = __builtin_amdgcn_readfirstlane(c_lab[0]);
-      int lab1 = __builtin_amdgcn_readfirstlane(c_lab[min(1, nb - 1)]);
-      const bool early = s0 == 0 && attempt == 0 && kv0 == dn_first && (!has_bits || mn0 == mn_first);
+      int kv0 = ent_kv(0), mn0 = ent_mn(0), lab0 = ent_lab(0);
+      int kv1 = ent_kv(min(1, nb - 1)), mn1 = ent_mn(min(1, nb - 1)), lab1 = ent_lab(min(1, nb - 1));
+      const bool early = attempt == 0 && kv0 == dn_first && (!has_bits || mn0 == mn_first);
       if (!early) {
         load_k(0, kv0, 0); load_m(0, mn0, 0);
         load_k(1, kv0, 1); load_m(1, mn0, 1);
@@ -1174,10 +1166,10 @@ void splash_fwd_wide(const FwdParams p) {
       // stage whose result is dropped, so all steps share one body.
       for (int j = 0; j < nb; ++j) {
         const bool more = j + 1 < nb;
-        // metadata of block j+2 / label of block j+2, for the next trip
-        const int kv2_v = c_kvb[min(j + 2, nb - 1)];
-        const int mn2_v = DENSE ? c_mn[min(j + 2, nb - 1)] : 0;
-        const int lab2_v = c_lab[min(j + 2, nb - 1)];
+        // walk entry j+2, for the next trip (a scalar load, one trip ahead)
+        const int kv2_v = ent_kv(min(j + 2, nb - 1));
+        const int mn2_v = ent_mn(min(j + 2, nb - 1));
+        const int lab2_v = ent_lab(min(j + 2, nb - 1));
 #pragma unroll
         for (int t = 0; t < kSteps; ++t) {
           const int u = kSteps * j + t;
@@ -1207,49 +1199,59 @@ void splash_fwd_wide(const FwdParams p) {
         kv0 = kv1;
         mn0 = mn1;
         lab0 = lab1;
-        kv1 = __builtin_amdgcn_readfirstlane(kv2_v);
-        mn1 = DENSE ? __builtin_amdgcn_readfirstlane(mn2_v) : 0;
-        lab1 = __builtin_amdgcn_readfirstlane(lab2_v);
+        kv1 = kv2_v;
+        mn1 = mn2_v;
+        lab1 = lab2_v;
       }
       // drain: PV(N-1); step N-1 = 4(nb-1) + 3 exponentiated into pf_b
       wait_vmcnt<0>();
       lds_barrier();
       wide_pv<D>(v_st[(N - 1) % kStages], pf_b, lane, half, o);
-    }
+    } while (false);
 
     // Rows whose sum outgrew kOverflowSum had a base far below their max;
-    // rows whose sum is tiny had a base far above it (or no allowed key at
-    // all).  Both run again with the exact max as base.  Workgroup-uniform
-    // decision: both waves run the same barriers.
+    // rows whose sum is tiny had a base far above it.  Both run again with
+    // the exact max as base.  A row with no allowed key (zero sum) is
+    // already final: out 0, lse -inf.  Workgroup-uniform decision: both
+    // waves run the same barriers.
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const float l_tot = pair_sum(rs.l[qs]);
-      rs.over |= attempt == 0 && (l_tot < kUnderflowSum || !(l_tot <= kOverflowSum));
+      const bool has_key = any_full || pair_max(key_bits[qs] != 0u ? 1.f : 0.f) > 0.f;
+      rs.over |= attempt == 0 && has_key && (l_tot < kUnderflowSum || !(l_tot <= kOverflowSum));
     }
-    const int any_over = __syncthreads_or(rs.over ? 1 : 0);
+    // Workgroup OR of the flag through LDS: __syncthreads_or would read the
+    // workgroup size from the dispatch packet, which sits in host memory --
+    // a load that costs microseconds at every workgroup's start.
+    if (lane == 0) wg_any[wave] = __builtin_amdgcn_ballot_w64(rs.over) != 0 ? 1 : 0;
+    __syncthreads();
+    int any_over = 0;
+#pragma unroll
+    for (int w = 0; w < kWWaves; ++w) any_over |= wg_any[w];
     if (attempt == 1 || any_over == 0) break;
 
     // Rare: some row's scores outgrew its base.  Find every row's exact max
     // (QK only, one stage at a time) and run the row again with it as base.
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) base_init[qs] = -INFINITY;
-    for (int s0 = 0; s0 < p.width; s0 += kWMeta) {
-      const int nb = compact(s0);
+    {
+      const int nb = w_len;
       for (int u = 0; u < kSteps * nb; ++u) {
+        const int key0u = ent_kv(u / kSteps) * kBK + kSK * (u % kSteps);
         wait_vmcnt<0>();
         lds_barrier();
-        issue_stage<D, false>(k_st[0], k_res, key0(u), wave, lane);
-        if (has_bits) issue_mask(__builtin_amdgcn_readfirstlane(c_mn[u / kSteps]), u % kSteps, 0);
+        issue_stage<D, false>(k_st[0], k_res, key0u, wave, lane);
+        if (has_bits) issue_mask(ent_mn(u / kSteps), u % kSteps, 0);
         wait_vmcnt<0>();
         lds_barrier();
         f32x16 sc[2];
         wide_qk<D>(k_st[0], qf, lane, half, sc);
-        unsigned mw[2] = {0u, 0u};
-        if (label(u) == 1) {
+        unsigned mw[2] = {0u, 0u}, unused[2] = {0u, 0u};
+        if (ent_lab(u / kSteps) == 1) {
           if (has_bits) mask_words(0, mw);
-          wide_cap_mask<CAP, DENSE, true>(p, sc, key0(u), half, lo, hi, mw);
+          wide_cap_mask<CAP, DENSE, true>(p, sc, key0u, half, lo, hi, mw, unused);
         } else {
-          wide_cap_mask<CAP, DENSE, false>(p, sc, key0(u), half, lo, hi, mw);
+          wide_cap_mask<CAP, DENSE, false>(p, sc, key0u, half, lo, hi, mw, unused);
         }
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
@@ -1265,6 +1267,32 @@ void splash_fwd_wide(const FwdParams p) {
   }
 
   // ---- epilogue: O / l, lse
+  if (n_split > 1) {
+    // A key split's partial result: its normalised output in float32 and its
+    // lse over its own keys (no sinks; the merge adds them).
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const int64_t q_row = q_row0 + 32 * qs;
+      const float l_tot = pair_sum(rs.l[qs]);
+      float inv, lse_row;
+      row_finish(l_tot, rs.base[qs] == -INFINITY ? 0.f : rs.base[qs], -INFINITY, inv, lse_row);
+      const int64_t prow = ((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + q_row;
+      float *po = p.part_o + prow * D;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float4 x;
+          x.x = o[dt][qs][4 * g + 0] * inv;
+          x.y = o[dt][qs][4 * g + 1] * inv;
+          x.z = o[dt][qs][4 * g + 2] * inv;
+          x.w = o[dt][qs][4 * g + 3] * inv;
+          *reinterpret_cast<float4 *>(po + 32 * dt + 8 * g + 4 * half) = x;
+        }
+      if (half == 0) p.part_lse[prow] = lse_row;
+    }
+    return;
+  }
   const float sl2 = sink_lse2(p, hq);
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
@@ -1287,11 +1315,68 @@ void splash_fwd_wide(const FwdParams p) {
   }
 }
 
+// Merge of the key splits' partial results into out and lse.  With
+// lse_s the partial lse of split s over its keys and o_s its normalised
+// output: lse = log sum_s e^(lse_s), out = sum_s e^(lse_s - lse) o_s -- the
+// flash rescaling of partial results (splash explainer, FAQ "What does ring
+// attention add on top of the splash kernel?").  Sinks join the sum once,
+// here.  A split with no allowed key has lse_s = -inf and adds nothing
+// (whatever its o_s holds).  Each thread moves 8 consecutive output
+// elements of one row; the D/8 threads of a row sit in one wavefront.
+template <int D>
+__global__ __launch_bounds__(256)
+void merge_splits(const FwdParams p) {
+  constexpr int kTPR = D / 8;                 // threads per row
+  const int64_t rows = p.B * p.Hq * p.Sq;
+  const int64_t row = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / kTPR;
+  const int c0 = (threadIdx.x % kTPR) * 8;
+  if (row >= rows) return;
+  const int64_t plane = rows;                 // rows per split
+  const int n = p.kv_splits;
+  float m = -INFINITY;
+  for (int s = 0; s < n; ++s) m = fmaxf(m, p.part_lse[s * plane + row]);
+  const int hq = static_cast<int>((row / p.Sq) % p.Hq);
+  const float sl2 = sink_lse2(p, hq);        // log2 of the sinks' sum, or -inf
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float l_sum = 0.f, lse2 = -INFINITY;
+  if (m != -INFINITY) {
+    const float m2 = m * kLog2e;
+    for (int s = 0; s < n; ++s) {
+      const float ls = p.part_lse[s * plane + row];
+      if (ls == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ls * kLog2e - m2);
+      const float4 *src = reinterpret_cast<const float4 *>(p.part_o + (s * plane + row) * D + c0);
+      const float4 x0 = src[0], x1 = src[1];
+      acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
+      acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+      l_sum += w;
+    }
+    lse2 = m2 + __builtin_amdgcn_logf(l_sum);  // log2 of the keys' sum
+  }
+  float scale = m != -INFINITY ? 1.f / l_sum : 0.f;
+  float lse2_tot = lse2;
+  if (sl2 != -INFINITY) {
+    const float mx = fmaxf(lse2, sl2);
+    lse2_tot = mx + __builtin_amdgcn_logf(__builtin_amdgcn_exp2f(lse2 - mx) + __builtin_amdgcn_exp2f(sl2 - mx));
+    if (m != -INFINITY) scale *= __builtin_amdgcn_exp2f(lse2 - lse2_tot);
+  }
+  union { __bf16 h[8]; u32x4 u; } pk;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pk.h[e] = static_cast<__bf16>(acc[e] * scale);
+  *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(p.out) + row * D + c0) = pk.u;
+  if (p.lse && c0 == 0) p.lse[row] = lse2_tot * kLn2;
+}
+
 template <int D, bool CAP, bool DENSE>
 hipError_t launch_wide(const FwdParams &p, hipStream_t stream) {
-  const int64_t blocks = p.B * p.Hq * p.nq;
+  const int64_t blocks = p.B * p.Hq * p.nq * p.kv_splits;
   hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE>), dim3(static_cast<unsigned>(blocks)), dim3(kWThreads), 0,
                      stream, p);
+  if (p.kv_splits > 1) {
+    const int64_t threads = p.B * p.Hq * p.Sq * (D / 8);
+    hipLaunchKernelGGL((merge_splits<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream,
+                       p);
+  }
   return hipGetLastError();
 }
 

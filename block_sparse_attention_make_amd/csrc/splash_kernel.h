@@ -32,9 +32,22 @@ struct FwdParams {
   const float *aux;   // device sink logits [aux_heads, num_sinks], or null
   int32_t aux_heads;  // 1 (shared), Hkv (row h / group) or Hq (row h)
   int32_t num_sinks;
+  // The bf16 kernel's walk (DeviceCopy::walk_kv / walk_mn / items): each
+  // workgroup reads its item -- block row, first walk entry, entry count,
+  // first data_next and mask_next -- and then its walk entries.
+  const int32_t *walk_kv, *walk_mn, *items;
+  // Split keys (bf16 kernel): the non-empty grid positions of each block row
+  // are divided into kv_splits ranges of about equal count, one workgroup
+  // each.  Each range writes its normalised output and lse (no sinks) to
+  // part_o [kv_splits, B, Hq, Sq, Dv] and part_lse [kv_splits, B, Hq, Sq]
+  // (float32); a second kernel merges them into out and lse and adds the
+  // sinks.
+  int32_t kv_splits;          // 1: no split, out and lse written directly
+  float *part_o, *part_lse;
 };
 
 // dtype: 0 = bf16, 1 = f32.  D in {64, 128}.  Returns hipGetLastError().
+// With p.kv_splits > 1 (bf16 only) it launches the forward and the merge.
 hipError_t launch_fwd(const FwdParams &p, int dtype, hipStream_t stream);
 
 // Backward launch parameters (bf16 only).  The forward's MaskInfo fields

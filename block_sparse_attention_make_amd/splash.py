@@ -70,6 +70,13 @@ def load_library(path=None):
     lib.splash_fwd_sinks.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32,
                                      ctypes.c_float, ctypes.c_float, vp, i32, i32, vp]
     lib.splash_fwd_sinks.restype = ctypes.c_int
+    lib.splash_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32,
+                                     ctypes.c_float, ctypes.c_float, vp, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.splash_fwd_split.restype = ctypes.c_int
+    lib.splash_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.splash_fwd_workspace_size.restype = ctypes.c_int
+    lib.splash_fwd_plan.argtypes = [vp, i64, i64, i32, ctypes.POINTER(ctypes.c_int32)]
+    lib.splash_fwd_plan.restype = ctypes.c_int
     lib.splash_make_mask_info_kv_slice.argtypes = [ctypes.POINTER(_MaskDesc), i64, i64, i32, i32,
                                                    ctypes.c_uint32, ctypes.POINTER(vp)]
     lib.splash_make_mask_info_kv_slice.restype = ctypes.c_int
@@ -229,12 +236,26 @@ def _check_buffer(name, t, shape, dtype, device):
                          f"got {t.dtype} {tuple(t.shape)}")
 
 
+def plan_kv_splits(mask_info, B, Hq, dtype_code=BF16):
+    """The library's recommended key-split count for this grid on the
+    current device (splash_fwd_plan)."""
+    lib = load_library()
+    n = ctypes.c_int32()
+    _check(lib, lib.splash_fwd_plan(mask_info.handle, int(B), int(Hq), int(dtype_code), ctypes.byref(n)))
+    return int(n.value)
+
+
 def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
-               out=None, lse=None, return_lse=True, stream=None, softmax_aux=None):
+               out=None, lse=None, return_lse=True, stream=None, softmax_aux=None, kv_splits="auto",
+               workspace=None):
     """Splash-attention forward on GPU torch tensors (contiguous BHSD).
 
     softmax_aux: optional attention-sink logits, a float32 GPU tensor [ns]
     (shared), [Hkv, ns] (query head h uses row h // (Hq // Hkv)) or [Hq, ns].
+    kv_splits: "auto" (the library's plan: splits only when the grid has
+    fewer block rows than the GPU has workgroup slots) or 1..8 -- each block
+    row's non-empty blocks divided into that many workgroups, merged by lse;
+    with more than one split a float32 workspace is allocated unless given.
     Returns (out, lse); lse is float32 [B, Hq, Sq] or None if return_lse is False.
     Launches asynchronously on `stream` (default: torch's current stream).
     """
@@ -263,20 +284,28 @@ def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
     cap = 0.0 if logits_soft_cap is None else float(logits_soft_cap)
     dt = BF16 if q.dtype == torch.bfloat16 else F32
     lse_p = lse.data_ptr() if lse is not None else None
+    aux_p, rows, ns = None, 0, 0
+    if softmax_aux is not None:
+        aux = softmax_aux
+        if not (aux.is_cuda and aux.dtype == torch.float32 and aux.is_contiguous() and aux.dim() in (1, 2)):
+            raise ValueError("softmax_aux must be a contiguous float32 GPU tensor [ns] or [rows, ns]")
+        rows, ns = (1, aux.shape[0]) if aux.dim() == 1 else (aux.shape[0], aux.shape[1])
+        aux_p = aux.data_ptr() if ns else None
     with torch.cuda.device(q.device):
-        if softmax_aux is None:
-            st = lib.splash_fwd(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                lse_p, B, Hq, Hkv, Sq, Skv, D, Dv, dt, scale, cap,
-                                ctypes.c_void_p(stream.cuda_stream))
-        else:
-            aux = softmax_aux
-            if not (aux.is_cuda and aux.dtype == torch.float32 and aux.is_contiguous() and aux.dim() in (1, 2)):
-                raise ValueError("softmax_aux must be a contiguous float32 GPU tensor [ns] or [rows, ns]")
-            rows, ns = (1, aux.shape[0]) if aux.dim() == 1 else (aux.shape[0], aux.shape[1])
-            st = lib.splash_fwd_sinks(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                      out.data_ptr(), lse_p, B, Hq, Hkv, Sq, Skv, D, Dv, dt, scale, cap,
-                                      aux.data_ptr() if ns else None, rows, ns,
-                                      ctypes.c_void_p(stream.cuda_stream))
+        splits = plan_kv_splits(mask_info, B, Hq, dt) if kv_splits == "auto" else int(kv_splits)
+        ws_p, ws_bytes = None, 0
+        if splits > 1:
+            nbytes = ctypes.c_size_t()
+            _check(lib, lib.splash_fwd_workspace_size(B, Hq, Sq, Dv, splits, ctypes.byref(nbytes)))
+            if workspace is None:
+                workspace = torch.empty(max(1, nbytes.value // 4), dtype=torch.float32, device=q.device)
+            elif not (workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous()
+                      and workspace.numel() * workspace.element_size() >= nbytes.value):
+                raise ValueError(f"workspace must be a contiguous GPU tensor of at least {nbytes.value} bytes")
+            ws_p, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        st = lib.splash_fwd_split(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse_p, B, Hq, Hkv, Sq, Skv, D, Dv, dt, scale, cap, aux_p, rows, ns, splits,
+                                  ws_p, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
     _check(lib, st)
     return out, lse
 

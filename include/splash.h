@@ -218,6 +218,51 @@ SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const void *q, c
                                           float logits_soft_cap, const float *softmax_aux,
                                           int32_t aux_heads, int32_t num_sinks, void *hip_stream);
 
+/* Split-key forward: splash_fwd_sinks with each block row's non-empty grid
+ * positions divided into kv_splits ranges of about equal count, one
+ * workgroup per range, and a second kernel that merges the ranges' results
+ * by their log-sum-exp (the rescaling of partial results that ring
+ * attention applies across devices, splash-attention explainer, FAQ "What
+ * does ring attention add on top of the splash kernel?", applied here
+ * across the workgroups of one device).  The result is the same attention;
+ * it exists so that grids with fewer block rows than the GPU has workgroup
+ * slots -- short sequences, few heads, a small batch -- still fill the
+ * machine.
+ *
+ * kv_splits: 1..8 (1 is exactly splash_fwd_sinks; workspace may then be
+ * NULL).  kv_splits > 1 runs bf16 only (float32 returns
+ * SPLASH_EUNSUPPORTED).  workspace: DEVICE scratch of at least
+ * splash_fwd_workspace_size bytes, 16-byte aligned, overwritten, owned by
+ * the caller and valid until the kernels end.  The first call with a given
+ * kv_splits on a device uploads that split's table of the MaskInfo (device
+ * memory owned by the MaskInfo); later calls allocate nothing.  Other
+ * arguments, requirements and errors as splash_fwd_sinks; a bad kv_splits
+ * or a missing / small workspace returns SPLASH_EINVAL before anything
+ * runs.  Asynchronous on hip_stream. */
+SPLASH_API splash_status splash_fwd_split(splash_mask_info *mi, const void *q, const void *k, const void *v,
+                                          void *out, float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                                          int64_t Skv, int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
+                                          float logits_soft_cap, const float *softmax_aux, int32_t aux_heads,
+                                          int32_t num_sinks, int32_t kv_splits, void *workspace,
+                                          size_t workspace_bytes, void *hip_stream);
+
+/* Workspace bytes of splash_fwd_split: float32 partial outputs and lses,
+ * kv_splits * B * Hq * Sq * (Dv + 1) * 4 (0 for kv_splits == 1).
+ * Errors: SPLASH_EINVAL for negative sizes, Dv <= 0, kv_splits outside
+ * 1..8 or a NULL bytes. */
+SPLASH_API splash_status splash_fwd_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t Dv, int32_t kv_splits,
+                                                   size_t *bytes);
+
+/* The key-split count the library recommends for this MaskInfo, batch and
+ * head count on the current device: 1 when the grid of B * Hq * (block rows)
+ * workgroups already fills the GPU's two workgroup slots per compute unit
+ * (or for float32), else enough splits to fill them, at most 8 and keeping
+ * at least two non-empty 128 x 128 blocks per split on average.  Host work
+ * and a device-attribute query only.  Errors: SPLASH_EINVAL (NULL
+ * arguments, negative sizes, unknown dtype), SPLASH_EHIP. */
+SPLASH_API splash_status splash_fwd_plan(const splash_mask_info *mi, int64_t B, int64_t Hq, int32_t dtype,
+                                         int32_t *kv_splits);
+
 /* Key-axis slice of a mask (ring attention on the splash-attention explainer
  * page, FAQ "What does ring attention add on top of the splash kernel?": the
  * MaskInfo is cut along the key axis to match the key/value shard a device

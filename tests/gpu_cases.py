@@ -18,10 +18,11 @@ def mask_rows_fn(kind, skv, left=None, right=None, chunk=None, dense=None):
 
 
 def run_gpu(q, k, v, kind, left=None, right=None, chunk=None, dense=None, cap=None, scale=None,
-            nan_fill=True, aux=None, **mi_kw):
+            nan_fill=True, aux=None, kv_splits="auto", **mi_kw):
     """splash_fwd on cuda:0 with a MaskInfo compiled for the mask (mi_kw:
-    further make_mask_info options, e.g. shrink / downcast); returns out and
-    lse as numpy arrays and the MaskInfo."""
+    further make_mask_info options, e.g. shrink / downcast) and the given key
+    splits ("auto": the library's plan); returns out and lse as numpy arrays
+    and the MaskInfo."""
     dev = torch.device("cuda:0")
     Sq, Skv = q.shape[2], k.shape[2]
     mi = make_mask_info(kind, Sq, Skv, left=left, right=right, chunk=chunk, dense=dense, **mi_kw)
@@ -32,7 +33,7 @@ def run_gpu(q, k, v, kind, left=None, right=None, chunk=None, dense=None, cap=No
         lse = torch.full((q.shape[0], q.shape[1], Sq), float("nan"), dtype=torch.float32, device=dev)
     auxd = None if aux is None else torch.as_tensor(np.asarray(aux, dtype=np.float32)).to(dev)
     out, lse = splash_fwd(qd, kd, vd, mi, softmax_scale=scale, logits_soft_cap=cap, out=out, lse=lse,
-                          softmax_aux=auxd)
+                          softmax_aux=auxd, kv_splits=kv_splits)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), mi
 

@@ -22,7 +22,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "splash_bwd", "splash_decode", "splash_decode_static", "splash_decode_workspace_size", "splash_fwd",
-        "splash_fwd_sinks",
+        "splash_fwd_plan", "splash_fwd_sinks", "splash_fwd_split", "splash_fwd_workspace_size",
         "splash_last_error", "splash_lse_merge",
         "splash_make_mask_info", "splash_make_mask_info_kv_slice", "splash_mask_info_destroy",
         "splash_mask_info_read_device", "splash_mask_info_upload", "splash_mask_info_view"])
@@ -237,3 +237,38 @@ def test_static_decode_rejects_more_than_its_scratch_before_running():
         b = dict(a, B=1, **over)
         assert lib.splash_decode_static(*b.values()) == status, (over, lib.splash_last_error())
     assert lib.splash_decode_static(*dict(a, B=0, q=0, k=0, v=0, out=0).values()) == splash.OK
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(splits=0), splash.EINVAL),
+    (dict(splits=9), splash.EINVAL),
+    (dict(splits=2, dtype=splash.F32), splash.EUNSUPPORTED),
+    (dict(splits=2, ws=None), splash.EINVAL),                 # no workspace
+    (dict(splits=2, ws_bytes=1024), splash.EINVAL),           # too small
+    (dict(splits=2, ws=24), splash.EINVAL),                   # misaligned
+    (dict(splits=2, Sq=256), splash.EINVAL),                  # MaskInfo mismatch, as splash_fwd
+])
+def test_fwd_split_validation_errors_before_launch(over, status):
+    lib = splash.load_library()
+    mi = splash.make_mask_info("causal", 512, 512)
+    a = dict(mi=mi.handle, q=16, k=16, v=16, out=16, lse=None, B=1, Hq=2, Hkv=2, Sq=512, Skv=512, D=128, Dv=128,
+             dtype=splash.BF16, scale=math.nan, cap=0.0, aux=None, aux_rows=0, ns=0, splits=1, ws=16,
+             ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    assert lib.splash_fwd_split(*a.values()) == status, lib.splash_last_error()
+    assert lib.splash_last_error()
+
+
+def test_fwd_workspace_size_and_plan_on_host():
+    lib = splash.load_library()
+    n = ctypes.c_size_t()
+    assert lib.splash_fwd_workspace_size(1, 8, 2048, 128, 4, ctypes.byref(n)) == splash.OK
+    assert n.value == 4 * 8 * 2048 * 129 * 4
+    assert lib.splash_fwd_workspace_size(1, 8, 2048, 128, 1, ctypes.byref(n)) == splash.OK and n.value == 0
+    assert lib.splash_fwd_workspace_size(1, 8, 2048, 128, 9, ctypes.byref(n)) == splash.EINVAL
+    mi = splash.make_mask_info("causal", 512, 512)
+    s = ctypes.c_int32(7)
+    # float32 never splits; no device query is needed for it
+    assert lib.splash_fwd_plan(mi.handle, 1, 2, splash.F32, ctypes.byref(s)) == splash.OK and s.value == 1
+    assert lib.splash_fwd_plan(mi.handle, 0, 2, splash.BF16, ctypes.byref(s)) == splash.OK and s.value == 1
+    assert lib.splash_fwd_plan(None, 1, 2, splash.BF16, ctypes.byref(s)) == splash.EINVAL

@@ -39,13 +39,16 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("splits", [1, "auto"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_parity(case):
+def test_small_parity(case, splits):
+    """Each case with one workgroup per block row, and with the library's
+    key-split plan (these small grids split up to 8 ways; float32 never)."""
     name, seed, B, Hq, Hkv, Sq, Skv, D, dt, mk, cap = case
     q, k, v = synthetic.make_qkv(seed, B, Hq, Hkv, Sq, Skv, D, D, dtype=dt)
-    o, l, _ = run_gpu(q, k, v, cap=cap, **mk)
+    o, l, _ = run_gpu(q, k, v, cap=cap, kv_splits=splits, **mk)
     o_ref, l_ref = oracle_full(q, k, v, cap=cap, **mk)
-    compare(o, l, o_ref, l_ref, TOL[dt], name)
+    compare(o, l, o_ref, l_ref, TOL[dt], f"{name} splits={splits}")
 
 
 @pytest.mark.parametrize("hm", [1, 4])
