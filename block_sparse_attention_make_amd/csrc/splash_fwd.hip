@@ -619,17 +619,23 @@ __device__ __forceinline__ void wide_qk(const char *ks_lds, const bf16x8 (*qf)[D
   qk_drain();   // callers read the scores right away
 }
 
-// Per-row softmax state of the wide kernel.  The exponent base of a row is
-// fixed by its first step with an allowed key and never moves afterwards, so
-// the accumulator is never rescaled inside the loop: exponentials of later,
-// larger scores simply exceed 1.  That is exact as long as they stay far
-// from the float range.  A row whose exponentials sum to more than 2^64 in
-// the end (the sum only grows, so no term ever exceeded it; an overflow to
-// +inf shows up the same way) raises `over`, and the whole row is then
-// computed again with its exact max as the base (found by a QK-only pass),
-// where every exponential is at most 1.
+// Per-row softmax state of the wide kernel: the online softmax with a lazy
+// running max.  A row's exponent base is set by its first step with an
+// allowed key and moves only when, at the end of a 128-key block, the row's
+// sum has grown past 2^40 (scores about 27 nats or more above the base):
+// then the base becomes the block's last step's max and the accumulator and
+// the sum are rescaled by 2^(old - new) -- the flash rescaling, taken rarely
+// instead of at every step, so a normal step needs no row max.  Between moves, exponentials of
+// larger scores simply exceed 1, which is exact far from the float range.
+// Two rare cases remain for a final exact pass: a row whose sum ends above
+// 2^64 (not expected after the moves; kept as a safety net) and a row whose
+// sum ends below 2^-64 with allowed keys (its first allowed step was fully
+// masked, so its base stayed 0, and all its logits lie far below 0).  Such a
+// workgroup computes every row's exact max (a QK-only pass) and runs again
+// with it as the base, where every exponential is at most 1.
 constexpr float kOverflowSum = 18446744073709551616.f;   // 2^64
 constexpr float kUnderflowSum = 5.421010862427522e-20f;   // 2^-64
+constexpr float kRescaleSum = 1099511627776.f;            // 2^40: a step's sum that moves the base
 
 struct RowState {
   float base[2];   // exponent base, base-2 units (-inf until the first allowed key)
@@ -933,7 +939,7 @@ void splash_fwd_wide(const FwdParams p) {
   // the row's fixed base; the step's row sums come from dot products of the
   // bf16 exponentials with ones (the same rounded values PV multiplies).
   auto body = [&](int u, f32x16 *sc_cur, f32x16 *sc_nxt, bf16x8 (*pf_cur)[2], bf16x8 (*pf_prv)[2],
-                  auto &&issue_loads) {
+                  auto &&issue_loads, float *step_sum) {
     constexpr int kPVOps = 2 * kDT;       // PV A operands per step: (h, dt)
     const char *kst = k_st[(u + 1) % kStages];
     const char *vst = v_st[(u + kStages - 1) % kStages];
@@ -1036,16 +1042,77 @@ void splash_fwd_wide(const FwdParams p) {
     }
     pack(7, 1);
     static_assert(kKS <= 8 && kPVOps <= 8, "slice plan assumes at most 8 operands");
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) rs.l[qs] += sum[qs];
     // Keep this step's softmax results here: without a use in this block
     // the compiler sinks the exponentials into the next step, after its
     // branches, where they no longer overlap these MFMAs.
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
+      rs.l[qs] += sum[qs];
+      step_sum[qs] = sum[qs];
+    }
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) asm volatile("" : "+v"(pf_cur[qs][h]));
       asm volatile("" : "+v"(rs.l[qs]));
+    }
+  };
+
+  // Rare: some row's sum, step u's exponentials included (scores sc, weights
+  // in pf, this lane's part of the step's sum in step_sum), has outgrown 2^40 --
+  // its scores have grown far past the base fixed at its first step.  Such a
+  // row moves its base up to the step's max (if that is higher): the output
+  // accumulator and the sum of the earlier steps are rescaled by
+  // 2^(old - new), and the step's weights and sum are formed again against
+  // the new base (with the body's own formulas, so the step's values stay
+  // consistent with the earlier ones).  Other rows keep their base (factor 1,
+  // same weights).  Whole-wave code on a uniform branch.
+  auto rebase = [&](f32x16 *sc, bf16x8 (*pf)[2], const float *step_sum) {
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      const bool need = pair_max(rs.l[qs] > kRescaleSum ? 1.f : 0.f) > 0.f;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[qs][v]);
+      mx = pair_max(mx);
+      float m2 = mx * c2e;
+      if constexpr (CAP) {
+        const float x = mx * p.c2;
+        const float e = __builtin_amdgcn_exp2f(-2.f * kLog2e * fabsf(x));
+        const float th = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+        m2 = copysignf(th, x) * p.cap_out;
+      }
+      const float old_b = rs.base[qs];
+      const float new_b = need ? fmaxf(m2, old_b) : old_b;
+      const float alpha = __builtin_amdgcn_exp2f(old_b - new_b);
+      rs.base[qs] = new_b;
+      // the earlier steps' sum (rs.l includes this step's): the subtraction
+      // errs by an ulp of the old sum, which alpha then makes negligible
+      rs.l[qs] = (rs.l[qs] - step_sum[qs]) * alpha;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][qs][v] *= alpha;
+      const float kc2 = 2.f * kLog2e * p.c2, m2cap = -2.f * p.cap_out, kr = p.cap_out - new_b;
+      float sum = 0.f;
+#pragma unroll
+      for (int v0 = 0; v0 < 16; v0 += 2) {
+        float e[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float x = sc[qs][v0 + k];
+          if constexpr (CAP) {
+            const float rr = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * kc2));
+            e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(rr, m2cap, __builtin_fmaf(x, 0x1p-100f, kr)));
+          } else {
+            e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2e, -new_b));
+          }
+        }
+        pf[qs][v0 / 8][v0 % 8] = static_cast<__bf16>(e[0]);
+        pf[qs][v0 / 8][v0 % 8 + 1] = static_cast<__bf16>(e[1]);
+        sum += e[0] + e[1];
+      }
+      rs.l[qs] += sum;
     }
   };
 
@@ -1192,7 +1259,11 @@ void splash_fwd_wide(const FwdParams p) {
             }
           };
           // body (with the refills), then the finish of S(u+1)
-          body(u, sc_cur, sc_nxt, pf_cur, pf_prv, refill);
+          float step_sum[2];
+          body(u, sc_cur, sc_nxt, pf_cur, pf_prv, refill, step_sum);
+          // once per block: a row whose sum has outgrown its base moves it
+          if (t == kSteps - 1 && __builtin_amdgcn_ballot_w64(fmaxf(rs.l[0], rs.l[1]) > kRescaleSum) != 0)
+            rebase(sc_cur, pf_cur, step_sum);
           if (t < kSteps - 1) finish(sc_nxt, lab0, t + 1, kv0 * kBK + kSK * (t + 1));
           else if (more) finish(sc_nxt, lab1, 0, kv1 * kBK);
         }

@@ -43,6 +43,7 @@ class Workload:
     soft_cap: Optional[float] = None
     block: int = 128
     seed: int = 0
+    growing: Optional[float] = None   # see make_inputs: logits growing along the keys
 
     @property
     def torch_dtype(self):
@@ -64,6 +65,13 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = ["tiny_causal_f32", "causal_mha_8k", "local_gqa_8k",
                   "chunked_gqa_16k_cap", "random_dense_2k"]
+
+# A stress input for the kernel's softmax rather than a measured workload:
+# the causal 8k shape with every row's logits growing along the keys (from
+# about 0 to about 74 at the diagonal), so an exponent base fixed early in a
+# row falls far below the row's final max.
+WORKLOADS["causal_growing_8k"] = Workload("causal_growing_8k", 1, 16, 16, 8192, 8192, 128, 128, "bf16",
+                                          MaskSpec("causal"), seed=7, growing=29.0)
 
 
 # Decode (one query per head against a key/value cache, every key allowed):
@@ -99,6 +107,14 @@ def make_inputs(w: Workload):
             dense = m[None]
         else:
             dense = random_dense_mask(rng, w.mask.dense_heads, w.Sq, w.Skv, w.mask.dense_p)
+    if w.growing is not None:
+        # q_i = a e0 + 0.05 noise, k_j = a (j / Skv) e0 + 0.05 noise: logits
+        # of row i grow along the keys up to about a^2 i / Skv / sqrt(D)
+        t = (np.arange(w.Skv, dtype=np.float32) / w.Skv)[:, None]
+        q = 0.05 * q
+        k = 0.05 * k
+        q[..., 0] += w.growing
+        k[..., 0] += w.growing * t[:, 0]
     td = w.torch_dtype
     return (torch.from_numpy(q).to(td), torch.from_numpy(k).to(td),
             torch.from_numpy(v).to(td), dense)

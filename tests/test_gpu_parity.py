@@ -159,3 +159,18 @@ def test_scores_outgrowing_base_dense_mask():
     o, l, _ = run_gpu(q, k, v, "dense", dense=dense)
     o_ref, l_ref = oracle_full(q, k, v, "dense", dense=dense)
     compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], "growing_dense")
+
+
+@pytest.mark.parametrize("kind,kw,cap,a", [
+    ("causal", {}, None, 31.0),
+    ("local", dict(left=None, right=None), None, 36.0),
+    ("chunked", dict(chunk=640), 30.0, 31.0),
+])
+def test_scores_growing_far_past_the_base_over_many_blocks(kind, kw, cap, a):
+    """Logits that grow along 2,048 keys to about a^2 / sqrt(D) (74 to 102
+    nats): the kernel's exponent base has to move up several times inside
+    each long row (the in-loop rescale), whole output against the oracle."""
+    q, k, v = _growing_scores(73, 1, 2, 2048, 128, a=a, b=a)
+    o, l, _ = run_gpu(q, k, v, kind, cap=cap, kv_splits=1, **kw)
+    o_ref, l_ref = oracle_full(q, k, v, kind, cap=cap, **kw)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], f"growing_{kind}_{a}")
