@@ -15,6 +15,14 @@ FLOPs on computed blocks = sum over (b, h) of the non-empty grid positions x
 2 * 128 * 128 * (D + Dv); softmax and masking work are not counted.  Prints
 one JSON line.
 
+Timing: --prewarm-s seconds of back-to-back steps (the clock settles), W
+warm-up steps, then K steps back to back between one HIP event pair on the
+launch stream, with a device synchronisation on both sides.  value divides
+the FLOPs by the host wall time per step; roofline.achieved divides them by
+the event time per step.  kernel_ms_median / kernel_ms_min come from 20 more
+steps timed one by one afterwards (an event between launches delays the next
+launch by several microseconds, so the timed steps carry none).
+
 --sinks N adds N attention-sink logits per key/value head (splash_fwd_sinks).
 --kv-shards P splits the keys into P equal shards and times the per-device
 part of ring attention instead: P splash_fwd calls on key-sliced MaskInfos
@@ -211,6 +219,38 @@ def prewarm(step, torch, seconds):
     return time.perf_counter() - t0
 
 
+def timed_region(step, torch, stream, steps):
+    """The timed steps: one HIP event pair on the launch stream around `steps`
+    back-to-back calls, bracketed by device synchronisations.  Returns (wall
+    seconds, event milliseconds).  An event recorded between launches holds
+    the next launch back (several microseconds per launch), so the timed
+    launches run without any; per-launch statistics come from
+    launch_stats afterwards."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, a.elapsed_time(b)
+
+
+def launch_stats(step, torch, stream, n=20):
+    """Median and minimum of n launches timed one by one (after the timed
+    region; each carries the cost of its own event pair)."""
+    import numpy as np
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return float(np.median(ms)), float(np.min(ms))
+
+
 def flops_per_block(w):
     return 2 * w.block * w.block * (w.D + w.Dv)
 
@@ -293,18 +333,11 @@ def bench_decode(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern = [a.elapsed_time(b) for a, b in ev]
+    wall, region_ms = timed_region(step, torch, stream, args.steps)
+    kav = region_ms / args.steps
+    med_ms, min_ms = launch_stats(step, torch, stream)
     kv_bytes = w.B * w.Hkv * w.Skv * (w.D + w.Dv) * 2
     ms = wall * 1e3 / args.steps
-    kav = float(np.mean(kern))
     res = {
         "metric": "splash decode K/V read bandwidth (one query per head, every key)",
         "value": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -313,7 +346,8 @@ def bench_decode(args):
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "kv_len": w.Skv,
                    "head_dim": w.D, "pass": "decode", "parallelism": "single-gpu"},
         "prewarm_s": round(prewarm_s, 2),
-        "kernel_ms_median": round(float(np.median(kern)), 5),
+        "kernel_ms_median": round(med_ms, 5),
+        "kernel_ms_min": round(min_ms, 5),
         "roofline": {"bound": "hbm", "achieved": round(kv_bytes / (kav * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(kv_bytes / (kav * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                      "traffic": measured_traffic(w.name, DECODE_SRC), "kernel": "decode_mfma + decode_merge",
@@ -462,17 +496,8 @@ def main():
     prewarm_s = prewarm(step, torch, args.prewarm_s)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    wall, region_ms = timed_region(step, torch, stream, args.steps)
+    med_ms, min_ms = launch_stats(step, torch, stream)
     cold = None
     if args.cold:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -511,7 +536,7 @@ def main():
                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                       "frac": round(m_bytes / (m_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     ms_per_step = wall * 1e3 / args.steps
-    kern_avg = float(np.mean(kern_ms))
+    kern_avg = region_ms / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops_exec / (kern_avg * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -542,8 +567,8 @@ def main():
         "blocks_skipped": blocks_total - blocks_computed,
         "blocks_total": blocks_total,
         "grid_width": int(bm.shape[-1]),
-        "kernel_ms_median": round(float(np.median(kern_ms)), 5),
-        "kernel_ms_min": round(float(np.min(kern_ms)), 5),
+        "kernel_ms_median": round(med_ms, 5),
+        "kernel_ms_min": round(min_ms, 5),
         "mask_compile_ms": round(mask_ms, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,

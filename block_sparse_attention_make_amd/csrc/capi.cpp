@@ -562,10 +562,10 @@ float resolve_scale(float softmax_scale, int64_t D) {
   return std::isnan(softmax_scale) ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(D))) : softmax_scale;
 }
 
-// Bytes of the split-key workspace: normalised partial outputs and lses,
-// float32, [S, B, Hq, Sq, Dv] then [S, B, Hq, Sq].
+// Bytes of the split-key workspace: normalised partial outputs, bf16
+// [S, B, Hq, Sq, Dv], then their lses, float32 [S, B, Hq, Sq].
 int64_t split_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t Dv, int64_t S) {
-  return S > 1 ? S * B * Hq * Sq * (Dv + 1) * 4 : 0;
+  return S > 1 ? S * B * Hq * Sq * (2 * Dv + 4) : 0;
 }
 
 splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const void *v, void *out,
@@ -617,8 +617,8 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
   p.kv_splits = kv_splits;
   p.items = dc->items[kv_splits];
   if (kv_splits > 1) {
-    p.part_o = static_cast<float *>(workspace);
-    p.part_lse = p.part_o + kv_splits * B * Hq * Sq * Dv;
+    p.part_o = workspace;
+    p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + kv_splits * B * Hq * Sq * Dv * 2);
   }
 
   hipError_t e = launch_fwd(p, dtype, static_cast<hipStream_t>(hip_stream));

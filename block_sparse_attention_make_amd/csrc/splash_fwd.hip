@@ -1339,8 +1339,10 @@ void splash_fwd_wide(const FwdParams p) {
 
   // ---- epilogue: O / l, lse
   if (n_split > 1) {
-    // A key split's partial result: its normalised output in float32 and its
-    // lse over its own keys (no sinks; the merge adds them).
+    // A key split's partial result: its normalised output in bf16 (each
+    // element at most max |v|, so the rounding errs by at most 2^-9 of that,
+    // as the final output's own rounding does) and its lse over its own
+    // keys in float32 (no sinks; the merge adds them).
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int64_t q_row = q_row0 + 32 * qs;
@@ -1348,17 +1350,15 @@ void splash_fwd_wide(const FwdParams p) {
       float inv, lse_row;
       row_finish(l_tot, rs.base[qs] == -INFINITY ? 0.f : rs.base[qs], -INFINITY, inv, lse_row);
       const int64_t prow = ((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + q_row;
-      float *po = p.part_o + prow * D;
+      __bf16 *po = static_cast<__bf16 *>(p.part_o) + prow * D;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          float4 x;
-          x.x = o[dt][qs][4 * g + 0] * inv;
-          x.y = o[dt][qs][4 * g + 1] * inv;
-          x.z = o[dt][qs][4 * g + 2] * inv;
-          x.w = o[dt][qs][4 * g + 3] * inv;
-          *reinterpret_cast<float4 *>(po + 32 * dt + 8 * g + 4 * half) = x;
+          union { __bf16 h[4]; u32x2 u; } pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk.h[e] = static_cast<__bf16>(o[dt][qs][4 * g + e] * inv);
+          *reinterpret_cast<u32x2 *>(po + 32 * dt + 8 * g + 4 * half) = pk.u;
         }
       if (half == 0) p.part_lse[prow] = lse_row;
     }
@@ -1393,8 +1393,10 @@ void splash_fwd_wide(const FwdParams p) {
 // attention add on top of the splash kernel?").  Sinks join the sum once,
 // here.  A split with no allowed key has lse_s = -inf and adds nothing
 // (whatever its o_s holds).  Each thread moves 8 consecutive output
-// elements of one row; the D/8 threads of a row sit in one wavefront.
-template <int D>
+// elements of one row; the D/8 threads of a row sit in one wavefront.  The
+// split count is a template parameter, so every load of a thread -- the S
+// lses and the S partial rows -- goes out before the first one is used.
+template <int D, int S>
 __global__ __launch_bounds__(256)
 void merge_splits(const FwdParams p) {
   constexpr int kTPR = D / 8;                 // threads per row
@@ -1403,23 +1405,30 @@ void merge_splits(const FwdParams p) {
   const int c0 = (threadIdx.x % kTPR) * 8;
   if (row >= rows) return;
   const int64_t plane = rows;                 // rows per split
-  const int n = p.kv_splits;
+  float ls[S];
+  union { u32x4 u; __bf16 h[8]; } x[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    ls[s] = p.part_lse[s * plane + row];
+    x[s].u = *reinterpret_cast<const u32x4 *>(static_cast<const __bf16 *>(p.part_o) + (s * plane + row) * D + c0);
+  }
   float m = -INFINITY;
-  for (int s = 0; s < n; ++s) m = fmaxf(m, p.part_lse[s * plane + row]);
+#pragma unroll
+  for (int s = 0; s < S; ++s) m = fmaxf(m, ls[s]);
   const int hq = static_cast<int>((row / p.Sq) % p.Hq);
   const float sl2 = sink_lse2(p, hq);        // log2 of the sinks' sum, or -inf
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float l_sum = 0.f, lse2 = -INFINITY;
   if (m != -INFINITY) {
     const float m2 = m * kLog2e;
-    for (int s = 0; s < n; ++s) {
-      const float ls = p.part_lse[s * plane + row];
-      if (ls == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(ls * kLog2e - m2);
-      const float4 *src = reinterpret_cast<const float4 *>(p.part_o + (s * plane + row) * D + c0);
-      const float4 x0 = src[0], x1 = src[1];
-      acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
-      acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      // e^(-inf) = 0 weighs an empty split out; its o_s may hold anything
+      // finite or not, so it is skipped rather than multiplied by zero
+      if (ls[s] == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ls[s] * kLog2e - m2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += w * static_cast<float>(x[s].h[e]);
       l_sum += w;
     }
     lse2 = m2 + __builtin_amdgcn_logf(l_sum);  // log2 of the keys' sum
@@ -1438,15 +1447,27 @@ void merge_splits(const FwdParams p) {
   if (p.lse && c0 == 0) p.lse[row] = lse2_tot * kLn2;
 }
 
+template <int D, int S>
+void launch_merge(const FwdParams &p, hipStream_t stream) {
+  const int64_t threads = p.B * p.Hq * p.Sq * (D / 8);
+  hipLaunchKernelGGL((merge_splits<D, S>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream,
+                     p);
+}
+
 template <int D, bool CAP, bool DENSE>
 hipError_t launch_wide(const FwdParams &p, hipStream_t stream) {
   const int64_t blocks = p.B * p.Hq * p.nq * p.kv_splits;
   hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE>), dim3(static_cast<unsigned>(blocks)), dim3(kWThreads), 0,
                      stream, p);
-  if (p.kv_splits > 1) {
-    const int64_t threads = p.B * p.Hq * p.Sq * (D / 8);
-    hipLaunchKernelGGL((merge_splits<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream,
-                       p);
+  switch (p.kv_splits) {   // 1..8, checked by the caller
+    case 1: break;
+    case 2: launch_merge<D, 2>(p, stream); break;
+    case 3: launch_merge<D, 3>(p, stream); break;
+    case 4: launch_merge<D, 4>(p, stream); break;
+    case 5: launch_merge<D, 5>(p, stream); break;
+    case 6: launch_merge<D, 6>(p, stream); break;
+    case 7: launch_merge<D, 7>(p, stream); break;
+    default: launch_merge<D, 8>(p, stream); break;
   }
   return hipGetLastError();
 }

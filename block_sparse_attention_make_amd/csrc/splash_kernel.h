@@ -38,12 +38,13 @@ struct FwdParams {
   const int32_t *walk_kv, *walk_mn, *items;
   // Split keys (bf16 kernel): the non-empty grid positions of each block row
   // are divided into kv_splits ranges of about equal count, one workgroup
-  // each.  Each range writes its normalised output and lse (no sinks) to
-  // part_o [kv_splits, B, Hq, Sq, Dv] and part_lse [kv_splits, B, Hq, Sq]
-  // (float32); a second kernel merges them into out and lse and adds the
-  // sinks.
+  // each.  Each range writes its normalised output to part_o
+  // [kv_splits, B, Hq, Sq, Dv] (bf16) and its lse (no sinks) to part_lse
+  // [kv_splits, B, Hq, Sq] (float32); a second kernel merges them into out
+  // and lse and adds the sinks.
   int32_t kv_splits;          // 1: no split, out and lse written directly
-  float *part_o, *part_lse;
+  void *part_o;
+  float *part_lse;
 };
 
 // dtype: 0 = bf16, 1 = f32.  D in {64, 128}.  Returns hipGetLastError().

@@ -246,8 +246,9 @@ SPLASH_API splash_status splash_fwd_split(splash_mask_info *mi, const void *q, c
                                           int32_t num_sinks, int32_t kv_splits, void *workspace,
                                           size_t workspace_bytes, void *hip_stream);
 
-/* Workspace bytes of splash_fwd_split: float32 partial outputs and lses,
- * kv_splits * B * Hq * Sq * (Dv + 1) * 4 (0 for kv_splits == 1).
+/* Workspace bytes of splash_fwd_split: the ranges' normalised outputs in
+ * bf16 and their lses in float32, kv_splits * B * Hq * Sq * (2 * Dv + 4)
+ * (0 for kv_splits == 1).
  * Errors: SPLASH_EINVAL for negative sizes, Dv <= 0, kv_splits outside
  * 1..8 or a NULL bytes. */
 SPLASH_API splash_status splash_fwd_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t Dv, int32_t kv_splits,

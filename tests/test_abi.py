@@ -263,7 +263,7 @@ def test_fwd_workspace_size_and_plan_on_host():
     lib = splash.load_library()
     n = ctypes.c_size_t()
     assert lib.splash_fwd_workspace_size(1, 8, 2048, 128, 4, ctypes.byref(n)) == splash.OK
-    assert n.value == 4 * 8 * 2048 * 129 * 4
+    assert n.value == 4 * 8 * 2048 * (2 * 128 + 4)
     assert lib.splash_fwd_workspace_size(1, 8, 2048, 128, 1, ctypes.byref(n)) == splash.OK and n.value == 0
     assert lib.splash_fwd_workspace_size(1, 8, 2048, 128, 9, ctypes.byref(n)) == splash.EINVAL
     mi = splash.make_mask_info("causal", 512, 512)
