@@ -540,7 +540,10 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops_exec / (kern_avg * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = measured_traffic(w.name)
+    # the committed traffic summaries were taken with the workload's default launch
+    default_launch = (args.kv_splits == "auto" and not args.sinks and P == 1 and not args.backward
+                      and args.block_q == w.block and args.block_kv == w.block)
+    traffic = measured_traffic(w.name) if default_launch else None
 
     res = {
         "metric": ("splash bwd TFLOP/s on computed blocks (5 products per block)" if args.backward else
