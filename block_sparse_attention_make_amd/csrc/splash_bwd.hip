@@ -67,16 +67,25 @@ __device__ __forceinline__ int load_index(const void *p, int bytes, int64_t i) {
 }
 
 // A 128 x D bf16 tile in LDS; 16-byte chunk c of row r sits at chunk
-// c ^ swz(r), which spreads the row reads of 16 consecutive rows over all
-// banks and keeps the transposing reads (4 rows x 4 chunks) apart too.
+// c ^ swz(r).  Each tile is read both ways, so the swizzle serves both:
+//  * row reads (ds_read_b128, 16 lanes on 16 consecutive rows, one logical
+//    chunk): swz is a bijection on the row bits that share a bank line
+//    (r mod 16 for D = 128, r / 2 mod 8 for D = 64), so the 16 lanes land
+//    on 16 different chunk slots;
+//  * transposing reads (ds_read_b64_tr_b16, 32 lanes on 4 consecutive rows
+//    x 4 consecutive chunks): rows 4k .. 4k + 3 get different high chunk
+//    bits (the bits above the 4 chunks' span), so the 16 chunks the 32
+//    lanes touch are all different as well.
+// The plain row & 15 kept the 4 rows' chunks inside one 4-chunk span: 4-way
+// conflicts on every transposing read.
 template <int D>
 struct BTile {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = kRowBytes / 16;
   static constexpr int kBytes = kBlk * kRowBytes;
   __device__ static int swz(int row) {
-    if constexpr (kChunks >= 16) return row & 15;
-    else return (row >> 1) & 7;
+    if constexpr (kChunks >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   }
 };
 
