@@ -1338,51 +1338,62 @@ void splash_fwd_wide(const FwdParams p) {
   }
 
   // ---- epilogue: O / l, lse
-  if (n_split > 1) {
-    // A key split's partial result: its normalised output in bf16 (each
-    // element at most max |v|, so the rounding errs by at most 2^-9 of that,
-    // as the final output's own rounding does) and its lse over its own
-    // keys in float32 (no sinks; the merge adds them).
+  // The O^T registers hold a lane's row in 4-element pieces 8 columns apart,
+  // so a direct store would scatter 64 rows' pieces over one instruction
+  // (64 partial-line writes).  Each wave instead writes its 64 normalised
+  // bf16 rows into its half of the K stages (16-byte chunks swizzled by row)
+  // and stores them back 16 bytes per lane, whole rows per instruction.  Both
+  // waves are past their last K-stage read (the barrier that ends the
+  // attempt loop); a workgroup with no block still has its prologue loads in
+  // flight into those stages, hence the wait.
+  wait_vmcnt<0>();
+  float inv[2], lse_row[2];
+  const float sl2 = n_split > 1 ? -INFINITY : sink_lse2(p, hq);   // the merge adds a split's sinks
+#pragma unroll
+  for (int qs = 0; qs < 2; ++qs)
+    row_finish(pair_sum(rs.l[qs]), rs.base[qs] == -INFINITY ? 0.f : rs.base[qs], sl2, inv[qs], lse_row[qs]);
+  {
+    constexpr int kRB = SG::kRowBytes;
+    constexpr int kChunks = kRB / 16;
+    auto swz_o = [](int rr) { return rr & (kChunks - 1); };
+    char *st = &k_st[0][0] + wave * 64 * kRB;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-      const int64_t q_row = q_row0 + 32 * qs;
-      const float l_tot = pair_sum(rs.l[qs]);
-      float inv, lse_row;
-      row_finish(l_tot, rs.base[qs] == -INFINITY ? 0.f : rs.base[qs], -INFINITY, inv, lse_row);
-      const int64_t prow = ((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + q_row;
-      __bf16 *po = static_cast<__bf16 *>(p.part_o) + prow * D;
+      const int rr = (lane & 31) + 32 * qs;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           union { __bf16 h[4]; u32x2 u; } pk;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pk.h[e] = static_cast<__bf16>(o[dt][qs][4 * g + e] * inv);
-          *reinterpret_cast<u32x2 *>(po + 32 * dt + 8 * g + 4 * half) = pk.u;
+          for (int e = 0; e < 4; ++e) pk.h[e] = static_cast<__bf16>(o[dt][qs][4 * g + e] * inv[qs]);
+          *reinterpret_cast<u32x2 *>(st + rr * kRB + (((4 * dt + g) ^ swz_o(rr)) * 16) + 8 * half) = pk.u;
         }
-      if (half == 0) p.part_lse[prow] = lse_row;
     }
-    return;
+    // this wave's rows only: its LDS writes and reads complete in order
+    const int64_t row_w = static_cast<int64_t>(r) * kBQ + 64 * wave;   // the wave's first row
+    char *dst = n_split > 1
+        ? reinterpret_cast<char *>(static_cast<__bf16 *>(p.part_o) +
+                                   (((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + row_w) * D)
+        : reinterpret_cast<char *>(static_cast<__bf16 *>(p.out) +
+                                   ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + row_w) * D);
+    constexpr int kRowsPer = 1024 / kRB;   // rows per instruction
+#pragma unroll
+    for (int i = 0; i < 64 / kRowsPer; ++i) {
+      const int rr = kRowsPer * i + lane / kChunks, c = lane % kChunks;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(st + rr * kRB + ((c ^ swz_o(rr)) * 16));
+      *reinterpret_cast<u32x4 *>(dst + rr * kRB + c * 16) = v;
+    }
   }
-  const float sl2 = sink_lse2(p, hq);
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
     const int64_t q_row = q_row0 + 32 * qs;
-    const float l_tot = pair_sum(rs.l[qs]);
-    float inv, lse_row;
-    row_finish(l_tot, rs.base[qs] == -INFINITY ? 0.f : rs.base[qs], sl2, inv, lse_row);
-    __bf16 *og = static_cast<__bf16 *>(p.out) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * dt + 8 * g + 4 * half;
-        union { __bf16 h[4]; u32x2 u; } pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk.h[e] = static_cast<__bf16>(o[dt][qs][4 * g + e] * inv);
-        *reinterpret_cast<u32x2 *>(og + col) = pk.u;
-      }
-    if (p.lse && half == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] = lse_row;
+    if (half == 0) {
+      if (n_split > 1)
+        p.part_lse[((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + q_row] = lse_row[qs];
+      else if (p.lse)
+        p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] = lse_row[qs];
+    }
   }
 }
 
