@@ -207,10 +207,18 @@ __device__ __forceinline__ void capped(float x, float kc2, float cap_out, float 
 }
 
 // Store a transposed fp32 accumulator (rows d, columns = the wave's 32 rows)
-// as rows of a [*, D] bf16 array, times `mul`.
+// as rows of a [*, D] bf16 array, times `mul`, through LDS: the accumulator
+// layout gives a lane 4-element pieces
+// of its row 8 columns apart, so direct stores scatter 32 rows over one
+// instruction.  The wave writes its 32 rows (bf16) into `lds` (32 x D, its
+// own region; 16-byte chunks swizzled by row) and stores them back 16 bytes
+// per lane, whole rows per instruction.  The wave's LDS writes and reads
+// complete in order.
 template <int D>
-__device__ __forceinline__ void store_t(__bf16 *g, const f32x16 (&acc)[D / 32], float mul, int lane, int half) {
-  __bf16 *row = g + static_cast<int64_t>(lane & 31) * D;
+__device__ __forceinline__ void store_t_rows(char *lds, __bf16 *g, const f32x16 (&acc)[D / 32], float mul, int lane,
+                                             int half) {
+  constexpr int kRB = D * 2, kChunks = kRB / 16;
+  const int rr = lane & 31;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -218,8 +226,15 @@ __device__ __forceinline__ void store_t(__bf16 *g, const f32x16 (&acc)[D / 32], 
       union { __bf16 h[4]; u32x2 u; } pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e) pk.h[e] = static_cast<__bf16>(acc[dt][4 * q4 + e] * mul);
-      *reinterpret_cast<u32x2 *>(row + 32 * dt + 8 * q4 + 4 * half) = pk.u;
+      *reinterpret_cast<u32x2 *>(lds + rr * kRB + (((4 * dt + q4) ^ (rr & (kChunks - 1))) * 16) + 8 * half) = pk.u;
     }
+  constexpr int kRowsPer = 1024 / kRB;
+#pragma unroll
+  for (int i = 0; i < 32 / kRowsPer; ++i) {
+    const int r2 = kRowsPer * i + lane / kChunks, c = lane % kChunks;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + r2 * kRB + ((c ^ (r2 & (kChunks - 1))) * 16));
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(g) + r2 * kRB + c * 16) = v;
+  }
 }
 
 // ---- delta: di = <dout_i, out_i> ------------------------------------------
@@ -601,8 +616,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
     e = e2;
     n = n2;
   }
-  store_t<D>(static_cast<__bf16 *>(p.dk) + kv_off, dk, p.scale, lane, half);
-  store_t<D>(static_cast<__bf16 *>(p.dv) + kv_off, dv, 1.f, lane, half);
+  // Every wave is past the loop's last barrier and no load is in flight, so
+  // the tiles are free: each wave stages its dk rows and then its dv rows in
+  // its own 2 x 32 rows.
+  char *st = &qdo_t[0][0][0] + wave * 64 * D * 2;
+  wait_all_loads();
+  store_t_rows<D>(st, static_cast<__bf16 *>(p.dk) + kv_off, dk, p.scale, lane, half);
+  store_t_rows<D>(st + 32 * D * 2, static_cast<__bf16 *>(p.dv) + kv_off, dv, 1.f, lane, half);
 }
 
 // ---- query-major kernel: dQ -----------------------------------------------
@@ -758,7 +778,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
     buf ^= 1;
     sl = sl2;
   }
-  store_t<D>(static_cast<__bf16 *>(p.dq) + q0, dq, p.scale, lane, half);
+  // every wave is past the loop's last barrier
+  wait_all_loads();
+  store_t_rows<D>(&kv_t[0][0][0] + wave * 32 * D * 2, static_cast<__bf16 *>(p.dq) + q0, dq, p.scale, lane, half);
 }
 
 template <int D, bool CAP, bool DENSE>
