@@ -54,6 +54,16 @@ def test_split_parity(case, splits):
     compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], f"{name} splits={splits}")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_split_head_dim_64(splits):
+    """D = 64: half-width rows through the output staging and the merge."""
+    q, k, v = synthetic.make_qkv(405, 1, 4, 2, 768, 768, 64, 64)
+    mk = dict(kind="local", left=200, right=0)
+    o, l = _run(q, k, v, mk, splits)
+    o_ref, l_ref = oracle_by_block_rows(q, k, v, **mk)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], f"d64 splits={splits}")
+
+
 @pytest.mark.parametrize("hm", [1, 4])
 @pytest.mark.parametrize("splits", [2, 5])
 def test_split_dense_with_empty_rows(hm, splits):
