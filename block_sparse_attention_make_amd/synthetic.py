@@ -26,6 +26,7 @@ class MaskSpec:
     chunk: Optional[int] = None     # chunked: chunk length
     dense_p: Optional[float] = None  # dense random: probability of keep
     dense_heads: int = 1            # dense random: Hm
+    empty_every: Optional[int] = None   # dense random: every n-th query row allows no key
 
 
 @dataclass(frozen=True)
@@ -73,6 +74,11 @@ WORKLOAD_ORDER = ["tiny_causal_f32", "causal_mha_8k", "local_gqa_8k",
 WORKLOADS["causal_growing_8k"] = Workload("causal_growing_8k", 1, 16, 16, 8192, 8192, 128, 128, "bf16",
                                           MaskSpec("causal"), seed=7, growing=29.0)
 
+# The random dense workload with every 16th query row allowing no key (as
+# padding or document masks produce): such rows must cost nothing extra.
+WORKLOADS["dense_empty_rows_2k"] = Workload("dense_empty_rows_2k", 1, 8, 8, 2048, 2048, 128, 128, "bf16",
+                                            MaskSpec("dense", dense_p=0.1, empty_every=16), seed=8)
+
 
 # Decode (one query per head against a key/value cache, every key allowed):
 # a GQA serving shape, measured against HBM bandwidth.
@@ -104,6 +110,8 @@ def make_inputs(w: Workload):
             m = rng.random((w.Sq, w.Skv)) < w.mask.dense_p
             n = min(w.Sq, w.Skv)
             m[np.arange(n), np.arange(n)] = True
+            if w.mask.empty_every:
+                m[::w.mask.empty_every] = False
             dense = m[None]
         else:
             dense = random_dense_mask(rng, w.mask.dense_heads, w.Sq, w.Skv, w.mask.dense_p)

@@ -40,6 +40,20 @@ def test_full_size_whole_output(name):
     compare(o, l, o_ref, l_ref, TOL[w.torch_dtype], f"{name} (all {o.shape[0] * o.shape[1] * o.shape[2]} rows)")
 
 
+def test_dense_empty_rows_whole_output():
+    """dense_empty_rows_2k as bench.py launches it (split keys): every 16th
+    row allows no key and must come out as 0 with lse -inf, the rest as the
+    oracle's."""
+    w = synthetic.WORKLOADS["dense_empty_rows_2k"]
+    q, k, v, dense = synthetic.make_inputs(w)
+    kw = _mask_kw(w, dense)
+    o, l, mi = run_gpu(q, k, v, cap=w.soft_cap, **kw)
+    assert np.isneginf(l[:, :, ::16]).all() and np.isfinite(l[:, :, 1::16]).all()
+    assert (o[:, :, ::16] == 0).all()
+    o_ref, l_ref = oracle_by_block_rows(q, k, v, cap=w.soft_cap, **kw)
+    compare(o, l, o_ref, l_ref, TOL[w.torch_dtype], f"{w.name} (all rows)")
+
+
 @pytest.mark.parametrize("name", synthetic.WORKLOAD_ORDER)
 def test_device_mask_info_bit_exact(name):
     w = synthetic.WORKLOADS[name]
