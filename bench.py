@@ -378,6 +378,9 @@ def main():
     ap.add_argument("--kv-shards", type=int, default=1, help="time the key/value-sharded path")
     ap.add_argument("--backward", action="store_true", help="time splash_bwd")
     ap.add_argument("--decode", action="store_true", help="time splash_decode on a decode workload")
+    ap.add_argument("--heads-per-wg", type=int, default=0, choices=(0, 1, 2),
+                    help="query heads per workgroup: 0 the library's choice, 1, or 2 (two heads of a GQA group "
+                         "sharing each K/V stage)")
     ap.add_argument("--kv-splits", default="auto",
                     help="key splits per block row: auto (the library's plan) or 1..8")
     ap.add_argument("--block-q", type=int, default=128, help="mask block rows (a multiple of 128)")
@@ -440,6 +443,7 @@ def main():
         flops_dense = w.B * w.Hq * w.Sq * w.Skv * 5 * 2 * w.D
 
     from block_sparse_attention_make_amd.splash import plan_kv_splits
+    from block_sparse_attention_make_amd.splash import plan_heads_per_workgroup
     splits = (plan_kv_splits(mi, w.B, w.Hq, 0 if w.dtype == "bf16" else 1) if args.kv_splits == "auto"
               else int(args.kv_splits))
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
@@ -491,7 +495,7 @@ def main():
             splash_fwd_kv_sharded(qd, ks, vs, shard_mis, logits_soft_cap=w.soft_cap, stream=stream)
         else:
             splash_fwd(qd, kd, vd, mi, logits_soft_cap=w.soft_cap, out=out, lse=lse, stream=stream,
-                       softmax_aux=aux, kv_splits=splits, workspace=split_ws)
+                       softmax_aux=aux, kv_splits=splits, workspace=split_ws, heads_per_workgroup=args.heads_per_wg)
 
     prewarm_s = prewarm(step, torch, args.prewarm_s)
     for _ in range(args.warmup):
@@ -541,7 +545,8 @@ def main():
     achieved = flops_exec / (kern_avg * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     # the committed traffic summaries were taken with the workload's default launch
-    default_launch = (args.kv_splits == "auto" and not args.sinks and P == 1 and not args.backward
+    default_launch = (args.kv_splits == "auto" and args.heads_per_wg == 0 and not args.sinks and P == 1
+                      and not args.backward
                       and args.block_q == w.block and args.block_kv == w.block)
     traffic = measured_traffic(w.name) if default_launch else None
 
@@ -563,6 +568,8 @@ def main():
                    "seq_len": w.Sq, "head_dim": w.D, "mask": m.kind, "block": w.block,
                    "soft_cap": w.soft_cap, "parallelism": "single-gpu",
                    "sinks_per_kv_head": args.sinks, "kv_shards": P, "kv_splits": splits,
+                   "heads_per_workgroup": (args.heads_per_wg or plan_heads_per_workgroup(
+                       mi, w.B, w.Hq, w.Hkv, w.D, 0 if w.dtype == "bf16" else 1, splits)),
                    "mask_block": [args.block_q, args.block_kv], "pass": "backward" if args.backward else "forward"},
         "prewarm_s": round(prewarm_s, 2),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),

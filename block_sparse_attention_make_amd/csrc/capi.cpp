@@ -568,15 +568,36 @@ int64_t split_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t Dv, int
   return S > 1 ? S * B * Hq * Sq * (2 * Dv + 4) : 0;
 }
 
+// Whether two query heads of a GQA group can share a workgroup (and its K/V
+// stages): the bf16 kernel at D = 128 with a computable mask and one mask
+// head (so both heads walk the same blocks) and an even group size (so the
+// pair shares its K/V head).
+bool head_pairs_possible(const splash_mask_info *mi, int64_t Hq, int64_t Hkv, int64_t D, int32_t dtype) {
+  return dtype == SPLASH_BF16 && D == 128 && mi->kind != SPLASH_MASK_DENSE && mi->num_heads == 1 && Hkv > 0 &&
+         (Hq / Hkv) % 2 == 0;
+}
+
+// The library's choice of heads per workgroup: pairs where possible, as long
+// as the pairs still give each CU a workgroup (a pair fills a CU alone).
+int32_t auto_heads_per_wg(const splash_mask_info *mi, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int32_t dtype,
+                          int32_t kv_splits) {
+  if (!head_pairs_possible(mi, Hq, Hkv, D, dtype)) return 1;
+  return B * (Hq / 2) * walk_of(mi).nq * kv_splits >= 256 ? 2 : 1;
+}
+
 splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const void *v, void *out,
                        float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
                        int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
                        float logits_soft_cap, const float *aux, int32_t aux_heads,
-                       int32_t num_sinks, int32_t kv_splits, void *workspace, size_t workspace_bytes,
-                       void *hip_stream) {
+                       int32_t num_sinks, int32_t kv_splits, int32_t heads_per_wg, void *workspace,
+                       size_t workspace_bytes, void *hip_stream) {
   // ---- validation: nothing below launches or allocates until all passes ----
   splash_status st = validate_call(mi, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale);
   if (st != SPLASH_OK) return st;
+  if (heads_per_wg < 0 || heads_per_wg > 2) return fail(SPLASH_EINVAL, "heads_per_workgroup must be 0, 1 or 2");
+  if (heads_per_wg == 2 && !head_pairs_possible(mi, Hq, Hkv, D, dtype))
+    return fail(SPLASH_EUNSUPPORTED, "two heads per workgroup need bf16, D = 128, a computable mask with one "
+                                     "mask head and an even GQA group");
   if (kv_splits < 1 || kv_splits > DeviceCopy::kMaxSplits)
     return fail(SPLASH_EINVAL, "kv_splits must be in 1..8");
   if (kv_splits > 1 && dtype != SPLASH_BF16)
@@ -616,6 +637,8 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
   p.num_sinks = num_sinks;
   p.kv_splits = kv_splits;
   p.items = dc->items[kv_splits];
+  const int32_t hpw = heads_per_wg != 0 ? heads_per_wg : auto_heads_per_wg(mi, B, Hq, Hkv, D, dtype, kv_splits);
+  p.head_pairs = hpw == 2 ? 1 : 0;
   if (kv_splits > 1) {
     p.part_o = workspace;
     p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + kv_splits * B * Hq * Sq * Dv * 2);
@@ -636,7 +659,7 @@ extern "C" SPLASH_API splash_status splash_fwd(splash_mask_info *mi, const void 
                                                void *hip_stream) {
   clear_error();
   return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale,
-                  logits_soft_cap, nullptr, 0, 0, 1, nullptr, 0, hip_stream);
+                  logits_soft_cap, nullptr, 0, 0, 1, 0, nullptr, 0, hip_stream);
 }
 
 extern "C" SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const void *q, const void *k,
@@ -648,7 +671,7 @@ extern "C" SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const
                                                      int32_t num_sinks, void *hip_stream) {
   clear_error();
   return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale,
-                  logits_soft_cap, softmax_aux, aux_heads, num_sinks, 1, nullptr, 0, hip_stream);
+                  logits_soft_cap, softmax_aux, aux_heads, num_sinks, 1, 0, nullptr, 0, hip_stream);
 }
 
 extern "C" SPLASH_API splash_status splash_fwd_workspace_size(int64_t B, int64_t Hq, int64_t Sq, int64_t Dv,
@@ -699,7 +722,32 @@ extern "C" SPLASH_API splash_status splash_fwd_split(splash_mask_info *mi, const
                                                      void *hip_stream) {
   clear_error();
   return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale, logits_soft_cap,
-                  softmax_aux, aux_heads, num_sinks, kv_splits, workspace, workspace_bytes, hip_stream);
+                  softmax_aux, aux_heads, num_sinks, kv_splits, 0, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" SPLASH_API splash_status splash_fwd_tiled(splash_mask_info *mi, const void *q, const void *k,
+                                                     const void *v, void *out, float *lse, int64_t B, int64_t Hq,
+                                                     int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D, int64_t Dv,
+                                                     int32_t dtype, float softmax_scale, float logits_soft_cap,
+                                                     const float *softmax_aux, int32_t aux_heads, int32_t num_sinks,
+                                                     int32_t kv_splits, int32_t heads_per_workgroup, void *workspace,
+                                                     size_t workspace_bytes, void *hip_stream) {
+  clear_error();
+  return fwd_impl(mi, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale, logits_soft_cap,
+                  softmax_aux, aux_heads, num_sinks, kv_splits, heads_per_workgroup, workspace, workspace_bytes,
+                  hip_stream);
+}
+
+extern "C" SPLASH_API splash_status splash_fwd_heads_per_workgroup(const splash_mask_info *mi, int64_t B,
+                                                                   int64_t Hq, int64_t Hkv, int64_t D, int32_t dtype,
+                                                                   int32_t kv_splits, int32_t *heads) {
+  clear_error();
+  if (!mi || !heads) return fail(SPLASH_EINVAL, "NULL argument");
+  if (B < 0 || Hq < 0 || Hkv <= 0) return fail(SPLASH_EINVAL, "bad head counts");
+  if (dtype != SPLASH_BF16 && dtype != SPLASH_F32) return fail(SPLASH_EINVAL, "unknown dtype");
+  if (kv_splits < 1 || kv_splits > DeviceCopy::kMaxSplits) return fail(SPLASH_EINVAL, "kv_splits must be in 1..8");
+  *heads = auto_heads_per_wg(mi, B, Hq, Hkv, D, dtype, kv_splits);
+  return SPLASH_OK;
 }
 
 extern "C" SPLASH_API splash_status splash_lse_merge(const void *out_a, const float *lse_a, int32_t dtype_a,

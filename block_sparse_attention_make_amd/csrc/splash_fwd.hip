@@ -484,12 +484,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // One 32-key stage of K or V: 32 rows of D bf16, 16-byte chunks XOR-swizzled
 // per row (the swizzles of the 128-row tiles above).
-template <int D>
+template <int D, int W = kWWaves>
 struct Stage {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = kRowBytes / 16;
   static constexpr int kBytes = kSK * kRowBytes;
-  static constexpr int kInsts = kBytes / 1024 / kWWaves;  // 1 KiB loads per wave per stage
+  static constexpr int kInsts = kBytes / 1024 / W;  // 1 KiB loads per wave per stage (W waves share it)
   __device__ static int swz_k(int row) {
     if constexpr (kChunks >= 16) return row & 15;
     else return (row >> 1) & 7;
@@ -517,9 +517,9 @@ struct Stage {
 // compiler computes for its own loads stay correct (loads retire in order, so
 // extra loads in flight only make them more conservative).  M0 is written in
 // the same statement as the loads that read it.
-template <int D, bool IS_V>
+template <int D, bool IS_V, int W = kWWaves>
 __device__ __forceinline__ uint32_t stage_voff(int wave, int lane, int i) {
-  using SG = Stage<D>;
+  using SG = Stage<D, W>;
   constexpr int kRowsPerSeg = 1024 / SG::kRowBytes;
   constexpr int kLanesPerRow = SG::kChunks;
   const int seg = wave * SG::kInsts + i;
@@ -529,9 +529,9 @@ __device__ __forceinline__ uint32_t stage_voff(int wave, int lane, int i) {
   return static_cast<uint32_t>((lane / kLanesPerRow) * SG::kRowBytes + c * 16);
 }
 
-template <int D, bool IS_V>
+template <int D, bool IS_V, int W = kWWaves>
 __device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, int wave, int lane) {
-  using SG = Stage<D>;
+  using SG = Stage<D, W>;
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) char *)(lds + wave * SG::kInsts * 1024)));
   const uint32_t soff = static_cast<uint32_t>(row0 * SG::kRowBytes) + wave * SG::kInsts * 1024;
@@ -544,8 +544,8 @@ __device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, 
         "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
         "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
         "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
-        :: "s"(m0), "v"(stage_voff<D, IS_V>(wave, lane, 0)), "v"(stage_voff<D, IS_V>(wave, lane, 1)),
-           "v"(stage_voff<D, IS_V>(wave, lane, 2)), "v"(stage_voff<D, IS_V>(wave, lane, 3)), "s"(res), "s"(soff)
+        :: "s"(m0), "v"(stage_voff<D, IS_V, W>(wave, lane, 0)), "v"(stage_voff<D, IS_V, W>(wave, lane, 1)),
+           "v"(stage_voff<D, IS_V, W>(wave, lane, 2)), "v"(stage_voff<D, IS_V, W>(wave, lane, 3)), "s"(res), "s"(soff)
         : "memory", "m0");
   } else {
     static_assert(SG::kInsts == 2, "stage loads per wave");
@@ -553,7 +553,7 @@ __device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, 
         "s_mov_b32 m0, %0\n\t"
         "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
         "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
-        :: "s"(m0), "v"(stage_voff<D, IS_V>(wave, lane, 0)), "v"(stage_voff<D, IS_V>(wave, lane, 1)), "s"(res),
+        :: "s"(m0), "v"(stage_voff<D, IS_V, W>(wave, lane, 0)), "v"(stage_voff<D, IS_V, W>(wave, lane, 1)), "s"(res),
            "s"(soff)
         : "memory", "m0");
   }
@@ -562,9 +562,9 @@ __device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, 
 
 // One segment (1 KiB, segment I of this wave's share) of a stage, for
 // spreading a stage's loads over several slices of a step.
-template <int D, bool IS_V, int I>
+template <int D, bool IS_V, int I, int W = kWWaves>
 __device__ __forceinline__ void issue_seg(char *lds, i32x4 res, int64_t row0, int wave, int lane) {
-  using SG = Stage<D>;
+  using SG = Stage<D, W>;
   static_assert(I < SG::kInsts, "segment index");
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) char *)(lds + wave * SG::kInsts * 1024)));
@@ -574,7 +574,7 @@ __device__ __forceinline__ void issue_seg(char *lds, i32x4 res, int64_t row0, in
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "buffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds"
-      :: "s"(m0), "v"(stage_voff<D, IS_V>(wave, lane, I)), "s"(res), "s"(soff), "n"(I * 1024)
+      :: "s"(m0), "v"(stage_voff<D, IS_V, W>(wave, lane, I)), "s"(res), "s"(soff), "n"(I * 1024)
       : "memory", "m0");
 #pragma clang diagnostic pop
 }
@@ -737,10 +737,17 @@ __device__ __forceinline__ void wait_at_most(int n) {
   }
 }
 
-template <int D, bool CAP, bool DENSE>
-__global__ __launch_bounds__(kWThreads, 1)
+// RU: query heads per workgroup.  RU = 2 runs two heads of one GQA group
+// (which share their key/value head and, with one mask head, their walk)
+// in four waves over one set of K/V stages: each stage's loads serve 256
+// query rows instead of 128.
+template <int D, bool CAP, bool DENSE, int RU = 1>
+__global__ __launch_bounds__(64 * kWWaves * RU, 1)
 void splash_fwd_wide(const FwdParams p) {
-  using SG = Stage<D>;
+  static_assert(RU == 1 || (RU == 2 && D == 128 && !DENSE), "head pairs: D = 128, computable masks");
+  constexpr int kW = kWWaves * RU;          // waves
+  constexpr int kThr = 64 * kW;
+  using SG = Stage<D, kW>;
   constexpr int kDT = D / 32;
   constexpr int kKS = D / 16;
   constexpr int kMaskBytes = kBQ * 4;            // one packed word per block row per step
@@ -749,16 +756,20 @@ void splash_fwd_wide(const FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char k_st[kStages][SG::kBytes];
   __shared__ __attribute__((aligned(1024))) char v_st[kStages][SG::kBytes];
   __shared__ __attribute__((aligned(16))) char m_st[DENSE ? kStages : 1][kMaskBytes];
-  __shared__ int wg_any[kWWaves];
+  __shared__ int wg_any[kW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
+  const int wr = wave % kWWaves;            // the wave's 64 rows of the block row
+  const int hsub = wave / kWWaves;          // which of the workgroup's RU heads
 
   // Same (batch, head, row) mapping as the 32-row kernel: XCD x gets a
   // contiguous range of (batch, head) pairs, rows go out longest first.
-  const int nbh = static_cast<int>(p.B * p.Hq);
+  // With RU heads per workgroup the pairs are (batch, group of RU heads).
+  const int heads_u = static_cast<int>(p.Hq) / RU;
+  const int nbh = static_cast<int>(p.B) * heads_u;
   const int pid = blockIdx.x;
   int bh, rank;
   if ((nbh & 7) == 0) {
@@ -773,8 +784,8 @@ void splash_fwd_wide(const FwdParams p) {
   // follow one another in launch order.
   const int n_split = p.kv_splits;
   const int split = rank % n_split;
-  const int b = bh / static_cast<int>(p.Hq);
-  const int hq = bh % static_cast<int>(p.Hq);
+  const int b = bh / heads_u;
+  const int hq = (bh % heads_u) * RU + hsub;
   const int hkv = hq / p.group;
   const int hm = p.hm == 1 ? 0 : hq;
   // The workgroup's item and walk: one scalar load names the block row, the
@@ -792,7 +803,7 @@ void splash_fwd_wide(const FwdParams p) {
   const int r = items[item_at + 0];
   const int w_off = items[item_at + 1];
   const int w_len = items[item_at + 2];
-  const int row_in_block0 = 64 * wave + (lane & 31);      // qs = 0; qs = 1 adds 32
+  const int row_in_block0 = 64 * wr + (lane & 31);      // qs = 0; qs = 1 adds 32
   const int64_t q_row0 = static_cast<int64_t>(r) * kBQ + row_in_block0;
 
   const __bf16 *kg = static_cast<const __bf16 *>(p.k) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
@@ -824,18 +835,18 @@ void splash_fwd_wide(const FwdParams p) {
   const int mn_first = has_bits ? items[item_at + 4] : 0;
 #pragma unroll
   for (int t = 0; t < kSteps; ++t) {
-    issue_stage<D, false>(k_st[t], k_res, static_cast<int64_t>(dn_first) * kBK + kSK * t, wave, lane);
+    issue_stage<D, false, kW>(k_st[t], k_res, static_cast<int64_t>(dn_first) * kBK + kSK * t, wave, lane);
     if (has_bits) issue_mask(mn_first, t, t);
   }
-  issue_stage<D, true>(v_st[0], v_res, static_cast<int64_t>(dn_first) * kBK, wave, lane);
-  issue_stage<D, true>(v_st[1], v_res, static_cast<int64_t>(dn_first) * kBK + kSK, wave, lane);
+  issue_stage<D, true, kW>(v_st[0], v_res, static_cast<int64_t>(dn_first) * kBK, wave, lane);
+  issue_stage<D, true, kW>(v_st[1], v_res, static_cast<int64_t>(dn_first) * kBK + kSK, wave, lane);
   static_assert(kSteps == kStages, "the prologue fills every K stage");
 
   // The other V stages start as zeros: the first step's PV(-1) reads the
   // last stage with zero P, and 0 * (uninitialised LDS) could be NaN.
 #pragma unroll
-  for (int i = 0; i < 2 * SG::kBytes / (16 * kWThreads); ++i)
-    reinterpret_cast<u32x4 *>(&v_st[2][0])[tid + kWThreads * i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < 2 * SG::kBytes / (16 * kThr); ++i)
+    reinterpret_cast<u32x4 *>(&v_st[2][0])[tid + kThr * i] = u32x4{0u, 0u, 0u, 0u};
 
   bf16x8 qf[2][kKS];       // Q (B operand of S^T = K Q^T), rows of both halves
   int lo[2], hi[2];        // computable masks: allowed key interval, clamped to [-1, Skv]
@@ -1144,10 +1155,10 @@ void splash_fwd_wide(const FwdParams p) {
         return SG::kInsts + (has_bits ? 1 : 0) + (w >= -2 ? SG::kInsts : 0);
       };
       auto load_k = [&](int stage, int kv, int t) {
-        issue_stage<D, false>(k_st[stage], k_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane);
+        issue_stage<D, false, kW>(k_st[stage], k_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane);
       };
       auto load_v = [&](int stage, int kv, int t) {
-        issue_stage<D, true>(v_st[stage], v_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane);
+        issue_stage<D, true, kW>(v_st[stage], v_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane);
       };
       auto load_m = [&](int stage, int mn, int t) {
         if (has_bits) issue_mask(mn, t, stage);
@@ -1157,30 +1168,30 @@ void splash_fwd_wide(const FwdParams p) {
         const int64_t r0 = static_cast<int64_t>(kv) * kBK + kSK * t;
         if constexpr (SG::kInsts == 4) {
           if (h == 0) {
-            issue_seg<D, false, 0>(k_st[stage], k_res, r0, wave, lane);
-            issue_seg<D, false, 1>(k_st[stage], k_res, r0, wave, lane);
+            issue_seg<D, false, 0, kW>(k_st[stage], k_res, r0, wave, lane);
+            issue_seg<D, false, 1, kW>(k_st[stage], k_res, r0, wave, lane);
           } else {
-            issue_seg<D, false, 2>(k_st[stage], k_res, r0, wave, lane);
-            issue_seg<D, false, 3>(k_st[stage], k_res, r0, wave, lane);
+            issue_seg<D, false, 2, kW>(k_st[stage], k_res, r0, wave, lane);
+            issue_seg<D, false, 3, kW>(k_st[stage], k_res, r0, wave, lane);
           }
         } else {
-          if (h == 0) issue_seg<D, false, 0>(k_st[stage], k_res, r0, wave, lane);
-          else issue_seg<D, false, 1>(k_st[stage], k_res, r0, wave, lane);
+          if (h == 0) issue_seg<D, false, 0, kW>(k_st[stage], k_res, r0, wave, lane);
+          else issue_seg<D, false, 1, kW>(k_st[stage], k_res, r0, wave, lane);
         }
       };
       auto load_v_half = [&](int h, int stage, int kv, int t) {
         const int64_t r0 = static_cast<int64_t>(kv) * kBK + kSK * t;
         if constexpr (SG::kInsts == 4) {
           if (h == 0) {
-            issue_seg<D, true, 0>(v_st[stage], v_res, r0, wave, lane);
-            issue_seg<D, true, 1>(v_st[stage], v_res, r0, wave, lane);
+            issue_seg<D, true, 0, kW>(v_st[stage], v_res, r0, wave, lane);
+            issue_seg<D, true, 1, kW>(v_st[stage], v_res, r0, wave, lane);
           } else {
-            issue_seg<D, true, 2>(v_st[stage], v_res, r0, wave, lane);
-            issue_seg<D, true, 3>(v_st[stage], v_res, r0, wave, lane);
+            issue_seg<D, true, 2, kW>(v_st[stage], v_res, r0, wave, lane);
+            issue_seg<D, true, 3, kW>(v_st[stage], v_res, r0, wave, lane);
           }
         } else {
-          if (h == 0) issue_seg<D, true, 0>(v_st[stage], v_res, r0, wave, lane);
-          else issue_seg<D, true, 1>(v_st[stage], v_res, r0, wave, lane);
+          if (h == 0) issue_seg<D, true, 0, kW>(v_st[stage], v_res, r0, wave, lane);
+          else issue_seg<D, true, 1, kW>(v_st[stage], v_res, r0, wave, lane);
         }
       };
 
@@ -1298,7 +1309,7 @@ void splash_fwd_wide(const FwdParams p) {
     __syncthreads();
     int any_over = 0;
 #pragma unroll
-    for (int w = 0; w < kWWaves; ++w) any_over |= wg_any[w];
+    for (int w = 0; w < kW; ++w) any_over |= wg_any[w];
     if (attempt == 1 || any_over == 0) break;
 
     // Rare: some row's scores outgrew its base.  Find every row's exact max
@@ -1311,7 +1322,7 @@ void splash_fwd_wide(const FwdParams p) {
         const int key0u = ent_kv(u / kSteps) * kBK + kSK * (u % kSteps);
         wait_vmcnt<0>();
         lds_barrier();
-        issue_stage<D, false>(k_st[0], k_res, key0u, wave, lane);
+        issue_stage<D, false, kW>(k_st[0], k_res, key0u, wave, lane);
         if (has_bits) issue_mask(ent_mn(u / kSteps), u % kSteps, 0);
         wait_vmcnt<0>();
         lds_barrier();
@@ -1356,7 +1367,8 @@ void splash_fwd_wide(const FwdParams p) {
     constexpr int kRB = SG::kRowBytes;
     constexpr int kChunks = kRB / 16;
     auto swz_o = [](int rr) { return rr & (kChunks - 1); };
-    char *st = &k_st[0][0] + wave * 64 * kRB;
+    // wave w's rows: the K stages hold waves 0 and 1, the V stages 2 and 3
+    char *st = (wave < kWWaves ? &k_st[0][0] : &v_st[0][0]) + wr * 64 * kRB;
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
       const int rr = (lane & 31) + 32 * qs;
@@ -1371,7 +1383,7 @@ void splash_fwd_wide(const FwdParams p) {
         }
     }
     // this wave's rows only: its LDS writes and reads complete in order
-    const int64_t row_w = static_cast<int64_t>(r) * kBQ + 64 * wave;   // the wave's first row
+    const int64_t row_w = static_cast<int64_t>(r) * kBQ + 64 * wr;   // the wave's first row
     char *dst = n_split > 1
         ? reinterpret_cast<char *>(static_cast<__bf16 *>(p.part_o) +
                                    (((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + row_w) * D)
@@ -1467,9 +1479,18 @@ void launch_merge(const FwdParams &p, hipStream_t stream) {
 
 template <int D, bool CAP, bool DENSE>
 hipError_t launch_wide(const FwdParams &p, hipStream_t stream) {
-  const int64_t blocks = p.B * p.Hq * p.nq * p.kv_splits;
-  hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE>), dim3(static_cast<unsigned>(blocks)), dim3(kWThreads), 0,
-                     stream, p);
+  if constexpr (D == 128 && !DENSE) {
+    if (p.head_pairs) {
+      const int64_t blocks = p.B * (p.Hq / 2) * p.nq * p.kv_splits;
+      hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE, 2>), dim3(static_cast<unsigned>(blocks)),
+                         dim3(2 * kWThreads), 0, stream, p);
+    }
+  }
+  if (!p.head_pairs || D != 128 || DENSE) {
+    const int64_t blocks = p.B * p.Hq * p.nq * p.kv_splits;
+    hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE>), dim3(static_cast<unsigned>(blocks)), dim3(kWThreads), 0,
+                       stream, p);
+  }
   switch (p.kv_splits) {   // 1..8, checked by the caller
     case 1: break;
     case 2: launch_merge<D, 2>(p, stream); break;

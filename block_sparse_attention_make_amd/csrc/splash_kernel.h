@@ -45,6 +45,10 @@ struct FwdParams {
   int32_t kv_splits;          // 1: no split, out and lse written directly
   void *part_o;
   float *part_lse;
+  // Two query heads of a GQA group per workgroup (four waves sharing each
+  // K/V stage).  Set only for D = 128, computable masks, one mask head and
+  // an even group size.
+  int32_t head_pairs;
 };
 
 // dtype: 0 = bf16, 1 = f32.  D in {64, 128}.  Returns hipGetLastError().

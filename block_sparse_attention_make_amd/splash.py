@@ -73,6 +73,11 @@ def load_library(path=None):
     lib.splash_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32,
                                      ctypes.c_float, ctypes.c_float, vp, i32, i32, i32, vp, ctypes.c_size_t, vp]
     lib.splash_fwd_split.restype = ctypes.c_int
+    lib.splash_fwd_tiled.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32,
+                                     ctypes.c_float, ctypes.c_float, vp, i32, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.splash_fwd_tiled.restype = ctypes.c_int
+    lib.splash_fwd_heads_per_workgroup.argtypes = [vp, i64, i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_int32)]
+    lib.splash_fwd_heads_per_workgroup.restype = ctypes.c_int
     lib.splash_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.splash_fwd_workspace_size.restype = ctypes.c_int
     lib.splash_fwd_plan.argtypes = [vp, i64, i64, i32, ctypes.POINTER(ctypes.c_int32)]
@@ -245,9 +250,20 @@ def plan_kv_splits(mask_info, B, Hq, dtype_code=BF16):
     return int(n.value)
 
 
+def plan_heads_per_workgroup(mask_info, B, Hq, Hkv, D, dtype_code=BF16, kv_splits=1):
+    """The library's choice of query heads per workgroup (1, or 2 for two
+    heads of a GQA group sharing each K/V stage) for this launch
+    (splash_fwd_heads_per_workgroup)."""
+    lib = load_library()
+    n = ctypes.c_int32()
+    _check(lib, lib.splash_fwd_heads_per_workgroup(mask_info.handle, int(B), int(Hq), int(Hkv), int(D),
+                                                   int(dtype_code), int(kv_splits), ctypes.byref(n)))
+    return int(n.value)
+
+
 def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
                out=None, lse=None, return_lse=True, stream=None, softmax_aux=None, kv_splits="auto",
-               workspace=None):
+               workspace=None, heads_per_workgroup=0):
     """Splash-attention forward on GPU torch tensors (contiguous BHSD).
 
     softmax_aux: optional attention-sink logits, a float32 GPU tensor [ns]
@@ -256,6 +272,8 @@ def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
     fewer block rows than the GPU has workgroup slots) or 1..8 -- each block
     row's non-empty blocks divided into that many workgroups, merged by lse;
     with more than one split a float32 workspace is allocated unless given.
+    heads_per_workgroup: 0 (the library's choice), 1, or 2 (two heads of a
+    GQA group per workgroup, sharing each K/V stage; see splash_fwd_tiled).
     Returns (out, lse); lse is float32 [B, Hq, Sq] or None if return_lse is False.
     Launches asynchronously on `stream` (default: torch's current stream).
     """
@@ -303,9 +321,9 @@ def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
                       and workspace.numel() * workspace.element_size() >= nbytes.value):
                 raise ValueError(f"workspace must be a contiguous GPU tensor of at least {nbytes.value} bytes")
             ws_p, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        st = lib.splash_fwd_split(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+        st = lib.splash_fwd_tiled(mask_info.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   lse_p, B, Hq, Hkv, Sq, Skv, D, Dv, dt, scale, cap, aux_p, rows, ns, splits,
-                                  ws_p, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
+                                  int(heads_per_workgroup), ws_p, ws_bytes, ctypes.c_void_p(stream.cuda_stream))
     _check(lib, st)
     return out, lse
 

@@ -264,6 +264,40 @@ SPLASH_API splash_status splash_fwd_workspace_size(int64_t B, int64_t Hq, int64_
 SPLASH_API splash_status splash_fwd_plan(const splash_mask_info *mi, int64_t B, int64_t Hq, int32_t dtype,
                                          int32_t *kv_splits);
 
+/* splash_fwd_split with the workgroup shape chosen by the caller (the block
+ * shapes of the Pallas flash-attention page, FAQ "What does block_k_major
+ * mean versus block_k in Pallas flash attention?": how much of the problem
+ * one kernel instance holds and how each K/V transfer is shared).  A
+ * workgroup holds one 128-row block row of heads_per_workgroup query heads:
+ *   1  two waves, 128 query rows, two workgroups per compute unit;
+ *   2  four waves, the same block row of two heads of one GQA group, which
+ *      share their key/value head and their walk, so each K/V stage loaded
+ *      into LDS serves 256 query rows; one workgroup per compute unit.
+ *      Needs bf16, D = 128, a computable mask (causal, local, chunked) with
+ *      one mask head, and Hq / Hkv even; else SPLASH_EUNSUPPORTED.
+ *   0  the library's choice (splash_fwd_heads_per_workgroup).
+ * The result is the same either way, bit for bit (each row's arithmetic is
+ * unchanged).  Other arguments, requirements and errors as
+ * splash_fwd_split; heads_per_workgroup outside 0..2 returns SPLASH_EINVAL
+ * before anything runs.  splash_fwd, splash_fwd_sinks and splash_fwd_split
+ * use 0. */
+SPLASH_API splash_status splash_fwd_tiled(splash_mask_info *mi, const void *q, const void *k, const void *v,
+                                          void *out, float *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                                          int64_t Skv, int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
+                                          float logits_soft_cap, const float *softmax_aux, int32_t aux_heads,
+                                          int32_t num_sinks, int32_t kv_splits, int32_t heads_per_workgroup,
+                                          void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* The heads per workgroup splash_fwd_tiled uses for heads_per_workgroup = 0:
+ * 2 where two heads can share a workgroup (see splash_fwd_tiled) and the
+ * grid of B * Hq / 2 * (block rows) * kv_splits workgroups still gives 256
+ * compute units one each, else 1.  Host work only.  Errors: SPLASH_EINVAL
+ * (NULL arguments, negative sizes, Hkv <= 0, unknown dtype, kv_splits
+ * outside 1..8). */
+SPLASH_API splash_status splash_fwd_heads_per_workgroup(const splash_mask_info *mi, int64_t B, int64_t Hq,
+                                                        int64_t Hkv, int64_t D, int32_t dtype, int32_t kv_splits,
+                                                        int32_t *heads);
+
 /* Key-axis slice of a mask (ring attention on the splash-attention explainer
  * page, FAQ "What does ring attention add on top of the splash kernel?": the
  * MaskInfo is cut along the key axis to match the key/value shard a device

@@ -22,7 +22,8 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "splash_bwd", "splash_decode", "splash_decode_static", "splash_decode_workspace_size", "splash_fwd",
-        "splash_fwd_plan", "splash_fwd_sinks", "splash_fwd_split", "splash_fwd_workspace_size",
+        "splash_fwd_heads_per_workgroup", "splash_fwd_plan", "splash_fwd_sinks", "splash_fwd_split",
+        "splash_fwd_tiled", "splash_fwd_workspace_size",
         "splash_last_error", "splash_lse_merge",
         "splash_make_mask_info", "splash_make_mask_info_kv_slice", "splash_mask_info_destroy",
         "splash_mask_info_read_device", "splash_mask_info_upload", "splash_mask_info_view"])
@@ -272,3 +273,51 @@ def test_fwd_workspace_size_and_plan_on_host():
     assert lib.splash_fwd_plan(mi.handle, 1, 2, splash.F32, ctypes.byref(s)) == splash.OK and s.value == 1
     assert lib.splash_fwd_plan(mi.handle, 0, 2, splash.BF16, ctypes.byref(s)) == splash.OK and s.value == 1
     assert lib.splash_fwd_plan(None, 1, 2, splash.BF16, ctypes.byref(s)) == splash.EINVAL
+
+
+@pytest.mark.parametrize("mask, over, status", [
+    ("causal", dict(heads=3), splash.EINVAL),                        # not 0, 1 or 2
+    ("causal", dict(heads=-1), splash.EINVAL),
+    ("causal", dict(heads=2, Hkv=4), splash.EUNSUPPORTED),           # group of one head
+    ("causal", dict(heads=2, Hq=6, Hkv=2), splash.EUNSUPPORTED),     # odd group
+    ("causal", dict(heads=2, D=64, Dv=64), splash.EUNSUPPORTED),     # D = 64
+    ("causal", dict(heads=2, dtype=splash.F32), splash.EUNSUPPORTED),
+    ("dense", dict(heads=2), splash.EUNSUPPORTED),                   # dense mask
+])
+def test_fwd_tiled_validation_errors_before_launch(mask, over, status):
+    """splash_fwd_tiled refuses shapes two heads cannot share a workgroup for
+    (on the host, before anything is launched)."""
+    lib = splash.load_library()
+    if mask == "dense":
+        mi = splash.make_mask_info("dense", 256, 256, dense=np.ones((1, 256, 256), dtype=bool))
+    else:
+        mi = splash.make_mask_info("causal", 256, 256)
+    a = dict(mi=mi.handle, q=16, k=16, v=16, out=16, lse=None, B=1, Hq=4, Hkv=2, Sq=256, Skv=256, D=128, Dv=128,
+             dtype=splash.BF16, scale=math.nan, cap=0.0, aux=None, aux_rows=0, ns=0, splits=1, heads=0, ws=None,
+             ws_bytes=0, stream=None)
+    a.update(over)
+    assert lib.splash_fwd_tiled(*a.values()) == status, lib.splash_last_error()
+    assert lib.splash_last_error()
+
+
+def test_heads_per_workgroup_choice_on_host():
+    lib = splash.load_library()
+    h = ctypes.c_int32(7)
+    causal = splash.make_mask_info("causal", 8192, 8192)
+    # local_gqa_8k's shape: 16 pairs x 64 block rows fill 256 compute units
+    assert lib.splash_fwd_heads_per_workgroup(causal.handle, 1, 32, 8, 128, splash.BF16, 1, ctypes.byref(h)) == 0
+    assert h.value == 2
+    # one head per kv head, float32, D = 64: no pairs
+    for args in ((1, 16, 16, 128, splash.BF16), (1, 32, 8, 128, splash.F32), (1, 32, 8, 64, splash.BF16)):
+        assert lib.splash_fwd_heads_per_workgroup(causal.handle, *args, 1, ctypes.byref(h)) == 0 and h.value == 1
+    # too few pairs to give every compute unit one, unless split
+    small = splash.make_mask_info("causal", 1024, 1024)
+    assert lib.splash_fwd_heads_per_workgroup(small.handle, 1, 8, 2, 128, splash.BF16, 1, ctypes.byref(h)) == 0
+    assert h.value == 1
+    assert lib.splash_fwd_heads_per_workgroup(small.handle, 1, 8, 2, 128, splash.BF16, 8, ctypes.byref(h)) == 0
+    assert h.value == 2
+    dense = splash.make_mask_info("dense", 8192, 8192, dense=np.ones((1, 8192, 8192), dtype=bool))
+    assert lib.splash_fwd_heads_per_workgroup(dense.handle, 1, 32, 8, 128, splash.BF16, 1, ctypes.byref(h)) == 0
+    assert h.value == 1
+    assert lib.splash_fwd_heads_per_workgroup(causal.handle, 1, 32, 0, 128, splash.BF16, 1, ctypes.byref(h)) == \
+        splash.EINVAL
