@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "splash_kernel.h"
 
@@ -643,6 +644,33 @@ struct RowState {
   bool over;       // the row needs the exact-max recompute
 };
 
+// The allowed keys of this lane's row of half qs in a 32-key step, as the
+// bits 8 (v / 4) + v % 4 of score element v: dense masks take the row's
+// staged word shifted to this lane's keys; computable masks turn the row's
+// key interval [lo, hi] into the same bits (bit c <=> key kb + c).
+template <bool DENSE>
+__device__ __forceinline__ unsigned lane_key_word(int key0, int half, const int *lo, const int *hi,
+                                                  const unsigned *mword, int qs) {
+  if constexpr (DENSE) {
+    return mword[qs] >> (4 * half);
+  } else {
+    const int kb = key0 + 4 * half;
+    const int b0 = min(max(lo[qs] - kb, 0), kSK);       // first allowed bit
+    const int b1 = min(max(hi[qs] - kb + 1, 0), kSK);   // one past the last
+    const uint64_t span = b1 > b0 ? (uint64_t(1) << b1) - (uint64_t(1) << b0) : 0;
+    return static_cast<uint32_t>(span);
+  }
+}
+
+// Score element v of a lane with key bit word w: the score, or -inf where
+// the key is masked -- bit c sign-extended (0 or all ones) selects, bit by
+// bit: a bitfield extract and a bitfield select.
+__device__ __forceinline__ float mask_select(float x, unsigned w, int v) {
+  const int c = 8 * (v / 4) + (v % 4);
+  const int m = __builtin_amdgcn_sbfe(static_cast<int>(w), c, 1);
+  return __int_as_float((m & __float_as_int(x)) | (~m & static_cast<int>(0xff800000u)));
+}
+
 // Scores of one step -> capped (base-2 units), masked.  MASK: label-1 step.
 // Computable masks use the row's key interval; dense masks the packed word
 // of the row (bit c <=> key c of the step).
@@ -662,38 +690,12 @@ __device__ __forceinline__ void wide_cap_mask(const FwdParams &p, f32x16 *sc, in
       }
   }
   if constexpr (MASK) {
-    if constexpr (DENSE) {
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        const unsigned w = mword[qs] >> (4 * half);
-        seen[qs] |= w & 0x0f0f0f0fu;   // this lane's keys: bits 8 (v / 4) + v % 4
+    for (int qs = 0; qs < 2; ++qs) {
+      const unsigned w = lane_key_word<DENSE>(key0, half, lo, hi, mword, qs);
+      seen[qs] |= w & 0x0f0f0f0fu;   // this lane's keys: bits 8 (v / 4) + v % 4
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          // bit c sign-extended (0 or all ones) selects the score or -inf,
-          // bit by bit: a bitfield extract and a bitfield select
-          const int c = 8 * (v / 4) + (v % 4);
-          const int m = __builtin_amdgcn_sbfe(static_cast<int>(w), c, 1);
-          sc[qs][v] = __int_as_float((m & __float_as_int(sc[qs][v])) | (~m & static_cast<int>(0xff800000u)));
-        }
-      }
-    } else {
-      const int kb = key0 + 4 * half;
-#pragma unroll
-      for (int qs = 0; qs < 2; ++qs) {
-        // the row's allowed keys [lo, hi] as a word of this lane's keys
-        // (bit c <=> key kb + c), then the dense masks' two-instruction select
-        const int b0 = min(max(lo[qs] - kb, 0), kSK);       // first allowed bit
-        const int b1 = min(max(hi[qs] - kb + 1, 0), kSK);   // one past the last
-        const uint64_t span = b1 > b0 ? (uint64_t(1) << b1) - (uint64_t(1) << b0) : 0;
-        const int w = static_cast<int>(static_cast<uint32_t>(span));
-        seen[qs] |= static_cast<unsigned>(w) & 0x0f0f0f0fu;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int c = 8 * (v / 4) + (v % 4);
-          const int m = __builtin_amdgcn_sbfe(w, c, 1);
-          sc[qs][v] = __int_as_float((m & __float_as_int(sc[qs][v])) | (~m & static_cast<int>(0xff800000u)));
-        }
-      }
+      for (int v = 0; v < 16; ++v) sc[qs][v] = mask_select(sc[qs][v], w, v);
     }
   }
 }
@@ -949,8 +951,13 @@ void splash_fwd_wide(const FwdParams p) {
   // and no operand lives longer than a few slices.  The softmax runs against
   // the row's fixed base; the step's row sums come from dot products of the
   // bf16 exponentials with ones (the same rounded values PV multiplies).
+  // MC: std::true_type for a label-1 block, whose scores S(u) are masked
+  // here, element by element beside the matrix instructions, with the key
+  // words kw (computed at the end of the previous step).  Masked scores are
+  // written back, so the block-end base move sees them.
   auto body = [&](int u, f32x16 *sc_cur, f32x16 *sc_nxt, bf16x8 (*pf_cur)[2], bf16x8 (*pf_prv)[2],
-                  auto &&issue_loads, float *step_sum) {
+                  auto &&issue_loads, float *step_sum, auto mc, const unsigned *kw) {
+    constexpr bool kMasked = decltype(mc)::value;
     constexpr int kPVOps = 2 * kDT;       // PV A operands per step: (h, dt)
     const char *kst = k_st[(u + 1) % kStages];
     const char *vst = v_st[(u + kStages - 1) % kStages];
@@ -995,7 +1002,11 @@ void splash_fwd_wide(const FwdParams p) {
     float eg[2][4];   // exponentials of slices i (even / odd), until packed
     auto exp_one = [&](int i, int k) {   // element 4(i%4) + k of row half i/4
       const int qs = i / 4;
-      const float x = sc_cur[qs][4 * (i % 4) + k];
+      float x = sc_cur[qs][4 * (i % 4) + k];
+      if constexpr (kMasked) {
+        x = mask_select(x, kw[qs], 4 * (i % 4) + k);
+        sc_cur[qs][4 * (i % 4) + k] = x;
+      }
       if constexpr (CAP) {
         // Capped logit in base-2 units, cap log2(e) tanh y with y = logit / cap:
         // with r = 1 / (1 + e^{2y}), tanh y = 1 - 2r, which reaches +-1
@@ -1202,17 +1213,34 @@ void splash_fwd_wide(const FwdParams p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) pf_b[qs][h] = bf16x8{};   // PV(-1) adds exact zeros
 
-      // Mask of freshly formed scores S(u) of a label-1 step, right after the
-      // QK that formed them.  (The empty volatile asm keeps the compiler from
-      // running the masking unconditionally and selecting the result.)
-      auto finish = [&](f32x16 *sc, int lab, int stage, int key0) {
+      // Masking of freshly formed scores S(u) of a label-1 step.  Computable
+      // masks (mostly label-2 blocks) mask right after the QK that formed
+      // them.  Dense masks (mostly label-1 blocks) only fetch the key words
+      // kw here; the next step's body masks S(u) element by element beside
+      // its matrix instructions (kw is all ones for a label-2 block).  S(0) of
+      // a row is always masked right away (first), since the row's exponent
+      // base is set from it.  (One body for both kinds of block: a second,
+      // unmasked copy of the step in the same loop pushed the kernel past
+      // its registers.)
+      unsigned kw[2] = {~0u, ~0u};
+      auto finish = [&](f32x16 *sc, int lab, int stage, int key0, bool first) {
         if (lab == 1) {
-          qk_drain();   // the scores were formed by the step that just ended
           unsigned mw[2] = {0u, 0u};
           mask_words(stage, mw);
-          wide_cap_mask<false, DENSE, true>(p, sc, key0, half, lo, hi, mw, key_bits);
+          if (!DENSE || first) {
+            qk_drain();   // the scores were formed by the step that just ended
+            wide_cap_mask<false, DENSE, true>(p, sc, key0, half, lo, hi, mw, key_bits);
+          }
+          if constexpr (DENSE) {
+#pragma unroll
+            for (int qs = 0; qs < 2; ++qs) {
+              kw[qs] = lane_key_word<DENSE>(key0, half, lo, hi, mw, qs);
+              key_bits[qs] |= kw[qs] & 0x0f0f0f0fu;
+            }
+          }
         } else {
           any_full = true;
+          kw[0] = kw[1] = ~0u;
         }
       };
 
@@ -1230,7 +1258,7 @@ void splash_fwd_wide(const FwdParams p) {
       wait_at_most<kMaxInFlight>(count(-3) + count(-2) + count(-1));
       lds_barrier();
       wide_qk<D>(k_st[0], qf, lane, half, sc_a);
-      finish(sc_a, lab0, 0, kv0 * kBK);
+      finish(sc_a, lab0, 0, kv0 * kBK, true);
       if (__builtin_amdgcn_ballot_w64(rs.base[0] == -INFINITY || rs.base[1] == -INFINITY) != 0) set_base(sc_a);
 
       // Trip j runs the four steps u = 4j + t of block j.  Step u:
@@ -1248,6 +1276,8 @@ void splash_fwd_wide(const FwdParams p) {
         const int kv2_v = ent_kv(min(j + 2, nb - 1));
         const int mn2_v = ent_mn(min(j + 2, nb - 1));
         const int lab2_v = ent_lab(min(j + 2, nb - 1));
+        // the block's four steps, masked or not (label 1 / 2)
+        auto trip = [&](auto mc) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < kSteps; ++t) {
           const int u = kSteps * j + t;
@@ -1271,13 +1301,15 @@ void splash_fwd_wide(const FwdParams p) {
           };
           // body (with the refills), then the finish of S(u+1)
           float step_sum[2];
-          body(u, sc_cur, sc_nxt, pf_cur, pf_prv, refill, step_sum);
+          body(u, sc_cur, sc_nxt, pf_cur, pf_prv, refill, step_sum, mc, kw);
           // once per block: a row whose sum has outgrown its base moves it
           if (t == kSteps - 1 && __builtin_amdgcn_ballot_w64(fmaxf(rs.l[0], rs.l[1]) > kRescaleSum) != 0)
             rebase(sc_cur, pf_cur, step_sum);
-          if (t < kSteps - 1) finish(sc_nxt, lab0, t + 1, kv0 * kBK + kSK * (t + 1));
-          else if (more) finish(sc_nxt, lab1, 0, kv1 * kBK);
+          if (t < kSteps - 1) finish(sc_nxt, lab0, t + 1, kv0 * kBK + kSK * (t + 1), false);
+          else if (more) finish(sc_nxt, lab1, 0, kv1 * kBK, false);
         }
+        };
+        trip(std::integral_constant<bool, DENSE>{});
         kv0 = kv1;
         mn0 = mn1;
         lab0 = lab1;
