@@ -17,7 +17,10 @@ one JSON line.
 
 Timing: --prewarm-s seconds of back-to-back steps (the clock settles), W
 warm-up steps, then K steps back to back between one HIP event pair on the
-launch stream, with a device synchronisation on both sides.  value divides
+launch stream, with a device synchronisation on both sides.  --graph
+captures one forward step into a HIP graph and times its replays instead
+("launch" in the JSON says which; replays measured slower than eager
+launches on this stack).  value divides
 the FLOPs by the host wall time per step; roofline.achieved divides them by
 the event time per step.  kernel_ms_median / kernel_ms_min come from 20 more
 steps timed one by one afterwards (an event between launches delays the next
@@ -378,6 +381,8 @@ def main():
     ap.add_argument("--kv-shards", type=int, default=1, help="time the key/value-sharded path")
     ap.add_argument("--backward", action="store_true", help="time splash_bwd")
     ap.add_argument("--decode", action="store_true", help="time splash_decode on a decode workload")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=False,
+                    help="time the forward as replays of a captured HIP graph of one step")
     ap.add_argument("--heads-per-wg", type=int, default=0, choices=(0, 1, 2),
                     help="query heads per workgroup: 0 the library's choice, 1, or 2 (two heads of a GQA group "
                          "sharing each K/V stage)")
@@ -487,19 +492,34 @@ def main():
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
         delta = torch.empty(lse.shape, dtype=torch.float32, device=dev)
 
-    def step():
+    def step(s=None):
+        s = stream if s is None else s
         if args.backward:
             splash_bwd(qd, kd, vd, out, lse, dout, mi, logits_soft_cap=w.soft_cap, dq=dq, dk=dk, dv=dv,
-                       delta=delta, stream=stream)
+                       delta=delta, stream=s)
         elif P > 1:
-            splash_fwd_kv_sharded(qd, ks, vs, shard_mis, logits_soft_cap=w.soft_cap, stream=stream)
+            splash_fwd_kv_sharded(qd, ks, vs, shard_mis, logits_soft_cap=w.soft_cap, stream=s)
         else:
-            splash_fwd(qd, kd, vd, mi, logits_soft_cap=w.soft_cap, out=out, lse=lse, stream=stream,
+            splash_fwd(qd, kd, vd, mi, logits_soft_cap=w.soft_cap, out=out, lse=lse, stream=s,
                        softmax_aux=aux, kv_splits=splits, workspace=split_ws, heads_per_workgroup=args.heads_per_wg)
 
     prewarm_s = prewarm(step, torch, args.prewarm_s)
     for _ in range(args.warmup):
         step()
+    # --graph: the forward's launches (the kernel, and the merge with split
+    # keys) captured once and replayed as a HIP graph, as a caller's step
+    # loop may do.
+    launch = "eager"
+    if args.graph and not args.backward and P == 1:
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+            step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        launch = "graph"
+        for _ in range(20):
+            graph.replay()
+        step = lambda s=None: graph.replay()   # noqa: E731 (replays on the current stream)
     wall, region_ms = timed_region(step, torch, stream, args.steps)
     med_ms, min_ms = launch_stats(step, torch, stream)
     cold = None
@@ -572,6 +592,7 @@ def main():
                        mi, w.B, w.Hq, w.Hkv, w.D, 0 if w.dtype == "bf16" else 1, splits)),
                    "mask_block": [args.block_q, args.block_kv], "pass": "backward" if args.backward else "forward"},
         "prewarm_s": round(prewarm_s, 2),
+        "launch": launch,
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "dense_equiv_tflops": round(flops_dense / (ms_per_step * 1e-3) / 1e12, 2),
         "blocks_skipped": blocks_total - blocks_computed,
