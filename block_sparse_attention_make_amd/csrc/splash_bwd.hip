@@ -297,9 +297,10 @@ __device__ __forceinline__ uint32_t seg_voff(int seg, int lane) {
 // offset advances both the LDS and the global address).  Issued from inline
 // assembly, awaited with an explicit vmcnt wait before the barrier that
 // publishes the buffer.
-template <int D>
+template <int D, int ROWS = kBlk>
 __device__ __forceinline__ void issue_tile(char *lds, i32x4 res, uint32_t goff, int wave, int lane) {
-  constexpr int kSegs = BTile<D>::kBytes / 1024 / 4;   // per wave
+  constexpr int kSegs = ROWS * BTile<D>::kRowBytes / 1024 / 4;   // per wave
+  static_assert(kSegs % 4 == 0, "whole groups of four segments per wave");
 #pragma unroll
   for (int g = 0; g < kSegs / 4; ++g) {
     const int seg0 = wave * kSegs + 4 * g;
@@ -628,12 +629,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
 // ---- query-major kernel: dQ -----------------------------------------------
 // Workgroup (b, hq, query block r); wave w owns queries 32 w .. 32 w + 31.
 // The row's non-empty key blocks stream through two LDS buffers.
-template <int D, bool CAP, bool DENSE>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
+// HALF (D = 128): the K and V tiles stream in 64-key halves (two buffers of
+// two half tiles, 64 KiB of LDS), so two workgroups share a CU and two
+// waves a SIMD: one wave's softmax gradient (VALU) runs beside the other's
+// matrix instructions.  With whole 128-key tiles the buffers take 128 KiB,
+// one workgroup per CU, and each wave's MFMAs stand still during its own
+// VALU work; that shape stays for grids of at most one workgroup per CU,
+// where half tiles only add barriers.  D = 64 takes whole tiles (64 KiB).
+template <int D, bool CAP, bool DENSE, bool HALF>
+__global__ __launch_bounds__(kThreads, HALF ? 2 : 1) void bwd_dq(const BwdParams p) {
+  static_assert(!HALF || D == 128, "half tiles at D = 128");
   using T = BTile<D>;
   constexpr int kKS = D / 16, kDT = D / 32;
-  // [buffer][K, V] (as in the dK/dV kernel)
-  __shared__ __attribute__((aligned(1024))) char kv_t[2][2][T::kBytes];
+  constexpr int kTileRows = HALF ? 64 : kBlk;   // keys per buffered tile
+  constexpr int kSub = kTileRows / 32;              // 32-key groups per tile
+  constexpr int kUnits = kBlk / kTileRows;          // tiles per 128-key block
+  constexpr int kTileBytes = kTileRows * T::kRowBytes;
+  // [buffer][K, V]
+  __shared__ __attribute__((aligned(1024))) char kv_t[2][2][kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned mw_s[2][4 * kBlk];
 
   const FwdParams &f = p.f;
@@ -673,11 +686,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
     while (sl < f.width && label_at(sl) == 0) ++sl;
     return sl;
   };
-  auto issue = [&](int buf, int sl) {
+  // tile `hf` (kTileRows keys) of the block at slot sl into buffer buf
+  auto issue = [&](int buf, int sl, int hf) {
     const int c = __builtin_amdgcn_readfirstlane(load_index(f.dn, f.dn_bytes, meta + sl));
-    const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(c) * T::kBytes);
-    issue_tile<D>(kv_t[buf][0], kr, goff, wave, lane);
-    issue_tile<D>(kv_t[buf][1], vr, goff, wave, lane);
+    const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(c) * T::kBytes + hf * kTileBytes);
+    issue_tile<D, kTileRows>(kv_t[buf][0], kr, goff, wave, lane);
+    issue_tile<D, kTileRows>(kv_t[buf][1], vr, goff, wave, lane);
   };
   auto load_words = [&](int sl, unsigned &m0, unsigned &m1) {
     const int mn = load_index(f.mn, f.mn_bytes, meta + sl);
@@ -686,8 +700,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
     m1 = src[tid + kThreads];
   };
 
-  int sl = next_slot(0);
-  int buf = 0;
+  // The walk: tiles (sl, hf) of the row's non-empty blocks in order; the
+  // mask words of a block live in mw_s[mb] for all of its tiles.
+  int sl = next_slot(0), hf = 0;
+  int buf = 0, mb = 0;
   if (sl < f.width) {
     if constexpr (DENSE) {
       if (label_at(sl) == 1) {
@@ -697,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
         mw_s[0][tid + kThreads] = m1;
       }
     }
-    issue(0, sl);
+    issue(0, sl, 0);
   }
   wait_all_loads();
   __syncthreads();
@@ -708,47 +724,52 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
     // this lane's key interval relative to the block, clamped to [-1, kBlk]
     const int rlo = static_cast<int>(lo - kbase < -1 ? -1 : (lo - kbase > kBlk ? kBlk : lo - kbase));
     const int rhi = static_cast<int>(hi - kbase < -1 ? -1 : (hi - kbase > kBlk ? kBlk : hi - kbase));
-    const int sl2 = next_slot(sl + 1);
+    // the next tile: the block's next half, or the first tile of the next block
+    const bool next_block = hf + 1 == kUnits;
+    const int sl2 = next_block ? next_slot(sl + 1) : sl;
+    const int hf2 = next_block ? 0 : hf + 1;
     const bool more = sl2 < f.width;
-    const int label2 = more ? label_at(sl2) : 0;
+    const int label2 = more && next_block ? label_at(sl2) : 0;
     unsigned m0 = 0u, m1 = 0u;
     if (more) {
       if constexpr (DENSE) {
-        if (label2 == 1) load_words(sl2, m0, m1);   // before the tile loads
+        if (next_block && label2 == 1) load_words(sl2, m0, m1);   // before the tile loads
       }
-      issue(buf ^ 1, sl2);
+      issue(buf ^ 1, sl2, hf2);
     }
 
 #pragma unroll 1
-    for (int kb4 = 0; kb4 < 4; ++kb4) {
+    for (int kb = 0; kb < kSub; ++kb) {
+      const int kg = hf * kSub + kb;   // the 32-key group of the block
       f32x16 s, dp;
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 ak = read_row<D>(kv_t[buf][0], 32 * kb4 + (lane & 31), ks, half);
-        const bf16x8 av = read_row<D>(kv_t[buf][1], 32 * kb4 + (lane & 31), ks, half);
+        const bf16x8 ak = read_row<D>(kv_t[buf][0], 32 * kb + (lane & 31), ks, half);
+        const bf16x8 av = read_row<D>(kv_t[buf][1], 32 * kb + (lane & 31), ks, half);
         mfma_v(s, ak, qb[ks], ks == 0);
         mfma_v(dp, av, dob[ks], ks == 0);
       }
       mfma_drain(s, dp);
-      // This lane's row's allowed keys among the 32 keys of kb4 as a word
-      // (bit c <=> key 32 kb4 + 4 half + c of the layout below), all ones in
-      // a full block.  A row with no allowed key has an empty word in every
-      // block it meets (label 2 blocks have none), so no lse test is needed.
+      // This lane's row's allowed keys among the 32 keys of group kg as a
+      // word (bit c <=> key 32 kg + 4 half + c of the layout below), all ones
+      // in a full block.  A row with no allowed key has an empty word in
+      // every block it meets (label 2 blocks have none), so no lse test is
+      // needed.
       unsigned word = ~0u;
       if (label == 1) {
         if constexpr (DENSE) {
-          word = mw_s[buf][kb4 * kBlk + 32 * wave + (lane & 31)] >> (4 * half);
+          word = mw_s[mb][kg * kBlk + 32 * wave + (lane & 31)] >> (4 * half);
         } else {
-          const int kb = 32 * kb4 + 4 * half;
-          const int b0 = min(max(rlo - kb, 0), 32);
-          const int b1 = min(max(rhi - kb + 1, 0), 32);
+          const int k0 = 32 * kg + 4 * half;
+          const int b0 = min(max(rlo - k0, 0), 32);
+          const int b1 = min(max(rhi - k0 + 1, 0), 32);
           word = b1 > b0 ? static_cast<unsigned>((uint64_t(1) << b1) - (uint64_t(1) << b0)) : 0u;
         }
       }
       bf16x8 sb[2];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int c = 8 * (v / 4) + (v % 4);   // key 32 kb4 + 4 half + c of the block
+        const int c = 8 * (v / 4) + (v % 4);   // key 32 kg + 4 half + c of the block
         float s2, gf = 1.f;
         if constexpr (CAP) capped(s[v], kc2, f.cap_out, s2, gf);
         else s2 = s[v] * f.c2;
@@ -762,25 +783,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq(const BwdParams p) {
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          const bf16x8 ak = tr(kv_t[buf][0], 32 * kb4, h2, dt);
+          const bf16x8 ak = tr(kv_t[buf][0], 32 * kb, h2, dt);
           dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sb[h2], dq[dt], 0, 0, 0);
         }
     }
 
     if constexpr (DENSE) {
-      if (more && label2 == 1) {
-        mw_s[buf ^ 1][tid] = m0;
-        mw_s[buf ^ 1][tid + kThreads] = m1;
+      if (more && next_block && label2 == 1) {
+        mw_s[mb ^ 1][tid] = m0;
+        mw_s[mb ^ 1][tid + kThreads] = m1;
       }
     }
     wait_all_loads();
     __syncthreads();
     buf ^= 1;
+    if (next_block) mb ^= 1;
     sl = sl2;
+    hf = hf2;
   }
   // every wave is past the loop's last barrier
   wait_all_loads();
   store_t_rows<D>(&kv_t[0][0][0] + wave * 32 * D * 2, static_cast<__bf16 *>(p.dq) + q0, dq, p.scale, lane, half);
+}
+
+// Compute units of the current device (looked up once per device; 256 if
+// the query fails).
+int compute_units() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 256;
+    __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+  }
+  return v;
 }
 
 template <int D, bool CAP, bool DENSE>
@@ -790,8 +827,14 @@ hipError_t go(const BwdParams &p, hipStream_t stream) {
   if (nkv > 0)
     hipLaunchKernelGGL((bwd_dkdv<D, CAP, DENSE>), dim3(static_cast<unsigned>(nkv)), dim3(kThreads), 0, stream, p);
   const int64_t nq = f.B * f.Hq * f.nq;
-  if (nq > 0)
-    hipLaunchKernelGGL((bwd_dq<D, CAP, DENSE>), dim3(static_cast<unsigned>(nq)), dim3(kThreads), 0, stream, p);
+  if (nq > 0) {
+    if (D == 128 && nq > compute_units())
+      hipLaunchKernelGGL((bwd_dq<D, CAP, DENSE, D == 128>), dim3(static_cast<unsigned>(nq)), dim3(kThreads), 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((bwd_dq<D, CAP, DENSE, false>), dim3(static_cast<unsigned>(nq)), dim3(kThreads), 0, stream,
+                         p);
+  }
   return hipGetLastError();
 }
 

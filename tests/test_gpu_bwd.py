@@ -68,6 +68,10 @@ CASES = [
     ("rect_sq_gt_skv", 108, 1, 2, 2, 640, 256, 128, dict(kind="causal"), None),
     # 258 key blocks per row (more than one 256-slot metadata chunk; int16 data_next)
     ("rows_258_blocks", 109, 1, 2, 1, 256, 33024, 128, dict(kind="local", left=None, right=None), None),
+    # more dQ workgroups (2 x 32 x 5 = 320) than compute units: the dQ kernel
+    # streams 64-key half tiles, two workgroups per CU
+    ("causal_half_tiles", 112, 2, 32, 8, 640, 640, 128, dict(kind="causal"), None),
+    ("chunked_cap_half_tiles", 113, 2, 32, 4, 640, 640, 128, dict(kind="chunked", chunk=200), 5.0),
 ]
 
 
@@ -92,6 +96,18 @@ def test_bwd_dense_with_empty_rows_and_blocks(hm):
         _check(f"dense_hm{hm}.{nm}", g_, r_)
     assert (got[0][:, :, 7] == 0).all()
     assert (got[1][:, :, 600:] == 0).all() and (got[2][:, :, 600:] == 0).all()
+
+
+def test_bwd_dense_half_tiles():
+    """A dense mask over more dQ workgroups than compute units (half tiles;
+    mask words shared by a block's two halves)."""
+    rng = np.random.default_rng(114)
+    dense = synthetic.random_dense_mask(rng, 1, 640, 640, 0.2, force_diagonal=True)
+    dense[:, 0:128, 128:256] = True          # a full block
+    dense[:, 128:256, 0:128] = False         # an empty block
+    got, ref = _run(115, 2, 32, 8, 640, 640, 128, "dense", dense=dense)
+    for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+        _check(f"dense_half_tiles.{nm}", g_, r_)
 
 
 def test_autograd_function_matches_splash_bwd():
