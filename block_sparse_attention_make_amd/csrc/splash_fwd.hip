@@ -5,8 +5,10 @@
 // attention?"); how it walks the work comes from the compiled MaskInfo
 // (FAQ "What is MaskInfo in splash attention?", "What does grid shrinking do
 // in splash attention?"):
-//   * one workgroup per (batch, query head, 128-row query block); its loop
-//     runs over the W grid positions of that block row;
+//   * one workgroup per (batch, query head, 128-row query block) -- or per
+//     key split of it, or per block row of two heads of a GQA group; its
+//     loop runs over the W grid positions of that block row (the bfloat16
+//     kernel walks a flattened list of the non-empty ones);
 //   * label 0: nothing runs and no key/value bytes are fetched;
 //   * label 2: the block is computed with no mask at all;
 //   * label 1: the block is computed and masked -- computable masks are
