@@ -588,8 +588,9 @@ def main():
                    "seq_len": w.Sq, "head_dim": w.D, "mask": m.kind, "block": w.block,
                    "soft_cap": w.soft_cap, "parallelism": "single-gpu",
                    "sinks_per_kv_head": args.sinks, "kv_shards": P, "kv_splits": splits,
-                   "heads_per_workgroup": (args.heads_per_wg or plan_heads_per_workgroup(
-                       mi, w.B, w.Hq, w.Hkv, w.D, 0 if w.dtype == "bf16" else 1, splits)),
+                   "heads_per_workgroup": None if args.backward or P > 1 else (
+                       args.heads_per_wg or plan_heads_per_workgroup(
+                           mi, w.B, w.Hq, w.Hkv, w.D, 0 if w.dtype == "bf16" else 1, splits)),
                    "mask_block": [args.block_q, args.block_kv], "pass": "backward" if args.backward else "forward"},
         "prewarm_s": round(prewarm_s, 2),
         "launch": launch,
