@@ -212,8 +212,8 @@ __device__ __forceinline__ void capped(float x, float kc2, float cap_out, float 
 // of its row 8 columns apart, so direct stores scatter 32 rows over one
 // instruction.  The wave writes its 32 rows (bf16) into `lds` (32 x D, its
 // own region; 16-byte chunks swizzled by row) and stores them back 16 bytes
-// per lane, whole rows per instruction.  The wave's LDS writes and reads
-// complete in order.
+// per lane, whole rows per instruction (non-temporal: the kernel does not
+// read them again).  The wave's LDS writes and reads complete in order.
 template <int D>
 __device__ __forceinline__ void store_t_rows(char *lds, __bf16 *g, const f32x16 (&acc)[D / 32], float mul, int lane,
                                              int half) {
@@ -233,7 +233,7 @@ __device__ __forceinline__ void store_t_rows(char *lds, __bf16 *g, const f32x16 
   for (int i = 0; i < 32 / kRowsPer; ++i) {
     const int r2 = kRowsPer * i + lane / kChunks, c = lane % kChunks;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + r2 * kRB + ((c ^ (r2 & (kChunks - 1))) * 16));
-    *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(g) + r2 * kRB + c * 16) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(g) + r2 * kRB + c * 16));
   }
 }
 

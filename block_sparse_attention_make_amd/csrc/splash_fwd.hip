@@ -1391,6 +1391,10 @@ void splash_fwd_wide(const FwdParams p) {
   // waves are past their last K-stage read (the barrier that ends the
   // attempt loop); a workgroup with no block still has its prologue loads in
   // flight into those stages, hence the wait.
+  // The global stores are non-temporal: nothing in this kernel reads the
+  // output again, and marking it so leaves L2 to the K/V lines that other
+  // workgroups re-read (the soft-capped 16k GQA forward, whose K/V exceeds
+  // L2 most, runs about 2% faster; outputs are unchanged).
   wait_vmcnt<0>();
   float inv[2], lse_row[2];
   const float sl2 = n_split > 1 ? -INFINITY : sink_lse2(p, hq);   // the merge adds a split's sinks
@@ -1428,7 +1432,7 @@ void splash_fwd_wide(const FwdParams p) {
     for (int i = 0; i < 64 / kRowsPer; ++i) {
       const int rr = kRowsPer * i + lane / kChunks, c = lane % kChunks;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(st + rr * kRB + ((c ^ swz_o(rr)) * 16));
-      *reinterpret_cast<u32x4 *>(dst + rr * kRB + c * 16) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + rr * kRB + c * 16));
     }
   }
 #pragma unroll
@@ -1436,9 +1440,10 @@ void splash_fwd_wide(const FwdParams p) {
     const int64_t q_row = q_row0 + 32 * qs;
     if (half == 0) {
       if (n_split > 1)
-        p.part_lse[((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + q_row] = lse_row[qs];
+        __builtin_nontemporal_store(lse_row[qs],
+                                    &p.part_lse[((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + q_row]);
       else if (p.lse)
-        p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] = lse_row[qs];
+        __builtin_nontemporal_store(lse_row[qs], &p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row]);
     }
   }
 }
@@ -1500,8 +1505,8 @@ void merge_splits(const FwdParams p) {
   union { __bf16 h[8]; u32x4 u; } pk;
 #pragma unroll
   for (int e = 0; e < 8; ++e) pk.h[e] = static_cast<__bf16>(acc[e] * scale);
-  *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(p.out) + row * D + c0) = pk.u;
-  if (p.lse && c0 == 0) p.lse[row] = lse2_tot * kLn2;
+  __builtin_nontemporal_store(pk.u, reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(p.out) + row * D + c0));
+  if (p.lse && c0 == 0) __builtin_nontemporal_store(lse2_tot * kLn2, &p.lse[row]);
 }
 
 template <int D, int S>
