@@ -114,10 +114,11 @@ def mfma_probe(torch):
 
 
 def read_probe(torch, nbytes):
-    """HBM read GB/s the GPU sustains on a plain grid-stride read of one
+    """HBM read GB/s the GPU sustains on a plain streaming read of one
     nbytes device buffer (as many bytes as a memory-bound kernel streams per
-    launch), 32 workgroups per CU, 1 s warm, median of 10 timed launches;
-    None if the probe library is absent."""
+    launch): 8 workgroups per CU, each reading one contiguous share with
+    non-temporal loads; 1 s warm, median of 10 timed launches; None if the
+    probe library is absent."""
     import ctypes
     import numpy as np
     path = os.path.join(ROOT, "block_sparse_attention_make_amd", "lib", "libsplash_probe.so")
@@ -126,7 +127,7 @@ def read_probe(torch, nbytes):
     lib = ctypes.CDLL(path)
     lib.splash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_void_p]
-    blocks = 32 * torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 8 * torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda:0")
     stream = torch.cuda.current_stream()
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda:0")
