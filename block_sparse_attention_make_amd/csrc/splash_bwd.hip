@@ -467,7 +467,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
     issue_tile<D>(qdo_t[buf][1], dr, goff, wave, lane);
   };
 
+  // The walk runs one pair ahead of the tiles: the list entry of the pair
+  // after the next is loaded while the current tile is computed (and
+  // awaited with the tile loads), so naming the next tile's query block
+  // never waits on a dependent load.  The raw entry travels in a VGPR until
+  // then.
   int buf = 0;
+  int g2 = g, e2 = e, n2 = n;   // the pair after the current one
+  if (g < f.group) advance(g2, e2, n2);
+  int ent_next = 0;             // its list entry, once loaded
   if (g < f.group) {
     int r, label;
     entry(g, e, r, label);
@@ -475,23 +483,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
     load_small(g, e, label, sm);
     store_small(0, label, sm);   // waits for the small loads, issued before any tile load
     issue(0, g, r);
+    if (g2 < f.group) ent_next = p.col_ent[list_of(g2) * p.col_w + e2];
   }
   wait_all_loads();
   __syncthreads();
 
   while (g < f.group) {
-    int r, label;
-    entry(g, e, r, label);
-    int g2 = g, e2 = e, n2 = n;
-    advance(g2, e2, n2);
     const bool more = g2 < f.group;
     int r2 = 0, label2 = 0;
+    if (more) {
+      const int ent = __builtin_amdgcn_readfirstlane(ent_next);
+      r2 = ent & 0x3fffffff;
+      label2 = static_cast<int>(static_cast<unsigned>(ent) >> 30);
+    }
+    // the pair after that; its count is loaded only where the walk changes
+    // query head, before any load of this iteration is in flight
+    int g3 = g2, e3 = e2, n3 = n2;
+    if (more) advance(g3, e3, n3);
     Small sm{};
     if (more) {
-      entry(g2, e2, r2, label2);
       load_small(g2, e2, label2, sm);   // before the tile loads: their wait does not wait on those
       issue(buf ^ 1, g2, r2);
     }
+    if (g3 < f.group) ent_next = p.col_ent[list_of(g3) * p.col_w + e3];
 
     // The tile's four 32-row query blocks run as a software pipeline: step
     // qb forms S and dP of block qb + 1 (A), the softmax gradient of block qb
@@ -616,6 +630,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
     g = g2;
     e = e2;
     n = n2;
+    g2 = g3;
+    e2 = e3;
+    n2 = n3;
   }
   // Every wave is past the loop's last barrier and no load is in flight, so
   // the tiles are free: each wave stages its dk rows and then its dv rows in
@@ -680,62 +697,85 @@ __global__ __launch_bounds__(kThreads, HALF ? 2 : 1) void bwd_dq(const BwdParams
   const int64_t kv_head = (static_cast<int64_t>(b) * f.Hkv + hkv) * f.Skv * D;
   const i32x4 kr = make_rsrc(static_cast<const __bf16 *>(f.k) + kv_head, f.Skv * D * 2);
   const i32x4 vr = make_rsrc(static_cast<const __bf16 *>(f.v) + kv_head, f.Skv * D * 2);
-  const int64_t meta = (static_cast<int64_t>(hm) * f.nq + r) * f.width;
-  auto label_at = [&](int sl) -> int { return __builtin_amdgcn_readfirstlane(load_index(f.bm, f.bm_bytes, meta + sl)); };
-  auto next_slot = [&](int sl) -> int {   // first slot >= sl with a non-empty block, else width
-    while (sl < f.width && label_at(sl) == 0) ++sl;
-    return sl;
-  };
-  // tile `hf` (kTileRows keys) of the block at slot sl into buffer buf
-  auto issue = [&](int buf, int sl, int hf) {
-    const int c = __builtin_amdgcn_readfirstlane(load_index(f.dn, f.dn_bytes, meta + sl));
+  // The row's walk: its non-empty blocks in order, one entry each (key
+  // block | label << 28, and the dense mask's partial block), the same
+  // lists the forward walks.  They are read-only for the kernel's lifetime,
+  // so they go through the constant address space (scalar loads, counted
+  // with the LDS operations rather than with the tile loads), and each
+  // entry is read one block ahead of its tiles' loads.
+  typedef const __attribute__((address_space(4))) int32_t *cptr;
+  const cptr items = (cptr)(f.items);
+  const cptr walk_kv = (cptr)(f.walk_kv);
+  const cptr walk_mn = (cptr)(DENSE ? f.walk_mn : f.walk_kv);
+  const int64_t item_at = (static_cast<int64_t>(hm) * f.nq + rank) * 8;
+  const int w_off = items[item_at + 1];
+  const int w_len = items[item_at + 2];
+  auto ent_kv = [](int ent) -> int { return ent & 0x0fffffff; };
+  auto ent_lab = [](int ent) -> int { return static_cast<int>(static_cast<uint32_t>(ent) >> 28); };
+  // tile `hf` (kTileRows keys) of key block c into buffer buf
+  auto issue = [&](int buf, int c, int hf) {
     const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(c) * T::kBytes + hf * kTileBytes);
     issue_tile<D, kTileRows>(kv_t[buf][0], kr, goff, wave, lane);
     issue_tile<D, kTileRows>(kv_t[buf][1], vr, goff, wave, lane);
   };
-  auto load_words = [&](int sl, unsigned &m0, unsigned &m1) {
-    const int mn = load_index(f.mn, f.mn_bytes, meta + sl);
+  auto load_words = [&](int mn, unsigned &m0, unsigned &m1) {
     const unsigned *src = f.pmb_bits + static_cast<int64_t>(mn) * 4 * kBlk;
     m0 = src[tid];
     m1 = src[tid + kThreads];
   };
 
-  // The walk: tiles (sl, hf) of the row's non-empty blocks in order; the
-  // mask words of a block live in mw_s[mb] for all of its tiles.
-  int sl = next_slot(0), hf = 0;
+  // The walk: tiles (j, hf) of the row's entries in order; the mask words of
+  // a block live in mw_s[mb] for all of its tiles.  ent / mn: entry j;
+  // ent_n / mn_n: entry j + 1 (loaded a block ahead).
+  int j = 0, hf = 0;
   int buf = 0, mb = 0;
-  if (sl < f.width) {
+  int ent = 0, mn = 0, ent_n = 0, mn_n = 0;
+  if (w_len > 0) {
+    ent = walk_kv[w_off];
+    if constexpr (DENSE) mn = walk_mn[w_off];
+    if (w_len > 1) {
+      ent_n = walk_kv[w_off + 1];
+      if constexpr (DENSE) mn_n = walk_mn[w_off + 1];
+    }
     if constexpr (DENSE) {
-      if (label_at(sl) == 1) {
+      if (ent_lab(ent) == 1) {
         unsigned m0, m1;
-        load_words(sl, m0, m1);
+        load_words(mn, m0, m1);
         mw_s[0][tid] = m0;
         mw_s[0][tid + kThreads] = m1;
       }
     }
-    issue(0, sl, 0);
+    issue(0, ent_kv(ent), 0);
   }
   wait_all_loads();
   __syncthreads();
 
-  while (sl < f.width) {
-    const int label = label_at(sl);
-    const int64_t kbase = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(load_index(f.dn, f.dn_bytes, meta + sl))) * kBlk;
+  while (j < w_len) {
+    const int label = ent_lab(ent);
+    const int64_t kbase = static_cast<int64_t>(ent_kv(ent)) * kBlk;
     // this lane's key interval relative to the block, clamped to [-1, kBlk]
     const int rlo = static_cast<int>(lo - kbase < -1 ? -1 : (lo - kbase > kBlk ? kBlk : lo - kbase));
     const int rhi = static_cast<int>(hi - kbase < -1 ? -1 : (hi - kbase > kBlk ? kBlk : hi - kbase));
     // the next tile: the block's next half, or the first tile of the next block
     const bool next_block = hf + 1 == kUnits;
-    const int sl2 = next_block ? next_slot(sl + 1) : sl;
+    const int j2 = next_block ? j + 1 : j;
     const int hf2 = next_block ? 0 : hf + 1;
-    const bool more = sl2 < f.width;
-    const int label2 = more && next_block ? label_at(sl2) : 0;
+    const bool more = j2 < w_len;
+    const int ent2 = next_block ? ent_n : ent;
+    const int mn2 = next_block ? mn_n : mn;
+    const int label2 = more && next_block ? ent_lab(ent2) : 0;
     unsigned m0 = 0u, m1 = 0u;
     if (more) {
       if constexpr (DENSE) {
-        if (next_block && label2 == 1) load_words(sl2, m0, m1);   // before the tile loads
+        if (next_block && label2 == 1) load_words(mn2, m0, m1);   // before the tile loads
       }
-      issue(buf ^ 1, sl2, hf2);
+      issue(buf ^ 1, ent_kv(ent2), hf2);
+    }
+    // entering a new block next: read the entry after it now
+    int ent_n2 = ent_n, mn_n2 = mn_n;
+    if (next_block && j2 + 1 < w_len) {
+      ent_n2 = walk_kv[w_off + j2 + 1];
+      if constexpr (DENSE) mn_n2 = walk_mn[w_off + j2 + 1];
     }
 
 #pragma unroll 1
@@ -798,7 +838,11 @@ __global__ __launch_bounds__(kThreads, HALF ? 2 : 1) void bwd_dq(const BwdParams
     __syncthreads();
     buf ^= 1;
     if (next_block) mb ^= 1;
-    sl = sl2;
+    ent = ent2;
+    mn = mn2;
+    ent_n = ent_n2;
+    mn_n = mn_n2;
+    j = j2;
     hf = hf2;
   }
   // every wave is past the loop's last barrier
