@@ -60,12 +60,6 @@ __device__ __forceinline__ bf16x8 join_tr_halves(s16x4 lo4, s16x4 hi4) {
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int load_index(const void *p, int bytes, int64_t i) {
-  if (bytes == 1) return static_cast<const int8_t *>(p)[i];
-  if (bytes == 2) return static_cast<const int16_t *>(p)[i];
-  return static_cast<const int32_t *>(p)[i];
-}
-
 // A 128 x D bf16 tile in LDS; 16-byte chunk c of row r sits at chunk
 // c ^ swz(r).  Each tile is read both ways, so the swizzle serves both:
 //  * row reads (ds_read_b128, 16 lanes on 16 consecutive rows, one logical

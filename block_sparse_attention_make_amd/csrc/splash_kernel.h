@@ -32,9 +32,10 @@ struct FwdParams {
   const float *aux;   // device sink logits [aux_heads, num_sinks], or null
   int32_t aux_heads;  // 1 (shared), Hkv (row h / group) or Hq (row h)
   int32_t num_sinks;
-  // The bf16 kernel's walk (DeviceCopy::walk_kv / walk_mn / items): each
+  // The bf16 kernels' walk (DeviceCopy::walk_kv / walk_mn / items): each
   // workgroup reads its item -- block row, first walk entry, entry count,
-  // first data_next and mask_next -- and then its walk entries.
+  // first data_next and mask_next -- and then its walk entries.  The
+  // backward's dQ kernel walks the same lists (one split).
   const int32_t *walk_kv, *walk_mn, *items;
   // Split keys (bf16 kernel): the non-empty grid positions of each block row
   // are divided into kv_splits ranges of about equal count, one workgroup
@@ -55,8 +56,8 @@ struct FwdParams {
 // With p.kv_splits > 1 (bf16 only) it launches the forward and the merge.
 hipError_t launch_fwd(const FwdParams &p, int dtype, hipStream_t stream);
 
-// Backward launch parameters (bf16 only).  The forward's MaskInfo fields
-// (`f`) drive the query-major dQ kernel; the key-major dK/dV kernel walks the
+// Backward launch parameters (bf16 only).  The forward's walk lists (in `f`)
+// drive the query-major dQ kernel; the key-major dK/dV kernel walks the
 // transposed lists: for mask head hm and key block c, col_n[hm * nk + c]
 // entries col_ent[(hm * nk + c) * col_w + e] = r | label << 30 (query block
 // rows in ascending order) with, for dense masks, the partial block index
