@@ -41,7 +41,9 @@ def _run(seed, B, Hq, Hkv, Sq, Skv, D, kind, cap=None, dense=None, **mk):
     q, k, v = synthetic.make_qkv(seed, B, Hq, Hkv, Sq, Skv, D, D)
     g = torch.Generator().manual_seed(seed + 1000)
     do = torch.randn((B, Hq, Sq, D), generator=g).to(torch.bfloat16)
-    mi = make_mask_info(kind, Sq, Skv, dense=dense, **mk)
+    # compile-only options (block shape, shrink, downcast) do not change the mask
+    compile_kw = {key: mk.pop(key) for key in ("block_q", "block_kv", "shrink", "downcast") if key in mk}
+    mi = make_mask_info(kind, Sq, Skv, dense=dense, **mk, **compile_kw)
     qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
     out, lse = splash_fwd(qd, kd, vd, mi, logits_soft_cap=cap)
     nan = float("nan")
@@ -72,6 +74,14 @@ CASES = [
     # streams 64-key half tiles, two workgroups per CU
     ("causal_half_tiles", 112, 2, 32, 8, 640, 640, 128, dict(kind="causal"), None),
     ("chunked_cap_half_tiles", 113, 2, 32, 4, 640, 640, 128, dict(kind="chunked", chunk=200), 5.0),
+    # MaskInfo variants the walks must follow: 256 x 512 blocks (walked as
+    # 128 x 128 sub-blocks), interior empty slots kept (shrink off), int32
+    # index arrays (downcast off), and shrink off with half tiles
+    ("causal_coarse_256x512", 114, 1, 4, 2, 1024, 1024, 128, dict(kind="causal", block_q=256, block_kv=512), None),
+    ("local_no_shrink", 115, 1, 2, 2, 768, 768, 128, dict(kind="local", left=130, right=0, shrink=False), None),
+    ("chunked_no_downcast_d64", 116, 1, 2, 1, 640, 640, 64, dict(kind="chunked", chunk=256, downcast=False), None),
+    ("local_no_shrink_half_tiles", 117, 2, 32, 8, 640, 640, 128,
+     dict(kind="local", left=150, right=20, shrink=False), None),
 ]
 
 
