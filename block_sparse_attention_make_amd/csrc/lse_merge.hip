@@ -11,7 +11,8 @@
 // HBM-bound elementwise work: each thread moves 8 consecutive elements of
 // one row with 16- or 32-byte accesses; the Dv / 8 threads of a row sit in
 // one wavefront, so the row's lse is read by all of them before any store
-// and the output may overwrite part a (or b) in place.
+// and the output may overwrite part a (or b) in place.  Every element is
+// read and written once, with non-temporal loads and stores.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -28,12 +29,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 struct Eight { float x[8]; };
 
 __device__ __forceinline__ Eight load8(const float *p) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + 4));
   return Eight{{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}};
 }
 __device__ __forceinline__ Eight load8(const __bf16 *p) {
-  const u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+  const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
   Eight r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -43,14 +44,14 @@ __device__ __forceinline__ Eight load8(const __bf16 *p) {
   return r;
 }
 __device__ __forceinline__ void store8(float *p, const Eight &v) {
-  *reinterpret_cast<f32x4 *>(p) = f32x4{v.x[0], v.x[1], v.x[2], v.x[3]};
-  *reinterpret_cast<f32x4 *>(p + 4) = f32x4{v.x[4], v.x[5], v.x[6], v.x[7]};
+  __builtin_nontemporal_store(f32x4{v.x[0], v.x[1], v.x[2], v.x[3]}, reinterpret_cast<f32x4 *>(p));
+  __builtin_nontemporal_store(f32x4{v.x[4], v.x[5], v.x[6], v.x[7]}, reinterpret_cast<f32x4 *>(p + 4));
 }
 __device__ __forceinline__ void store8(__bf16 *p, const Eight &v) {
   union { __bf16 h[8]; u32x4 u; } pk;
 #pragma unroll
   for (int i = 0; i < 8; ++i) pk.h[i] = static_cast<__bf16>(v.x[i]);
-  *reinterpret_cast<u32x4 *>(p) = pk.u;
+  __builtin_nontemporal_store(pk.u, reinterpret_cast<u32x4 *>(p));
 }
 
 template <typename TA, typename TB, typename TO>
