@@ -1023,6 +1023,29 @@ void splash_fwd_wide(const FwdParams p) {
         eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2e, -b2[qs]));
       }
     };
+    // With the cap each element's exponent is a chain of three dependent
+    // transcendentals (e^{2y}, the reciprocal, the exponential).  Run as one
+    // chain per sub-slice, the in-order wave waits out each link's latency
+    // and the matrix unit idles; so the chain is cut into three stages and
+    // sub-slice e issues stage A of element e + 2, B of e + 1 and C of e,
+    // each reading what the previous sub-slice produced.  Elements are
+    // numbered e = 4 i + k (slice i, sub-slice k), as exp_one numbers them.
+    float cap_e[4], cap_r[4];   // stage outputs, ring indexed by e % 4
+    auto cap_a = [&](int e) {   // masked score (written back), e^{2y}
+      const int i = e >> 2, k = e & 3, qs = i / 4, v = 4 * (i % 4) + k;
+      float x = sc_cur[qs][v];
+      if constexpr (kMasked) {
+        x = mask_select(x, kw[qs], v);
+        sc_cur[qs][v] = x;
+      }
+      cap_e[e & 3] = __builtin_amdgcn_exp2f(x * kc2);
+    };
+    auto cap_b = [&](int e) { cap_r[e & 3] = __builtin_amdgcn_rcpf(1.f + cap_e[e & 3]); };
+    auto cap_c = [&](int e) {   // the capped logit's exponential, as in exp_one
+      const int i = e >> 2, k = e & 3, qs = i / 4;
+      const float x = sc_cur[qs][4 * (i % 4) + k];
+      eg[i & 1][k] = __builtin_amdgcn_exp2f(__builtin_fmaf(cap_r[e & 3], m2cap, __builtin_fmaf(x, 0x1p-100f, kr[qs])));
+    };
     auto pack = [&](int i, int pr) {   // elements 2pr, 2pr+1 of slice i -> P, row sum
       const int qs = i / 4, v0 = 4 * (i % 4) + 2 * pr;
       const float e0 = eg[i & 1][2 * pr], e1 = eg[i & 1][2 * pr + 1];
@@ -1044,6 +1067,11 @@ void splash_fwd_wide(const FwdParams p) {
       b2[qs] = rs.base[qs] == -INFINITY ? 0.f : rs.base[qs];
       kr[qs] = p.cap_out - b2[qs];
     }
+    if constexpr (CAP) {   // the cap pipeline's first stages
+      cap_a(0);
+      cap_a(1);
+      cap_b(0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     // Each slice is four sub-slices of one matrix instruction each, with
     // about one matrix instruction's worth of other work beneath it (an
@@ -1059,7 +1087,14 @@ void splash_fwd_wide(const FwdParams p) {
         if (sub == 0 && i + 2 < 8) reads_slice(i + 2);
         if (sub == 1) issue_loads(i);
         if (sub == 0 && i > 0) pack(i - 1, 1);
-        exp_one(i, sub);
+        if constexpr (CAP) {
+          const int e = 4 * i + sub;
+          if (e + 2 < 32) cap_a(e + 2);
+          if (e + 1 < 32) cap_b(e + 1);
+          cap_c(e);
+        } else {
+          exp_one(i, sub);
+        }
         if (sub == 2) pack(i, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
