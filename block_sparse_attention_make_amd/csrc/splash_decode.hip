@@ -331,11 +331,13 @@ __global__ __launch_bounds__(64) void decode_merge(const DecodeParams p) {
 #pragma unroll
   for (int j = 0; j < kCols; ++j) o[j] = 0.f;
   if (m != -INFINITY) {
+    // An empty range has m = -inf (weight e^-inf = 0) and a written zero sum
+    // and output, so no range is skipped: the loop body has no branch, and
+    // the unrolled iterations' loads go out together.
+#pragma unroll 8
     for (int c = 0; c < p.n_chunks; ++c) {
       const int64_t slot = (unit * p.n_chunks + c) * G + g;
-      const float mc = p.ws_m[slot];
-      if (mc == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(mc - m);
+      const float w = __builtin_amdgcn_exp2f(p.ws_m[slot] - m);
       l += w * p.ws_l[slot];
 #pragma unroll
       for (int j = 0; j < kCols; ++j) o[j] += w * p.ws_o[slot * D + kCols * lane + j];
