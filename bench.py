@@ -264,12 +264,22 @@ def cpu_baseline(w, q, k, v, dense, block_mask, budget_s=12.0):
     whole 128-row query blocks of (batch 0, head h), taken round-robin over
     heads and block rows, until about budget_s seconds of CPU work.  Its rate
     is counted in the same unit as the GPU's: FLOPs of the computed blocks of
-    the rows it produced, per second."""
+    the rows it produced, per second.  The oracle's MaskInfo builder is timed
+    separately on the workload's whole mask (mask_info_ms, beside the
+    library's mask_compile_ms)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import attention as oatt
+    from oracle import mask_info as omi
     from oracle import masks as omasks
+
+    t_mi = time.perf_counter()
+    full = omasks.materialize(w.mask.kind, w.Sq, w.Skv, left=w.mask.left, right=w.mask.right,
+                              chunk=w.mask.chunk, dense=dense)
+    omi.build(full, w.block, w.block, computable=w.mask.kind != "dense")
+    mask_info_ms = (time.perf_counter() - t_mi) * 1e3
+    del full
 
     qn = q.double().numpy()
     kn = k.double().numpy()
@@ -305,6 +315,7 @@ def cpu_baseline(w, q, k, v, dense, block_mask, budget_s=12.0):
         "cpu_model": model,
         "host_cores_usable": usable,
         "kind": "oracle",
+        "mask_info_ms": round(mask_info_ms, 1),
         "sample": (f"fp64 oracle on {rows_done} of {w.B * w.Hq * nq} query blocks (128 rows each, "
                    f"batch 0, longest block rows first, round-robin over heads) in {dt:.1f} s; "
                    f"FLOPs counted on computed blocks as for the GPU"),
