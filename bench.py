@@ -255,6 +255,29 @@ def launch_stats(step, torch, stream, n=20):
     return float(np.median(ms)), float(np.min(ms))
 
 
+def computed_work(w, block_mask, block_q=128, block_kv=128, backward=False):
+    """Blocks and FLOPs of one launch on workload w with a MaskInfo whose
+    block_mask is [Hm, nq', nk'] at block_q x block_kv: every 128 x 128
+    sub-block of a non-empty mask block is computed.  Forward: 2 products of
+    2 * 128 * 128 * D each per computed block; backward: 5 by the usual count
+    (S, dP, dV, dQ, dK) and 7 executed (S and dP in both kernels)."""
+    hm = block_mask.shape[0]
+    nq, nk = w.Sq // w.block, w.Skv // w.block
+    sub = (block_q // w.block) * (block_kv // w.block)   # 128 x 128 sub-blocks per mask block
+    computed_slots = int((block_mask > 0).sum()) * sub  # per mask head set
+    heads_per_mask = w.Hq if hm == 1 else 1
+    blocks_computed = computed_slots * heads_per_mask * w.B
+    res = {"blocks_computed": blocks_computed, "blocks_total": nq * nk * w.Hq * w.B}
+    if backward:
+        res["flops"] = blocks_computed * 5 * 2 * w.block * w.block * w.D
+        res["flops_exec"] = blocks_computed * 7 * 2 * w.block * w.block * w.D
+        res["flops_dense"] = w.B * w.Hq * w.Sq * w.Skv * 5 * 2 * w.D
+    else:
+        res["flops"] = res["flops_exec"] = blocks_computed * flops_per_block(w)
+        res["flops_dense"] = w.B * w.Hq * w.Sq * w.Skv * 2 * (w.D + w.Dv)
+    return res
+
+
 def flops_per_block(w):
     return 2 * w.block * w.block * (w.D + w.Dv)
 
@@ -444,20 +467,10 @@ def main():
     mask_ms = (time.perf_counter() - t0) * 1e3
     mi.upload()
     bm = mi.block_mask
-    hm = bm.shape[0]
     nq, nk = w.Sq // w.block, w.Skv // w.block
-    sub = (args.block_q // w.block) * (args.block_kv // w.block)   # 128 x 128 sub-blocks per mask block
-    computed_slots = int((bm > 0).sum()) * sub                # per mask head set
-    heads_per_mask = w.Hq if hm == 1 else 1
-    blocks_computed = computed_slots * heads_per_mask * w.B
-    blocks_total = nq * nk * w.Hq * w.B
-    flops = blocks_computed * flops_per_block(w)
-    flops_dense = w.B * w.Hq * w.Sq * w.Skv * 2 * (w.D + w.Dv)
-    flops_exec = flops
-    if args.backward:
-        flops = blocks_computed * 5 * 2 * w.block * w.block * w.D
-        flops_exec = blocks_computed * 7 * 2 * w.block * w.block * w.D
-        flops_dense = w.B * w.Hq * w.Sq * w.Skv * 5 * 2 * w.D
+    work = computed_work(w, bm, args.block_q, args.block_kv, args.backward)
+    blocks_computed, blocks_total = work["blocks_computed"], work["blocks_total"]
+    flops, flops_exec, flops_dense = work["flops"], work["flops_exec"], work["flops_dense"]
 
     from block_sparse_attention_make_amd.splash import plan_kv_splits
     from block_sparse_attention_make_amd.splash import plan_heads_per_workgroup
