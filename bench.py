@@ -88,29 +88,39 @@ def measured_traffic(workload, src=KERNEL_SRC):
 
 
 def mfma_probe(torch):
-    """bf16 MFMA TFLOP/s the GPU sustains (4 independent 32x32x16 chains per
-    wave, one wave per SIMD, 1.5 s warm); None if the probe library is absent."""
+    """bf16 MFMA TFLOP/s the GPU sustains (independent 32x32x16 chains, one
+    wave per SIMD, 1.5 s warm each): `tflops` on constant operands (the
+    matrix cores' ceiling at full clock) and `tflops_random_operands` on
+    changing random bf16 operands, like an attention step's, which draw more
+    power; None if the probe library is absent."""
     import ctypes
     path = os.path.join(ROOT, "block_sparse_attention_make_amd", "lib", "libsplash_probe.so")
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)
-    lib.splash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     props = torch.cuda.get_device_properties(0)
-    blocks, iters = props.multi_processor_count, 20000
+    blocks = props.multi_processor_count
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
-    t0 = time.time()
-    while time.time() - t0 < 1.5:
-        lib.splash_probe_mfma(blocks, iters, sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+
+    def rate(fn, iters, mfma_per_iter):
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        t0 = time.time()
+        while time.time() - t0 < 1.5:
+            fn(blocks, iters, sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn(blocks, iters, sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        b.record(stream)
         torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    lib.splash_probe_mfma(blocks, iters, sink.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
-    b.record(stream)
-    torch.cuda.synchronize()
-    flops = blocks * 4 * iters * 4 * 32768
-    return {"tflops": round(flops / (a.elapsed_time(b) * 1e-3) / 1e12, 1), "cus": blocks}
+        flops = blocks * 4 * iters * mfma_per_iter * 32768
+        return round(flops / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
+
+    res = {"tflops": rate(lib.splash_probe_mfma, 20000, 4), "cus": blocks}
+    if hasattr(lib, "splash_probe_mfma_random"):
+        res["tflops_random_operands"] = rate(lib.splash_probe_mfma_random, 10000, 8)
+    return res
 
 
 def read_probe(torch, nbytes):
@@ -643,6 +653,8 @@ def main():
         res["vs_baseline"] = None
     if probe is not None:
         res["mfma_probe"] = {**probe, "frac_of_probe": round(achieved / probe["tflops"], 4)}
+        if probe.get("tflops_random_operands"):
+            res["mfma_probe"]["frac_of_random_probe"] = round(achieved / probe["tflops_random_operands"], 4)
     if cold is not None:
         res["cold_cache"] = cold
     if merge_info is not None:

@@ -30,12 +30,59 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float *sink)
   sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// The same throughput with operands like an attention step's: eight sets of
+// pseudo-random bf16 values in [-2, 2) per lane, cycled so consecutive
+// matrix instructions see different data.  The matrix cores draw more power
+// on changing data than on the constant operands above, and under the GPU's
+// power limit the clock, and so the rate, drops.
+__device__ __forceinline__ float probe_value(unsigned x) {   // integer hash -> [-2, 2)
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return (static_cast<float>(x & 0xffffu) / 32768.f - 1.f) * 2.f;
+}
+
+__global__ __launch_bounds__(256) void mfma_probe_random_kernel(int iters, float *sink) {
+  bf16x8 a[8], b[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned s = (blockIdx.x * 256u + threadIdx.x) * 128u + k * 16u + i;
+      a[k][i] = static_cast<__bf16>(probe_value(s));
+      b[k][i] = static_cast<__bf16>(probe_value(s + 8u));
+    }
+  f32x16 c[4] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], b[k], c[k & 3], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += c[j][i];
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 // Launches `blocks` workgroups of 4 waves, each wave running `iters` x 4
 // MFMAs (32768 flops each) into sink[blocks * 256].
 extern "C" __attribute__((visibility("default"))) int splash_probe_mfma(int blocks, int iters, float *sink,
                                                                        void *stream) {
   if (blocks <= 0 || iters <= 0 || !sink) return 1;
   hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+// Launches `blocks` workgroups of 4 waves, each wave running `iters` x 8
+// MFMAs (32768 flops each) on changing random operands into sink[blocks * 256].
+extern "C" __attribute__((visibility("default"))) int splash_probe_mfma_random(int blocks, int iters, float *sink,
+                                                                              void *stream) {
+  if (blocks <= 0 || iters <= 0 || !sink) return 1;
+  hipLaunchKernelGGL(mfma_probe_random_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters,
+                     sink);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
