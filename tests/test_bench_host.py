@@ -87,3 +87,18 @@ def test_traffic_only_for_the_measured_source(tmp_path):
     assert bench.measured_traffic("no_such_workload") is None
     got = bench.measured_traffic("causal_mha_8k")
     assert got is None or got > 0
+
+
+def test_per_head_masks_count_each_head_once():
+    """A MaskInfo with one mask per query head (Hm = Hq): each head's own
+    non-empty blocks are counted once, not multiplied by the head count."""
+    import dataclasses
+    w = dataclasses.replace(synthetic.WORKLOADS["random_dense_2k"], Hq=2, Hkv=2, Sq=512, Skv=512)
+    rng = np.random.default_rng(11)
+    dense = rng.random((2, 512, 512)) < 0.1
+    dense[0, :, 256:] = False                  # head 0: the right half of the keys is empty
+    mi = make_mask_info("dense", 512, 512, dense=dense)
+    work = bench.computed_work(w, mi.block_mask)
+    labels = omi.classify_fast(dense, 128, 128)
+    assert labels.shape[0] == 2
+    assert work["blocks_computed"] == int((labels > 0).sum()) == 16 + 8
