@@ -349,8 +349,8 @@ def cpu_baseline(w, q, k, v, dense, block_mask, budget_s=12.0):
         "host_cores_usable": usable,
         "kind": "oracle",
         "mask_info_ms": round(mask_info_ms, 1),
-        "sample": (f"fp64 oracle on {rows_done} of {w.B * w.Hq * nq} query blocks (128 rows each, "
-                   f"batch 0, longest block rows first, round-robin over heads) in {dt:.1f} s; "
+        "sample": (f"fp64 oracle on {rows_done} of the {w.Hq * nq} query blocks of batch 0 (128 rows each, "
+                   f"longest block rows first, round-robin over heads) in {dt:.1f} s; "
                    f"FLOPs counted on computed blocks as for the GPU"),
     }
 
