@@ -454,9 +454,21 @@ namespace {
 // Largest byte count one buffer resource (32-bit size field) covers.
 constexpr int64_t kMaxHeadBytes = 0x7fffffffLL;
 
+// Head dims the bf16 forward runs zero-padded inside its 64- or 128-column
+// kernel: D and Dv multiples of 16 up to 128.  (The EasyDeL BlockSparseAttn
+// page types the key and value head dims apart, and on GPU sends only dims
+// that are multiples of 16 to its block-sparse kernel.)
+bool padded_dims_ok(int64_t D, int64_t Dv) {
+  return D % 16 == 0 && Dv % 16 == 0 && D >= 16 && Dv >= 16 && D <= 128 && Dv <= 128;
+}
+bool native_dims(int64_t D, int64_t Dv) { return D == Dv && (D == 64 || D == 128); }
+int64_t padded_kernel_dim(int64_t D, int64_t Dv) { return std::max(D, Dv) <= 64 ? 64 : 128; }
+
 // Checks shared by the forward and the backward entry points.
+
 splash_status validate_call(const splash_mask_info *mi, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
-                            int64_t Skv, int64_t D, int64_t Dv, int32_t dtype, float softmax_scale) {
+                            int64_t Skv, int64_t D, int64_t Dv, int32_t dtype, float softmax_scale,
+                            bool padded_ok = false) {
   if (!mi) return fail(SPLASH_EINVAL, "MaskInfo is NULL");
   if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || D <= 0 || Dv <= 0)
     return fail(SPLASH_EINVAL, "negative size or non-positive head dim");
@@ -471,8 +483,12 @@ splash_status validate_call(const splash_mask_info *mi, int64_t B, int64_t Hq, i
     return fail(SPLASH_EINVAL, "softmax_scale must be NaN (default) or finite and > 0");
   if (mi->block_q % 128 || mi->block_kv % 128)
     return fail(SPLASH_EUNSUPPORTED, "the kernels run MaskInfo blocks that are multiples of 128 x 128");
-  if (D != Dv || (D != 64 && D != 128))
-    return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
+  if (!native_dims(D, Dv)) {
+    if (!padded_ok || dtype != SPLASH_BF16)
+      return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
+    if (!padded_dims_ok(D, Dv))
+      return fail(SPLASH_EUNSUPPORTED, "the bf16 forward takes D and Dv that are multiples of 16 up to 128");
+  }
   const int64_t n_wg = B * Hq * (Sq / 128);
   if (n_wg > 0x7fffffffLL || B * Hq > 0x7fffffffLL || B * Hkv * (Skv / 128) > 0x7fffffffLL)
     return fail(SPLASH_EUNSUPPORTED, "grid too large");
@@ -513,6 +529,8 @@ FwdParams make_params(const splash_mask_info *mi, const DeviceCopy *dc, const vo
   p.Sq = Sq;
   p.Skv = Skv;
   p.D = static_cast<int32_t>(D);
+  p.dk = p.dv = static_cast<int32_t>(D);
+  p.padded = 0;
   p.group = static_cast<int32_t>(Hq / Hkv);
   p.nq = static_cast<int32_t>(mi->nq);
   p.width = static_cast<int32_t>(mi->width);
@@ -592,9 +610,14 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
                        int32_t num_sinks, int32_t kv_splits, int32_t heads_per_wg, void *workspace,
                        size_t workspace_bytes, void *hip_stream) {
   // ---- validation: nothing below launches or allocates until all passes ----
-  splash_status st = validate_call(mi, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale);
+  splash_status st = validate_call(mi, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale, true);
   if (st != SPLASH_OK) return st;
+  const bool padded = !native_dims(D, Dv);
   if (heads_per_wg < 0 || heads_per_wg > 2) return fail(SPLASH_EINVAL, "heads_per_workgroup must be 0, 1 or 2");
+  if (padded && heads_per_wg == 2)
+    return fail(SPLASH_EUNSUPPORTED, "head dims other than D == Dv in {64, 128} run one head per workgroup");
+  if (padded && kv_splits > 1)
+    return fail(SPLASH_EUNSUPPORTED, "head dims other than D == Dv in {64, 128} run without key splits");
   if (heads_per_wg == 2 && !head_pairs_possible(mi, Hq, Hkv, D, dtype))
     return fail(SPLASH_EUNSUPPORTED, "two heads per workgroup need bf16, D = 128, a computable mask with one "
                                      "mask head and an even GQA group");
@@ -637,8 +660,14 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
   p.num_sinks = num_sinks;
   p.kv_splits = kv_splits;
   p.items = dc->items[kv_splits];
-  const int32_t hpw = heads_per_wg != 0 ? heads_per_wg : auto_heads_per_wg(mi, B, Hq, Hkv, D, dtype, kv_splits);
+  const int32_t hpw = padded ? 1 : heads_per_wg != 0 ? heads_per_wg : auto_heads_per_wg(mi, B, Hq, Hkv, D, dtype, kv_splits);
   p.head_pairs = hpw == 2 ? 1 : 0;
+  if (padded) {
+    p.D = static_cast<int32_t>(padded_kernel_dim(D, Dv));
+    p.dk = static_cast<int32_t>(D);
+    p.dv = static_cast<int32_t>(Dv);
+    p.padded = 1;
+  }
   if (kv_splits > 1) {
     p.part_o = workspace;
     p.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + kv_splits * B * Hq * Sq * Dv * 2);

@@ -532,9 +532,42 @@ __device__ __forceinline__ uint32_t stage_voff(int wave, int lane, int i) {
   return static_cast<uint32_t>((lane / kLanesPerRow) * SG::kRowBytes + c * 16);
 }
 
-template <int D, bool IS_V, int W = kWWaves>
-__device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, int wave, int lane) {
+// Padded head dims (PAD): the stage keeps its D-column layout, but the array
+// in memory has rows of `mrow` bytes of which the first `mvalid` hold data.
+// Each segment then gets its own M0 and per-lane offsets (the instruction
+// offset can no longer step the LDS and the global address together); a
+// lane whose chunk lies in the padding gets an offset past the resource's
+// end, which reads zeros.
+template <int D, bool IS_V, int W>
+__device__ __forceinline__ void issue_seg_padded(char *lds, i32x4 res, int64_t row0, int wave, int lane, int i,
+                                                 uint32_t mrow, uint32_t mvalid) {
   using SG = Stage<D, W>;
+  constexpr int kRowsPerSeg = 1024 / SG::kRowBytes;
+  constexpr int kLanesPerRow = SG::kChunks;
+  const int seg = wave * SG::kInsts + i;
+  const int row = seg * kRowsPerSeg + lane / kLanesPerRow;
+  const int c = (lane % kLanesPerRow) ^ (IS_V ? SG::swz_v(row) : SG::swz_k(row));
+  const uint32_t voff = static_cast<uint32_t>(c * 16) < mvalid
+      ? static_cast<uint32_t>((row0 + row) * mrow) + static_cast<uint32_t>(c * 16)
+      : 0x80000000u;
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) char *)(lds + seg * 1024)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(res) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+template <int D, bool IS_V, int W = kWWaves, bool PAD = false>
+__device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, int wave, int lane,
+                                            uint32_t mrow = 0, uint32_t mvalid = 0) {
+  using SG = Stage<D, W>;
+  if constexpr (PAD) {
+#pragma unroll
+    for (int i = 0; i < SG::kInsts; ++i) issue_seg_padded<D, IS_V, W>(lds, res, row0, wave, lane, i, mrow, mvalid);
+    return;
+  }
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) char *)(lds + wave * SG::kInsts * 1024)));
   const uint32_t soff = static_cast<uint32_t>(row0 * SG::kRowBytes) + wave * SG::kInsts * 1024;
@@ -565,10 +598,15 @@ __device__ __forceinline__ void issue_stage(char *lds, i32x4 res, int64_t row0, 
 
 // One segment (1 KiB, segment I of this wave's share) of a stage, for
 // spreading a stage's loads over several slices of a step.
-template <int D, bool IS_V, int I, int W = kWWaves>
-__device__ __forceinline__ void issue_seg(char *lds, i32x4 res, int64_t row0, int wave, int lane) {
+template <int D, bool IS_V, int I, int W = kWWaves, bool PAD = false>
+__device__ __forceinline__ void issue_seg(char *lds, i32x4 res, int64_t row0, int wave, int lane,
+                                          uint32_t mrow = 0, uint32_t mvalid = 0) {
   using SG = Stage<D, W>;
   static_assert(I < SG::kInsts, "segment index");
+  if constexpr (PAD) {
+    issue_seg_padded<D, IS_V, W>(lds, res, row0, wave, lane, I, mrow, mvalid);
+    return;
+  }
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) char *)(lds + wave * SG::kInsts * 1024)));
   const uint32_t soff = static_cast<uint32_t>(row0 * SG::kRowBytes) + wave * SG::kInsts * 1024;
@@ -745,10 +783,11 @@ __device__ __forceinline__ void wait_at_most(int n) {
 // (which share their key/value head and, with one mask head, their walk)
 // in four waves over one set of K/V stages: each stage's loads serve 256
 // query rows instead of 128.
-template <int D, bool CAP, bool DENSE, int RU = 1>
+template <int D, bool CAP, bool DENSE, int RU = 1, bool PAD = false>
 __global__ __launch_bounds__(64 * kWWaves * RU, 1)
 void splash_fwd_wide(const FwdParams p) {
   static_assert(RU == 1 || (RU == 2 && D == 128 && !DENSE), "head pairs: D = 128, computable masks");
+  static_assert(!PAD || RU == 1, "padded head dims: one head per workgroup");
   constexpr int kW = kWWaves * RU;          // waves
   constexpr int kThr = 64 * kW;
   using SG = Stage<D, kW>;
@@ -810,10 +849,17 @@ void splash_fwd_wide(const FwdParams p) {
   const int row_in_block0 = 64 * wr + (lane & 31);      // qs = 0; qs = 1 adds 32
   const int64_t q_row0 = static_cast<int64_t>(r) * kBQ + row_in_block0;
 
-  const __bf16 *kg = static_cast<const __bf16 *>(p.k) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
-  const __bf16 *vg = static_cast<const __bf16 *>(p.v) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
-  const i32x4 k_res = make_rsrc(kg, p.Skv * D * 2);
-  const i32x4 v_res = make_rsrc(vg, p.Skv * D * 2);
+  // Head dims in memory: D itself, or (PAD) the caller's D and Dv, which the
+  // kernel runs zero-padded to D columns -- Q and the stages hold zeros in
+  // the padding, so QK sums only real columns, and the padded output columns
+  // are not stored.
+  const int mk = PAD ? p.dk : D;
+  const int mv = PAD ? p.dv : D;
+  const __bf16 *kg = static_cast<const __bf16 *>(p.k) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * mk;
+  const __bf16 *vg = static_cast<const __bf16 *>(p.v) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * mv;
+  const i32x4 k_res = make_rsrc(kg, p.Skv * mk * 2);
+  const i32x4 v_res = make_rsrc(vg, p.Skv * mv * 2);
+  const uint32_t krow = static_cast<uint32_t>(mk * 2), vrow = static_cast<uint32_t>(mv * 2);
   const bool has_bits = DENSE && p.pmb_bits != nullptr;
   const i32x4 m_res = make_rsrc(has_bits ? static_cast<const void *>(p.pmb_bits) : p.k,
                                 has_bits ? p.pmb_bits_bytes : 0);
@@ -837,13 +883,24 @@ void splash_fwd_wide(const FwdParams p) {
   // latencies overlap.  (A split with no block loads a block it never uses.)
   const int dn_first = items[item_at + 3];
   const int mn_first = has_bits ? items[item_at + 4] : 0;
+  if constexpr (PAD) {
+    // the padding columns of every stage start (and stay) zero; written and
+    // published before any load into the stages
+#pragma unroll
+    for (int i = 0; i < kStages * SG::kBytes / (16 * kThr); ++i) {
+      reinterpret_cast<u32x4 *>(&k_st[0][0])[tid + kThr * i] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4 *>(&v_st[0][0])[tid + kThr * i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int t = 0; t < kSteps; ++t) {
-    issue_stage<D, false, kW>(k_st[t], k_res, static_cast<int64_t>(dn_first) * kBK + kSK * t, wave, lane);
+    issue_stage<D, false, kW, PAD>(k_st[t], k_res, static_cast<int64_t>(dn_first) * kBK + kSK * t, wave, lane, krow,
+                                   krow);
     if (has_bits) issue_mask(mn_first, t, t);
   }
-  issue_stage<D, true, kW>(v_st[0], v_res, static_cast<int64_t>(dn_first) * kBK, wave, lane);
-  issue_stage<D, true, kW>(v_st[1], v_res, static_cast<int64_t>(dn_first) * kBK + kSK, wave, lane);
+  issue_stage<D, true, kW, PAD>(v_st[0], v_res, static_cast<int64_t>(dn_first) * kBK, wave, lane, vrow, vrow);
+  issue_stage<D, true, kW, PAD>(v_st[1], v_res, static_cast<int64_t>(dn_first) * kBK + kSK, wave, lane, vrow, vrow);
   static_assert(kSteps == kStages, "the prologue fills every K stage");
 
   // The other V stages start as zeros: the first step's PV(-1) reads the
@@ -859,13 +916,17 @@ void splash_fwd_wide(const FwdParams p) {
     // All Q loads (and the rows' positions) go out before anything waits
     // for them: a register move placed after each load would make every
     // load wait for the one before it.
-    const __bf16 *qg = static_cast<const __bf16 *>(p.q) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row0) * D;
+    const __bf16 *qg = static_cast<const __bf16 *>(p.q) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row0) * mk;
     bf16x8 x[2][kKS];
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks)
-        x[qs][ks] = *reinterpret_cast<const bf16x8 *>(qg + static_cast<int64_t>(32 * qs) * D + 16 * ks + 8 * half);
+      for (int ks = 0; ks < kKS; ++ks) {
+        if (!PAD || 16 * ks + 8 * half < mk)
+          x[qs][ks] = *reinterpret_cast<const bf16x8 *>(qg + static_cast<int64_t>(32 * qs) * mk + 16 * ks + 8 * half);
+        else
+          x[qs][ks] = bf16x8{};   // padding columns: zero
+      }
     if constexpr (!DENSE) {
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) qpos_ld[qs] = p.q_seq[q_row0 + 32 * qs];
@@ -1203,10 +1264,10 @@ void splash_fwd_wide(const FwdParams p) {
         return SG::kInsts + (has_bits ? 1 : 0) + (w >= -2 ? SG::kInsts : 0);
       };
       auto load_k = [&](int stage, int kv, int t) {
-        issue_stage<D, false, kW>(k_st[stage], k_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane);
+        issue_stage<D, false, kW, PAD>(k_st[stage], k_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane, krow, krow);
       };
       auto load_v = [&](int stage, int kv, int t) {
-        issue_stage<D, true, kW>(v_st[stage], v_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane);
+        issue_stage<D, true, kW, PAD>(v_st[stage], v_res, static_cast<int64_t>(kv) * kBK + kSK * t, wave, lane, vrow, vrow);
       };
       auto load_m = [&](int stage, int mn, int t) {
         if (has_bits) issue_mask(mn, t, stage);
@@ -1216,30 +1277,30 @@ void splash_fwd_wide(const FwdParams p) {
         const int64_t r0 = static_cast<int64_t>(kv) * kBK + kSK * t;
         if constexpr (SG::kInsts == 4) {
           if (h == 0) {
-            issue_seg<D, false, 0, kW>(k_st[stage], k_res, r0, wave, lane);
-            issue_seg<D, false, 1, kW>(k_st[stage], k_res, r0, wave, lane);
+            issue_seg<D, false, 0, kW, PAD>(k_st[stage], k_res, r0, wave, lane, krow, krow);
+            issue_seg<D, false, 1, kW, PAD>(k_st[stage], k_res, r0, wave, lane, krow, krow);
           } else {
-            issue_seg<D, false, 2, kW>(k_st[stage], k_res, r0, wave, lane);
-            issue_seg<D, false, 3, kW>(k_st[stage], k_res, r0, wave, lane);
+            issue_seg<D, false, 2, kW, PAD>(k_st[stage], k_res, r0, wave, lane, krow, krow);
+            issue_seg<D, false, 3, kW, PAD>(k_st[stage], k_res, r0, wave, lane, krow, krow);
           }
         } else {
-          if (h == 0) issue_seg<D, false, 0, kW>(k_st[stage], k_res, r0, wave, lane);
-          else issue_seg<D, false, 1, kW>(k_st[stage], k_res, r0, wave, lane);
+          if (h == 0) issue_seg<D, false, 0, kW, PAD>(k_st[stage], k_res, r0, wave, lane, krow, krow);
+          else issue_seg<D, false, 1, kW, PAD>(k_st[stage], k_res, r0, wave, lane, krow, krow);
         }
       };
       auto load_v_half = [&](int h, int stage, int kv, int t) {
         const int64_t r0 = static_cast<int64_t>(kv) * kBK + kSK * t;
         if constexpr (SG::kInsts == 4) {
           if (h == 0) {
-            issue_seg<D, true, 0, kW>(v_st[stage], v_res, r0, wave, lane);
-            issue_seg<D, true, 1, kW>(v_st[stage], v_res, r0, wave, lane);
+            issue_seg<D, true, 0, kW, PAD>(v_st[stage], v_res, r0, wave, lane, vrow, vrow);
+            issue_seg<D, true, 1, kW, PAD>(v_st[stage], v_res, r0, wave, lane, vrow, vrow);
           } else {
-            issue_seg<D, true, 2, kW>(v_st[stage], v_res, r0, wave, lane);
-            issue_seg<D, true, 3, kW>(v_st[stage], v_res, r0, wave, lane);
+            issue_seg<D, true, 2, kW, PAD>(v_st[stage], v_res, r0, wave, lane, vrow, vrow);
+            issue_seg<D, true, 3, kW, PAD>(v_st[stage], v_res, r0, wave, lane, vrow, vrow);
           }
         } else {
-          if (h == 0) issue_seg<D, true, 0, kW>(v_st[stage], v_res, r0, wave, lane);
-          else issue_seg<D, true, 1, kW>(v_st[stage], v_res, r0, wave, lane);
+          if (h == 0) issue_seg<D, true, 0, kW, PAD>(v_st[stage], v_res, r0, wave, lane, vrow, vrow);
+          else issue_seg<D, true, 1, kW, PAD>(v_st[stage], v_res, r0, wave, lane, vrow, vrow);
         }
       };
 
@@ -1391,7 +1452,7 @@ void splash_fwd_wide(const FwdParams p) {
         const int key0u = ent_kv(u / kSteps) * kBK + kSK * (u % kSteps);
         wait_vmcnt<0>();
         lds_barrier();
-        issue_stage<D, false, kW>(k_st[0], k_res, key0u, wave, lane);
+        issue_stage<D, false, kW, PAD>(k_st[0], k_res, key0u, wave, lane, krow, krow);
         if (has_bits) issue_mask(ent_mn(u / kSteps), u % kSteps, 0);
         wait_vmcnt<0>();
         lds_barrier();
@@ -1457,17 +1518,19 @@ void splash_fwd_wide(const FwdParams p) {
     }
     // this wave's rows only: its LDS writes and reads complete in order
     const int64_t row_w = static_cast<int64_t>(r) * kBQ + 64 * wr;   // the wave's first row
+    const int64_t ostride = PAD ? mv : D;   // output row in elements (PAD: the caller's Dv)
     char *dst = n_split > 1
         ? reinterpret_cast<char *>(static_cast<__bf16 *>(p.part_o) +
-                                   (((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + row_w) * D)
+                                   (((static_cast<int64_t>(split) * p.B + b) * p.Hq + hq) * p.Sq + row_w) * ostride)
         : reinterpret_cast<char *>(static_cast<__bf16 *>(p.out) +
-                                   ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + row_w) * D);
+                                   ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + row_w) * ostride);
     constexpr int kRowsPer = 1024 / kRB;   // rows per instruction
 #pragma unroll
     for (int i = 0; i < 64 / kRowsPer; ++i) {
       const int rr = kRowsPer * i + lane / kChunks, c = lane % kChunks;
       const u32x4 v = *reinterpret_cast<const u32x4 *>(st + rr * kRB + ((c ^ swz_o(rr)) * 16));
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + rr * kRB + c * 16));
+      if (!PAD || c * 8 < mv)   // PAD: the padding columns stay unstored
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + rr * ostride * 2 + c * 16));
     }
   }
 #pragma unroll
@@ -1562,6 +1625,12 @@ hipError_t launch_wide(const FwdParams &p, hipStream_t stream) {
       hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE, 2>), dim3(static_cast<unsigned>(blocks)),
                          dim3(2 * kWThreads), 0, stream, p);
     }
+  }
+  if (p.padded) {   // one split, one head per workgroup (checked by the caller)
+    const int64_t blocks = p.B * p.Hq * p.nq;
+    hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE, 1, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kWThreads), 0, stream, p);
+    return hipGetLastError();
   }
   if (!p.head_pairs || D != 128 || DENSE) {
     const int64_t blocks = p.B * p.Hq * p.nq * p.kv_splits;

@@ -12,7 +12,11 @@ struct FwdParams {
   void *out;
   float *lse;             // may be null
   int64_t B, Hq, Hkv, Sq, Skv;
-  int32_t D;              // == Dv
+  int32_t D;              // the kernel's head dim (64 or 128); == Dv unless padded
+  // Padded head dims (bf16 forward): q and k rows hold dk elements and v and
+  // out rows dv, each a multiple of 16 up to D; the kernel runs them
+  // zero-padded to D columns.  padded = 0: dk == dv == D.
+  int32_t dk, dv, padded;
   int32_t group;          // Hq / Hkv
   int32_t nq, width, hm;  // MaskInfo grid: block rows, grid width W, mask heads
   const void *bm, *dn, *mn;           // device MaskInfo index arrays (downcast types)

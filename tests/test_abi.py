@@ -55,8 +55,13 @@ def _fwd_args(info, **over):
 @pytest.mark.parametrize("over,status", [
     (dict(Sq=256), splash.EINVAL),                 # does not match the MaskInfo
     (dict(Hq=3, Hkv=2), splash.EINVAL),            # head ratio
-    (dict(D=96, Dv=96), splash.EUNSUPPORTED),      # head dim not built
-    (dict(D=128, Dv=64), splash.EUNSUPPORTED),
+    (dict(D=96, Dv=96, dtype=splash.F32), splash.EUNSUPPORTED),   # float32 runs D == Dv in {64, 128}
+    (dict(D=128, Dv=64, dtype=splash.F32), splash.EUNSUPPORTED),
+    (dict(D=72, Dv=72), splash.EUNSUPPORTED),      # bf16 pads multiples of 16 only
+    (dict(D=128, Dv=120), splash.EUNSUPPORTED),
+    (dict(D=144, Dv=144), splash.EUNSUPPORTED),    # above the 128-column kernel
+    (dict(D=64, Dv=256), splash.EUNSUPPORTED),
+    (dict(D=8, Dv=8), splash.EUNSUPPORTED),
     (dict(dtype=7), splash.EINVAL),
     (dict(scale=-1.0), splash.EINVAL),
     (dict(scale=math.inf), splash.EINVAL),
@@ -248,6 +253,8 @@ def test_static_decode_rejects_more_than_its_scratch_before_running():
     (dict(splits=2, ws_bytes=1024), splash.EINVAL),           # too small
     (dict(splits=2, ws=24), splash.EINVAL),                   # misaligned
     (dict(splits=2, Sq=256), splash.EINVAL),                  # MaskInfo mismatch, as splash_fwd
+    (dict(splits=2, D=96, Dv=96), splash.EUNSUPPORTED),       # padded head dims run unsplit
+    (dict(splits=2, D=128, Dv=64), splash.EUNSUPPORTED),
 ])
 def test_fwd_split_validation_errors_before_launch(over, status):
     lib = splash.load_library()
@@ -282,6 +289,8 @@ def test_fwd_workspace_size_and_plan_on_host():
     ("causal", dict(heads=2, Hq=6, Hkv=2), splash.EUNSUPPORTED),     # odd group
     ("causal", dict(heads=2, D=64, Dv=64), splash.EUNSUPPORTED),     # D = 64
     ("causal", dict(heads=2, dtype=splash.F32), splash.EUNSUPPORTED),
+    ("causal", dict(heads=2, Dv=96), splash.EUNSUPPORTED),           # padded Dv: one head per workgroup
+    ("causal", dict(heads=2, D=96, Dv=96), splash.EUNSUPPORTED),
     ("dense", dict(heads=2), splash.EUNSUPPORTED),                   # dense mask
 ])
 def test_fwd_tiled_validation_errors_before_launch(mask, over, status):

@@ -1,0 +1,112 @@
+"""GPU parity for head dims other than D == Dv in {64, 128}: the bf16 forward
+runs any D and Dv that are multiples of 16 up to 128 zero-padded inside its
+64- or 128-column kernel (the EasyDeL BlockSparseAttn signature types the
+query/key head dim and the value head dim apart).
+
+Each case is compared element by element with the fp64 oracle (whose
+attention is pinned with Dv != D and the default scale of the true D) at the
+bf16 tolerance, 2e-2 max-abs on out and lse.  The cases cover both padded
+kernels, with and without the soft cap, computable and dense masks, GQA /
+MQA, Sq != Skv, attention sinks, and the default softmax scale (D ** -0.5 of
+the caller's D, not of the padded one).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_make_amd import make_mask_info, splash_fwd, synthetic
+from tests.gpu_cases import TOL, compare, oracle_full, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+CASES = [
+    # name, seed, B, Hq, Hkv, Sq, Skv, D, Dv, mask kwargs, cap
+    # 64-column kernel (D, Dv <= 64)
+    ("d32_causal_mqa_b2", 201, 2, 2, 1, 384, 384, 32, 32, dict(kind="causal"), None),
+    ("d48_local_cap", 202, 1, 4, 2, 640, 640, 48, 48, dict(kind="local", left=200, right=50), 5.0),
+    ("d16_dv48_chunked", 203, 1, 2, 2, 768, 768, 16, 48, dict(kind="chunked", chunk=300), None),
+    ("d64_dv32_causal_rect", 204, 1, 2, 2, 256, 640, 64, 32, dict(kind="causal"), None),
+    # 128-column kernel
+    ("d96_causal_gqa", 205, 1, 4, 2, 640, 640, 96, 96, dict(kind="causal"), None),
+    ("d128_dv64_local", 206, 1, 2, 2, 768, 768, 128, 64, dict(kind="local", left=None, right=100), None),
+    ("d64_dv128_chunked_cap", 207, 1, 4, 2, 1024, 1024, 64, 128, dict(kind="chunked", chunk=300), 5.0),
+    ("d80_dv112_causal_rect", 208, 1, 2, 1, 640, 256, 80, 112, dict(kind="causal"), None),
+    ("d112_dv16_full_cap", 209, 1, 2, 2, 384, 384, 112, 16, dict(kind="local", left=None, right=None), 2.0),
+    ("d96_long_causal", 210, 1, 2, 2, 2048, 2048, 96, 96, dict(kind="causal"), None),
+    ("d96_one_block", 211, 1, 1, 1, 128, 128, 96, 96, dict(kind="causal"), None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_padded_head_dims_parity(case):
+    """kv_splits="auto": these small grids would split with native dims; the
+    binding runs padded dims unsplit."""
+    name, seed, B, Hq, Hkv, Sq, Skv, D, Dv, mk, cap = case
+    q, k, v = synthetic.make_qkv(seed, B, Hq, Hkv, Sq, Skv, D, Dv)
+    o, l, _ = run_gpu(q, k, v, cap=cap, **mk)
+    assert o.shape == (B, Hq, Sq, Dv)
+    o_ref, l_ref = oracle_full(q, k, v, cap=cap, **mk)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], name)
+
+
+@pytest.mark.parametrize("D,Dv,cap", [(48, 64, None), (96, 80, 3.0)], ids=["kernel64", "kernel128_cap"])
+@pytest.mark.parametrize("hm", [1, 2])
+def test_padded_head_dims_dense(D, Dv, cap, hm):
+    """Dense masks (partial blocks read from the mask bits) in both padded
+    kernels, shared and per-head masks, with an empty and a full block."""
+    rng = np.random.default_rng(220 + hm + D)
+    q, k, v = synthetic.make_qkv(221 + D, 1, 2, 2, 512, 640, D, Dv)
+    dense = synthetic.random_dense_mask(rng, hm, 512, 640, 0.2, force_diagonal=True)
+    dense[:, 0:128, 128:256] = True
+    dense[:, 128:256, 0:128] = False
+    o, l, _ = run_gpu(q, k, v, "dense", dense=dense, cap=cap)
+    o_ref, l_ref = oracle_full(q, k, v, "dense", dense=dense, cap=cap)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], f"dense D={D} Dv={Dv} hm={hm}")
+
+
+@pytest.mark.parametrize("D,Dv", [(32, 48), (96, 112)])
+def test_padded_head_dims_sinks(D, Dv):
+    """Attention sinks per key/value head, with a fully masked block row (its
+    rows then hold only the sinks: out 0, lse = log sum exp of the sinks)."""
+    q, k, v = synthetic.make_qkv(230 + D, 1, 4, 2, 384, 512, D, Dv)
+    dense = np.ones((1, 384, 512), dtype=bool)
+    dense[0, 128:256, :] = False
+    aux = np.array([[0.5, -1.0], [1.5, -np.inf]], dtype=np.float32)
+    o, l, _ = run_gpu(q, k, v, "dense", dense=dense, aux=aux)
+    o_ref, l_ref = oracle_full(q, k, v, "dense", dense=dense, aux=aux)
+    compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], f"sinks D={D} Dv={Dv}")
+    assert (o[:, :, 128:256] == 0).all()
+
+
+def test_padded_head_dims_explicit_scale_and_neighbours_untouched():
+    """An explicit softmax_scale, and an output buffer carved from a larger
+    one: the kernel writes exactly [B, Hq, Sq, Dv] elements, nothing past
+    them (the 128-column kernel must not store its padding columns)."""
+    B, Hq, Hkv, S, D, Dv = 1, 2, 2, 384, 96, 80
+    q, k, v = synthetic.make_qkv(240, B, Hq, Hkv, S, S, D, Dv)
+    mi = make_mask_info("causal", S, S)
+    n = B * Hq * S * Dv
+    buf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[:n].view(B, Hq, S, Dv)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
+    splash_fwd(q.to(DEV), k.to(DEV), v.to(DEV), mi, softmax_scale=0.05, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert (buf[n:] == 7.0).all()
+    o_ref, l_ref = oracle_full(q, k, v, "causal", scale=0.05)
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, TOL[torch.bfloat16], "scale 0.05")
+
+
+def test_padded_head_dims_refuse_splits():
+    q, k, v = synthetic.make_qkv(250, 1, 2, 2, 256, 256, 96, 96)
+    mi = make_mask_info("causal", 256, 256)
+    with pytest.raises(RuntimeError, match="key splits"):
+        splash_fwd(q.to(DEV), k.to(DEV), v.to(DEV), mi, kv_splits=2)
