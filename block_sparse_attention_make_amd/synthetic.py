@@ -79,6 +79,11 @@ WORKLOADS["causal_growing_8k"] = Workload("causal_growing_8k", 1, 16, 16, 8192, 
 WORKLOADS["dense_empty_rows_2k"] = Workload("dense_empty_rows_2k", 1, 8, 8, 2048, 2048, 128, 128, "bf16",
                                             MaskSpec("dense", dense_p=0.1, empty_every=16), seed=8)
 
+# The causal 8k shape at head dims the forward runs zero-padded (D = Dv = 96
+# inside the 128-column kernel): what a head dim off the kernel's own costs.
+WORKLOADS["causal_d96_8k"] = Workload("causal_d96_8k", 1, 16, 16, 8192, 8192, 96, 96, "bf16",
+                                      MaskSpec("causal"), seed=9)
+
 
 # Decode (one query per head against a key/value cache, every key allowed):
 # a GQA serving shape, measured against HBM bandwidth.

@@ -25,6 +25,7 @@ EXPECTED = {
     "local_gqa_8k": (17_280, 144_955_146_240),
     "chunked_gqa_16k_cap": (34_816, 292_057_776_128),
     "random_dense_2k": (2_048, 17_179_869_184),
+    "causal_d96_8k": (33_280, 209_379_655_680),     # causal blocks at D = Dv = 96
 }
 
 

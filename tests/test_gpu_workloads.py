@@ -14,7 +14,7 @@ from tests.gpu_cases import TOL, compare, mask_rows_fn, oracle_by_block_rows, ru
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["causal_mha_8k", "local_gqa_8k", "chunked_gqa_16k_cap", "random_dense_2k"]
+FULL = ["causal_mha_8k", "local_gqa_8k", "chunked_gqa_16k_cap", "random_dense_2k", "causal_d96_8k"]
 
 
 @pytest.fixture(autouse=True)
