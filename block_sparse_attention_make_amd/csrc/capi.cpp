@@ -811,7 +811,7 @@ extern "C" SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void 
                                                void *hip_stream) {
   clear_error();
   // ---- validation: nothing below launches or allocates until all passes ----
-  splash_status st = validate_call(mi, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale);
+  splash_status st = validate_call(mi, B, Hq, Hkv, Sq, Skv, D, Dv, dtype, softmax_scale, true);
   if (st != SPLASH_OK) return st;
   if (dtype != SPLASH_BF16) return fail(SPLASH_EUNSUPPORTED, "the backward kernels run bf16 only");
   if (B == 0 || Hq == 0 || (Sq == 0 && Skv == 0)) return SPLASH_OK;
@@ -834,6 +834,12 @@ extern "C" SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void 
   BwdParams p{};
   p.f = make_params(mi, dc, q, k, v, const_cast<void *>(out), const_cast<float *>(lse), B, Hq, Hkv, Sq, Skv, D,
                     resolve_scale(softmax_scale, D), logits_soft_cap);
+  if (!native_dims(D, Dv)) {   // run zero-padded, as the forward does
+    p.f.D = static_cast<int32_t>(padded_kernel_dim(D, Dv));
+    p.f.dk = static_cast<int32_t>(D);
+    p.f.dv = static_cast<int32_t>(Dv);
+    p.f.padded = 1;
+  }
   p.dout = dout;
   p.delta = delta;
   p.dq = dq;

@@ -181,12 +181,19 @@ __device__ __forceinline__ void mfma_drain(f32x16 &a, f32x16 &b) {
 }
 
 // B operands of a row block kept in registers: lane (j, half) holds row
-// row0 + j, elements 16 ks + 8 half .. + 7.
-template <int D>
-__device__ __forceinline__ void load_rows_b(bf16x8 (&dst)[D / 16], const __bf16 *g, int lane, int half) {
+// row0 + j, elements 16 ks + 8 half .. + 7.  PAD: the rows hold `mdim`
+// elements in memory (a multiple of 16, at most D); the rest read as zeros.
+template <int D, bool PAD = false>
+__device__ __forceinline__ void load_rows_b(bf16x8 (&dst)[D / 16], const __bf16 *g, int lane, int half,
+                                            int mdim = D) {
+  const int stride = PAD ? mdim : D;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    dst[ks] = *reinterpret_cast<const bf16x8 *>(g + static_cast<int64_t>(lane & 31) * D + 16 * ks + 8 * half);
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if (!PAD || 16 * ks + 8 * half < mdim)
+      dst[ks] = *reinterpret_cast<const bf16x8 *>(g + static_cast<int64_t>(lane & 31) * stride + 16 * ks + 8 * half);
+    else
+      dst[ks] = bf16x8{};
+  }
 }
 
 // Soft-cap pieces of one score: base-2 capped logit and the derivative
@@ -208,9 +215,11 @@ __device__ __forceinline__ void capped(float x, float kc2, float cap_out, float 
 // own region; 16-byte chunks swizzled by row) and stores them back 16 bytes
 // per lane, whole rows per instruction (non-temporal: the kernel does not
 // read them again).  The wave's LDS writes and reads complete in order.
-template <int D>
+// PAD: the array's rows hold `mdim` elements (a multiple of 16, at most D);
+// the padding columns are not stored.
+template <int D, bool PAD = false>
 __device__ __forceinline__ void store_t_rows(char *lds, __bf16 *g, const f32x16 (&acc)[D / 32], float mul, int lane,
-                                             int half) {
+                                             int half, int mdim = D) {
   constexpr int kRB = D * 2, kChunks = kRB / 16;
   const int rr = lane & 31;
 #pragma unroll
@@ -227,20 +236,26 @@ __device__ __forceinline__ void store_t_rows(char *lds, __bf16 *g, const f32x16 
   for (int i = 0; i < 32 / kRowsPer; ++i) {
     const int r2 = kRowsPer * i + lane / kChunks, c = lane % kChunks;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(lds + r2 * kRB + ((c ^ (r2 & (kChunks - 1))) * 16));
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(g) + r2 * kRB + c * 16));
+    if (!PAD || c * 8 < mdim)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(g) +
+                                                                r2 * (PAD ? mdim * 2 : kRB) + c * 16));
   }
 }
 
 // ---- delta: di = <dout_i, out_i> ------------------------------------------
+// Rows of dv elements (a multiple of 8, at most D); D / 8 threads per row.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_delta(const __bf16 *o, const __bf16 *dout, float *delta, int64_t rows) {
+__global__ __launch_bounds__(256) void bwd_delta(const __bf16 *o, const __bf16 *dout, float *delta, int64_t rows,
+                                                 int dv) {
   constexpr int kPerRow = D / 8;   // threads per row, 8 elements each
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t row = t / kPerRow;
+  const int c = static_cast<int>(t % kPerRow);
   float acc = 0.f;
-  if (row < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4 *>(o + t * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4 *>(dout + t * 8);
+  if (row < rows && c * 8 < dv) {
+    const int64_t at = row * dv + c * 8;
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(o + at);
+    const u32x4 b = *reinterpret_cast<const u32x4 *>(dout + at);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc += __uint_as_float(a[i] << 16) * __uint_as_float(b[i] << 16);
@@ -249,7 +264,7 @@ __global__ __launch_bounds__(256) void bwd_delta(const __bf16 *o, const __bf16 *
   }
 #pragma unroll
   for (int m = kPerRow / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && (t % kPerRow) == 0) delta[row] = acc;
+  if (row < rows && c == 0) delta[row] = acc;
 }
 
 // ---- staging ----------------------------------------------------------------
@@ -291,10 +306,40 @@ __device__ __forceinline__ uint32_t seg_voff(int seg, int lane) {
 // offset advances both the LDS and the global address).  Issued from inline
 // assembly, awaited with an explicit vmcnt wait before the barrier that
 // publishes the buffer.
-template <int D, int ROWS = kBlk>
-__device__ __forceinline__ void issue_tile(char *lds, i32x4 res, uint32_t goff, int wave, int lane) {
-  constexpr int kSegs = ROWS * BTile<D>::kRowBytes / 1024 / 4;   // per wave
+//
+// PAD: the array's rows hold `mrow` bytes in memory (a multiple of 32, at
+// most the tile's row), and the tile starts at array row `row0` (goff is
+// unused).  Each segment then takes its own M0 and per-lane offsets (the
+// packed row stride no longer matches the tile's, so one instruction offset
+// cannot step both addresses), and a lane whose chunk lies in the padding
+// gets an offset past the resource's end, which reads zeros; the tiles'
+// padding columns are zeroed before their first load and stay zero.
+template <int D, int ROWS = kBlk, bool PAD = false>
+__device__ __forceinline__ void issue_tile(char *lds, i32x4 res, uint32_t goff, int wave, int lane,
+                                           uint32_t row0 = 0, uint32_t mrow = 0) {
+  using T = BTile<D>;
+  constexpr int kSegs = ROWS * T::kRowBytes / 1024 / 4;   // per wave
   static_assert(kSegs % 4 == 0, "whole groups of four segments per wave");
+  if constexpr (PAD) {
+    constexpr int kRowsPerSeg = 1024 / T::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < kSegs; ++i) {
+      const int seg = wave * kSegs + i;
+      const int row = seg * kRowsPerSeg + lane / T::kChunks;
+      const int c = (lane % T::kChunks) ^ T::swz(row);
+      const uint32_t voff = static_cast<uint32_t>(c * 16) < mrow
+          ? (row0 + static_cast<uint32_t>(row)) * mrow + static_cast<uint32_t>(c * 16)
+          : 0x80000000u;
+      const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) char *)(lds + seg * 1024)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(m0), "v"(voff), "s"(res) : "memory", "m0");
+#pragma clang diagnostic pop
+    }
+    return;
+  }
 #pragma unroll
   for (int g = 0; g < kSegs / 4; ++g) {
     const int seg0 = wave * kSegs + 4 * g;
@@ -348,7 +393,11 @@ __device__ __forceinline__ void xcd_map(int pid, int units, int &unit, int &rank
 // query blocks to visit -- every (query head g of the group, entry e of the
 // transposed list of mask head hm(g)) -- stream through two LDS buffers: the
 // next block's Q and dO tiles load while the current one is computed.
-template <int D, bool CAP, bool DENSE>
+// PAD: head dims other than the kernel's D (q, k, dq, dk rows of f.dk
+// elements, v, dout, dv rows of f.dv), run zero-padded to D columns: the
+// padding of every operand is zero, so every product sums only real
+// columns, and the padding columns of dK and dV are not stored.
+template <int D, bool CAP, bool DENSE, bool PAD>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
   using T = BTile<D>;
   constexpr int kKS = D / 16, kDT = D / 32;
@@ -371,11 +420,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
   const int c = p.col_order[rank];
   const int b = bh / static_cast<int>(f.Hkv), hkv = bh % static_cast<int>(f.Hkv);
   const int64_t key0 = static_cast<int64_t>(c) * kBlk + 32 * wave;   // the wave's first key
-  const int64_t kv_off = ((static_cast<int64_t>(b) * f.Hkv + hkv) * f.Skv + key0) * D;
+  const int mk = PAD ? f.dk : D, mv = PAD ? f.dv : D;   // row lengths in memory
+  const int64_t kv_row = (static_cast<int64_t>(b) * f.Hkv + hkv) * f.Skv + key0;
 
   bf16x8 kb[kKS], vb[kKS];
-  load_rows_b<D>(kb, static_cast<const __bf16 *>(f.k) + kv_off, lane, half);
-  load_rows_b<D>(vb, static_cast<const __bf16 *>(f.v) + kv_off, lane, half);
+  load_rows_b<D, PAD>(kb, static_cast<const __bf16 *>(f.k) + kv_row * mk, lane, half, mk);
+  load_rows_b<D, PAD>(vb, static_cast<const __bf16 *>(f.v) + kv_row * mv, lane, half, mv);
+  if constexpr (PAD) {
+    // the tiles' padding columns start (and stay) zero; written and
+    // published before any load into the tiles
+    constexpr int kVec = 2 * 2 * T::kBytes / 16;
+#pragma unroll
+    for (int i = 0; i < kVec / kThreads; ++i)
+      reinterpret_cast<u32x4 *>(&qdo_t[0][0][0])[tid + kThreads * i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
   f32x16 dk[kDT], dv[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
@@ -453,12 +512,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
   };
   auto issue = [&](int buf, int gg, int r) {
     const int hq = hkv * f.group + gg;
-    const int64_t head = (static_cast<int64_t>(b) * f.Hq + hq) * f.Sq * D;
-    const i32x4 qr = make_rsrc(static_cast<const __bf16 *>(f.q) + head, f.Sq * D * 2);
-    const i32x4 dr = make_rsrc(static_cast<const __bf16 *>(p.dout) + head, f.Sq * D * 2);
-    const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(r) * T::kBytes);
-    issue_tile<D>(qdo_t[buf][0], qr, goff, wave, lane);
-    issue_tile<D>(qdo_t[buf][1], dr, goff, wave, lane);
+    const int64_t head = (static_cast<int64_t>(b) * f.Hq + hq) * f.Sq;   // the head's first row
+    const i32x4 qr = make_rsrc(static_cast<const __bf16 *>(f.q) + head * mk, f.Sq * mk * 2);
+    const i32x4 dr = make_rsrc(static_cast<const __bf16 *>(p.dout) + head * mv, f.Sq * mv * 2);
+    if constexpr (PAD) {
+      const uint32_t row0 = static_cast<uint32_t>(r) * kBlk;
+      issue_tile<D, kBlk, true>(qdo_t[buf][0], qr, 0, wave, lane, row0, static_cast<uint32_t>(mk * 2));
+      issue_tile<D, kBlk, true>(qdo_t[buf][1], dr, 0, wave, lane, row0, static_cast<uint32_t>(mv * 2));
+    } else {
+      const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(r) * T::kBytes);
+      issue_tile<D>(qdo_t[buf][0], qr, goff, wave, lane);
+      issue_tile<D>(qdo_t[buf][1], dr, goff, wave, lane);
+    }
   };
 
   // The walk runs one pair ahead of the tiles: the list entry of the pair
@@ -633,8 +698,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
   // its own 2 x 32 rows.
   char *st = &qdo_t[0][0][0] + wave * 64 * D * 2;
   wait_all_loads();
-  store_t_rows<D>(st, static_cast<__bf16 *>(p.dk) + kv_off, dk, p.scale, lane, half);
-  store_t_rows<D>(st + 32 * D * 2, static_cast<__bf16 *>(p.dv) + kv_off, dv, 1.f, lane, half);
+  store_t_rows<D, PAD>(st, static_cast<__bf16 *>(p.dk) + kv_row * mk, dk, p.scale, lane, half, mk);
+  store_t_rows<D, PAD>(st + 32 * D * 2, static_cast<__bf16 *>(p.dv) + kv_row * mv, dv, 1.f, lane, half, mv);
 }
 
 // ---- query-major kernel: dQ -----------------------------------------------
@@ -647,7 +712,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv(const BwdParams p) {
 // one workgroup per CU, and each wave's MFMAs stand still during its own
 // VALU work; that shape stays for grids of at most one workgroup per CU,
 // where half tiles only add barriers.  D = 64 takes whole tiles (64 KiB).
-template <int D, bool CAP, bool DENSE, bool HALF>
+// PAD: padded head dims, as in bwd_dkdv.
+template <int D, bool CAP, bool DENSE, bool HALF, bool PAD>
 __global__ __launch_bounds__(kThreads, HALF ? 2 : 1) void bwd_dq(const BwdParams p) {
   static_assert(!HALF || D == 128, "half tiles at D = 128");
   using T = BTile<D>;
@@ -672,11 +738,21 @@ __global__ __launch_bounds__(kThreads, HALF ? 2 : 1) void bwd_dq(const BwdParams
   const int hm = f.hm == 1 ? 0 : hq;
   const int64_t q_row = static_cast<int64_t>(r) * kBlk + 32 * wave + (lane & 31);   // this lane's query
   const int64_t row_base = (static_cast<int64_t>(b) * f.Hq + hq) * f.Sq;
-  const int64_t q0 = (row_base + static_cast<int64_t>(r) * kBlk + 32 * wave) * D;
+  const int mk = PAD ? f.dk : D, mv = PAD ? f.dv : D;   // row lengths in memory
+  const int64_t q0 = row_base + static_cast<int64_t>(r) * kBlk + 32 * wave;   // the wave's first row
 
   bf16x8 qb[kKS], dob[kKS];
-  load_rows_b<D>(qb, static_cast<const __bf16 *>(f.q) + q0, lane, half);
-  load_rows_b<D>(dob, static_cast<const __bf16 *>(p.dout) + q0, lane, half);
+  load_rows_b<D, PAD>(qb, static_cast<const __bf16 *>(f.q) + q0 * mk, lane, half, mk);
+  load_rows_b<D, PAD>(dob, static_cast<const __bf16 *>(p.dout) + q0 * mv, lane, half, mv);
+  if constexpr (PAD) {
+    // the tiles' padding columns start (and stay) zero; written and
+    // published before any load into the tiles
+    constexpr int kVec = 2 * 2 * kTileBytes / 16;
+#pragma unroll
+    for (int i = 0; i < kVec / kThreads; ++i)
+      reinterpret_cast<u32x4 *>(&kv_t[0][0][0])[tid + kThreads * i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
   const float lse2 = f.lse[row_base + q_row] * kLog2e;
   const float di = p.delta[row_base + q_row];
   int64_t lo = 0, hi = 0;
@@ -688,9 +764,9 @@ __global__ __launch_bounds__(kThreads, HALF ? 2 : 1) void bwd_dq(const BwdParams
 #pragma unroll
     for (int v = 0; v < 16; ++v) dq[dt][v] = 0.f;
 
-  const int64_t kv_head = (static_cast<int64_t>(b) * f.Hkv + hkv) * f.Skv * D;
-  const i32x4 kr = make_rsrc(static_cast<const __bf16 *>(f.k) + kv_head, f.Skv * D * 2);
-  const i32x4 vr = make_rsrc(static_cast<const __bf16 *>(f.v) + kv_head, f.Skv * D * 2);
+  const int64_t kv_head = (static_cast<int64_t>(b) * f.Hkv + hkv) * f.Skv;   // the head's first row
+  const i32x4 kr = make_rsrc(static_cast<const __bf16 *>(f.k) + kv_head * mk, f.Skv * mk * 2);
+  const i32x4 vr = make_rsrc(static_cast<const __bf16 *>(f.v) + kv_head * mv, f.Skv * mv * 2);
   // The row's walk: its non-empty blocks in order, one entry each (key
   // block | label << 28, and the dense mask's partial block), the same
   // lists the forward walks.  They are read-only for the kernel's lifetime,
@@ -708,9 +784,15 @@ __global__ __launch_bounds__(kThreads, HALF ? 2 : 1) void bwd_dq(const BwdParams
   auto ent_lab = [](int ent) -> int { return static_cast<int>(static_cast<uint32_t>(ent) >> 28); };
   // tile `hf` (kTileRows keys) of key block c into buffer buf
   auto issue = [&](int buf, int c, int hf) {
-    const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(c) * T::kBytes + hf * kTileBytes);
-    issue_tile<D, kTileRows>(kv_t[buf][0], kr, goff, wave, lane);
-    issue_tile<D, kTileRows>(kv_t[buf][1], vr, goff, wave, lane);
+    if constexpr (PAD) {
+      const uint32_t row0 = static_cast<uint32_t>(c) * kBlk + static_cast<uint32_t>(hf * kTileRows);
+      issue_tile<D, kTileRows, true>(kv_t[buf][0], kr, 0, wave, lane, row0, static_cast<uint32_t>(mk * 2));
+      issue_tile<D, kTileRows, true>(kv_t[buf][1], vr, 0, wave, lane, row0, static_cast<uint32_t>(mv * 2));
+    } else {
+      const uint32_t goff = static_cast<uint32_t>(static_cast<int64_t>(c) * T::kBytes + hf * kTileBytes);
+      issue_tile<D, kTileRows>(kv_t[buf][0], kr, goff, wave, lane);
+      issue_tile<D, kTileRows>(kv_t[buf][1], vr, goff, wave, lane);
+    }
   };
   auto load_words = [&](int mn, unsigned &m0, unsigned &m1) {
     const unsigned *src = f.pmb_bits + static_cast<int64_t>(mn) * 4 * kBlk;
@@ -841,7 +923,8 @@ __global__ __launch_bounds__(kThreads, HALF ? 2 : 1) void bwd_dq(const BwdParams
   }
   // every wave is past the loop's last barrier
   wait_all_loads();
-  store_t_rows<D>(&kv_t[0][0][0] + wave * 32 * D * 2, static_cast<__bf16 *>(p.dq) + q0, dq, p.scale, lane, half);
+  store_t_rows<D, PAD>(&kv_t[0][0][0] + wave * 32 * D * 2, static_cast<__bf16 *>(p.dq) + q0 * mk, dq, p.scale, lane,
+                       half, mk);
 }
 
 // Compute units of the current device (looked up once per device; 256 if
@@ -858,22 +941,29 @@ int compute_units() {
   return v;
 }
 
-template <int D, bool CAP, bool DENSE>
+template <int D, bool CAP, bool DENSE, bool PAD>
 hipError_t go(const BwdParams &p, hipStream_t stream) {
   const FwdParams &f = p.f;
   const int64_t nkv = f.B * f.Hkv * p.nk;
   if (nkv > 0)
-    hipLaunchKernelGGL((bwd_dkdv<D, CAP, DENSE>), dim3(static_cast<unsigned>(nkv)), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv<D, CAP, DENSE, PAD>), dim3(static_cast<unsigned>(nkv)), dim3(kThreads), 0, stream,
+                       p);
   const int64_t nq = f.B * f.Hq * f.nq;
   if (nq > 0) {
     if (D == 128 && nq > compute_units())
-      hipLaunchKernelGGL((bwd_dq<D, CAP, DENSE, D == 128>), dim3(static_cast<unsigned>(nq)), dim3(kThreads), 0,
+      hipLaunchKernelGGL((bwd_dq<D, CAP, DENSE, D == 128, PAD>), dim3(static_cast<unsigned>(nq)), dim3(kThreads), 0,
                          stream, p);
     else
-      hipLaunchKernelGGL((bwd_dq<D, CAP, DENSE, false>), dim3(static_cast<unsigned>(nq)), dim3(kThreads), 0, stream,
-                         p);
+      hipLaunchKernelGGL((bwd_dq<D, CAP, DENSE, false, PAD>), dim3(static_cast<unsigned>(nq)), dim3(kThreads), 0,
+                         stream, p);
   }
   return hipGetLastError();
+}
+
+template <int D, bool PAD>
+hipError_t go_p(const BwdParams &p, hipStream_t stream) {
+  if (p.f.cap) return p.f.dense ? go<D, true, true, PAD>(p, stream) : go<D, true, false, PAD>(p, stream);
+  return p.f.dense ? go<D, false, true, PAD>(p, stream) : go<D, false, false, PAD>(p, stream);
 }
 
 template <int D>
@@ -883,10 +973,10 @@ hipError_t go_d(const BwdParams &p, hipStream_t stream) {
   if (rows > 0) {
     const int64_t threads = rows * (D / 8);
     hipLaunchKernelGGL((bwd_delta<D>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, stream,
-                       static_cast<const __bf16 *>(f.out), static_cast<const __bf16 *>(p.dout), p.delta, rows);
+                       static_cast<const __bf16 *>(f.out), static_cast<const __bf16 *>(p.dout), p.delta, rows,
+                       f.padded ? f.dv : D);
   }
-  if (f.cap) return f.dense ? go<D, true, true>(p, stream) : go<D, true, false>(p, stream);
-  return f.dense ? go<D, false, true>(p, stream) : go<D, false, false>(p, stream);
+  return f.padded ? go_p<D, true>(p, stream) : go_p<D, false>(p, stream);
 }
 
 }  // namespace

@@ -400,7 +400,8 @@ def splash_bwd(q, k, v, out, lse, dout, mask_info, softmax_scale=None, logits_so
                dq=None, dk=None, dv=None, delta=None, stream=None):
     """Gradients (dq, dk, dv) of splash_fwd's output for the output gradient
     dout (bf16 GPU tensors, contiguous BHSD; lse is splash_fwd's).  delta is
-    an optional float32 [B, Hq, Sq] workspace."""
+    an optional float32 [B, Hq, Sq] workspace.  Head dims as splash_fwd's
+    bf16 forward."""
     import torch
     lib = load_library()
     if q.dtype != torch.bfloat16:

@@ -367,9 +367,11 @@ SPLASH_API splash_status splash_lse_merge(const void *out_a, const float *lse_a,
  * dq, dk, dv: DEVICE outputs shaped like q, k, v, fully overwritten (key
  * blocks no query sees get zeros).  delta: DEVICE float32 workspace of
  * B * Hq * Sq elements, overwritten.  All caller-owned, 16-byte aligned
- * (lse and delta 4-byte), valid until the kernels end.  bf16 with D == Dv
- * in {64, 128} only (float32 or other head dims return
- * SPLASH_EUNSUPPORTED); other requirements as splash_fwd.  The first
+ * (lse and delta 4-byte), valid until the kernels end.  bf16 only (float32
+ * returns SPLASH_EUNSUPPORTED); head dims as splash_fwd's bf16 forward (D
+ * and Dv other than D == Dv in {64, 128} run zero-padded, dq and dk rows
+ * packed at D elements and dv rows at Dv); other requirements as
+ * splash_fwd.  The first
  * backward call on a device also uploads the transposed block lists of the
  * MaskInfo; later calls allocate nothing.  Asynchronous on hip_stream. */
 SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void *q, const void *k, const void *v,

@@ -211,6 +211,21 @@ def test_fwd_and_bwd_reject_heads_beyond_32bit_buffers(dtype, skv):
     assert lib.splash_fwd(*_fwd_args(mi_ok, Hq=1, Hkv=1, dtype=dtype, B=0)) == splash.OK
 
 
+@pytest.mark.parametrize("D,Dv,dtype,status", [
+    (96, 96, splash.BF16, splash.OK),              # padded head dims pass validation (B = 0: no-op)
+    (128, 64, splash.BF16, splash.OK),
+    (96, 96, splash.F32, splash.EUNSUPPORTED),     # float32 runs D == Dv in {64, 128}
+    (72, 72, splash.BF16, splash.EUNSUPPORTED),    # not a multiple of 16
+    (160, 160, splash.BF16, splash.EUNSUPPORTED),  # above the 128-column kernels
+])
+def test_bwd_head_dims_validation(D, Dv, dtype, status):
+    lib = splash.load_library()
+    mi = splash.make_mask_info("causal", 256, 256)
+    st = lib.splash_bwd(mi.handle, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 2, 2, 256, 256, D, Dv, dtype, math.nan, 0.0,
+                        None)
+    assert st == status, lib.splash_last_error()
+
+
 def test_binding_checks_caller_buffers():
     """Outputs the caller passes must have the shape and dtype the kernel
     writes; the check runs before any GPU work (CPU tensors are refused too)."""

@@ -8,14 +8,17 @@ attention is pinned with Dv != D and the default scale of the true D) at the
 bf16 tolerance, 2e-2 max-abs on out and lse.  The cases cover both padded
 kernels, with and without the soft cap, computable and dense masks, GQA /
 MQA, Sq != Skv, attention sinks, and the default softmax scale (D ** -0.5 of
-the caller's D, not of the padded one).
+the caller's D, not of the padded one).  The backward runs the same
+padding; its gradients are compared with the oracle's attention_bwd (pinned
+with Dv != D against torch autograd and central differences).
 """
 import numpy as np
 import pytest
 import torch
 
-from block_sparse_attention_make_amd import make_mask_info, splash_fwd, synthetic
-from tests.gpu_cases import TOL, compare, oracle_full, run_gpu
+from block_sparse_attention_make_amd import make_mask_info, splash_bwd, splash_fwd, synthetic
+from oracle import attention as oatt
+from tests.gpu_cases import TOL, compare, mask_rows_fn, oracle_full, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +113,93 @@ def test_padded_head_dims_refuse_splits():
     mi = make_mask_info("causal", 256, 256)
     with pytest.raises(RuntimeError, match="key splits"):
         splash_fwd(q.to(DEV), k.to(DEV), v.to(DEV), mi, kv_splits=2)
+
+
+# ---- backward at padded head dims --------------------------------------------
+# Tolerance as in the backward's own parity tests: max-abs error of each
+# gradient at most 1e-2 of the larger of 1 and the oracle's max-abs (bf16
+# gradients and bf16 p and ds in the products sit near 0.4 % of the scale).
+GRAD_TOL = 1e-2
+
+
+def _grad_check(name, got, ref):
+    got = got.float().cpu().numpy()
+    assert np.isfinite(got).all(), f"{name}: non-finite"
+    scale = max(1.0, float(np.abs(ref).max()))
+    err = float(np.abs(got - ref).max())
+    print(f"{name}: max|d|={err:.3e} ref max={scale:.3e}", flush=True)
+    assert err <= GRAD_TOL * scale, (name, err, scale)
+
+
+def _run_bwd(seed, B, Hq, Hkv, Sq, Skv, D, Dv, kind, cap=None, dense=None, **mk):
+    q, k, v = synthetic.make_qkv(seed, B, Hq, Hkv, Sq, Skv, D, Dv)
+    g = torch.Generator().manual_seed(seed + 1000)
+    do = torch.randn((B, Hq, Sq, Dv), generator=g).to(torch.bfloat16)
+    mi = make_mask_info(kind, Sq, Skv, dense=dense, **mk)
+    qd, kd, vd, dod = q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV)
+    out, lse = splash_fwd(qd, kd, vd, mi, logits_soft_cap=cap)
+    nan = float("nan")
+    dq, dk, dv = torch.full_like(qd, nan), torch.full_like(kd, nan), torch.full_like(vd, nan)
+    splash_bwd(qd, kd, vd, out, lse, dod, mi, logits_soft_cap=cap, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    fn = mask_rows_fn(kind, Skv, dense=dense, **mk)
+    ref = oatt.attention_bwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), do.double().numpy(), fn,
+                             soft_cap=cap)
+    return (dq, dk, dv), ref
+
+
+BWD_CASES = [
+    # name, seed, B, Hq, Hkv, Sq, Skv, D, Dv, mask kwargs, cap
+    ("d96_causal_gqa", 260, 1, 4, 2, 640, 640, 96, 96, dict(kind="causal"), None),
+    ("d32_local_cap", 261, 1, 2, 1, 512, 512, 32, 32, dict(kind="local", left=200, right=50), 3.0),
+    ("d128_dv64_chunked", 262, 1, 2, 2, 768, 768, 128, 64, dict(kind="chunked", chunk=300), None),
+    ("d48_dv112_rect", 263, 1, 2, 2, 256, 640, 48, 112, dict(kind="causal"), None),
+    ("d64_dv16_rect", 264, 1, 2, 1, 640, 256, 64, 16, dict(kind="causal"), 4.0),
+    # more dQ workgroups (2 x 32 x 5 = 320) than compute units: the
+    # 128-column dQ kernel streams 64-key half tiles
+    ("d80_half_tiles_cap", 265, 2, 32, 8, 640, 640, 80, 80, dict(kind="causal"), 5.0),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_padded_head_dims_bwd(case):
+    name, seed, B, Hq, Hkv, Sq, Skv, D, Dv, mk, cap = case
+    got, ref = _run_bwd(seed, B, Hq, Hkv, Sq, Skv, D, Dv, cap=cap, **mk)
+    for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+        _grad_check(f"{name}.{nm}", g_, r_)
+
+
+@pytest.mark.parametrize("D,Dv", [(48, 32), (112, 96)])
+def test_padded_head_dims_bwd_dense(D, Dv):
+    """Dense masks in both padded backward kernels: a full block, an empty
+    block, a row with no allowed key (zero dq) and keys no query sees (zero
+    dk, dv)."""
+    rng = np.random.default_rng(270 + D)
+    dense = synthetic.random_dense_mask(rng, 1, 512, 640, 0.2, force_diagonal=True)
+    dense[:, 0:128, 128:256] = True
+    dense[:, 128:256, 0:128] = False
+    dense[:, 7, :] = False
+    dense[:, :, 600:] = False
+    got, ref = _run_bwd(271 + D, 1, 2, 1, 512, 640, D, Dv, "dense", dense=dense)
+    for nm, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+        _grad_check(f"dense D={D} Dv={Dv}.{nm}", g_, r_)
+    assert (got[0][:, :, 7] == 0).all()
+    assert (got[1][:, :, 600:] == 0).all() and (got[2][:, :, 600:] == 0).all()
+
+
+def test_padded_head_dims_autograd():
+    """splash_attention (the autograd wrapper) at D = 96, Dv = 64 against the
+    oracle's gradients."""
+    from block_sparse_attention_make_amd import splash_attention
+    q, k, v = synthetic.make_qkv(280, 1, 2, 2, 384, 384, 96, 64)
+    mi = make_mask_info("causal", 384, 384)
+    g = torch.Generator().manual_seed(281)
+    do = torch.randn((1, 2, 384, 64), generator=g).to(torch.bfloat16)
+    qd, kd, vd = (t.to(DEV).requires_grad_() for t in (q, k, v))
+    o = splash_attention(qd, kd, vd, mi)
+    o.backward(do.to(DEV))
+    torch.cuda.synchronize()
+    fn = mask_rows_fn("causal", 384)
+    ref = oatt.attention_bwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), do.double().numpy(), fn)
+    for nm, g_, r_ in zip(("dq", "dk", "dv"), (qd.grad, kd.grad, vd.grad), ref):
+        _grad_check(f"autograd.{nm}", g_, r_)
