@@ -484,12 +484,8 @@ def main():
 
     from block_sparse_attention_make_amd.splash import plan_kv_splits
     from block_sparse_attention_make_amd.splash import plan_heads_per_workgroup
-    native_dims = w.D == w.Dv and w.D in (64, 128)   # other head dims run zero-padded, unsplit
-    if not native_dims and args.backward:
-        print(f"--backward runs head dims D == Dv in {{64, 128}}; {w.name} has D={w.D}, Dv={w.Dv}", file=sys.stderr)
-        sys.exit(2)
-    splits = ((plan_kv_splits(mi, w.B, w.Hq, 0 if w.dtype == "bf16" else 1) if native_dims else 1)
-              if args.kv_splits == "auto" else int(args.kv_splits))
+    splits = (plan_kv_splits(mi, w.B, w.Hq, 0 if w.dtype == "bf16" else 1) if args.kv_splits == "auto"
+              else int(args.kv_splits))
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty((w.B, w.Hq, w.Sq, w.Dv), dtype=q.dtype, device=dev)
     split_ws = None
@@ -627,7 +623,7 @@ def main():
                    "seq_len": w.Sq, "head_dim": w.D, "vhead_dim": w.Dv, "mask": m.kind, "block": w.block,
                    "soft_cap": w.soft_cap, "parallelism": "single-gpu",
                    "sinks_per_kv_head": args.sinks, "kv_shards": P, "kv_splits": splits,
-                   "heads_per_workgroup": None if args.backward or P > 1 else 1 if not native_dims else (
+                   "heads_per_workgroup": None if args.backward or P > 1 else (
                        args.heads_per_wg or plan_heads_per_workgroup(
                            mi, w.B, w.Hq, w.Hkv, w.D, 0 if w.dtype == "bf16" else 1, splits)),
                    "mask_block": [args.block_q, args.block_kv], "pass": "backward" if args.backward else "forward"},

@@ -590,16 +590,18 @@ int64_t split_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t Dv, int
 // stages): the bf16 kernel at D = 128 with a computable mask and one mask
 // head (so both heads walk the same blocks) and an even group size (so the
 // pair shares its K/V head).
-bool head_pairs_possible(const splash_mask_info *mi, int64_t Hq, int64_t Hkv, int64_t D, int32_t dtype) {
-  return dtype == SPLASH_BF16 && D == 128 && mi->kind != SPLASH_MASK_DENSE && mi->num_heads == 1 && Hkv > 0 &&
-         (Hq / Hkv) % 2 == 0;
+bool head_pairs_possible(const splash_mask_info *mi, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
+                         int32_t dtype) {
+  const int64_t kernel_dim = native_dims(D, Dv) ? D : padded_kernel_dim(D, Dv);
+  return dtype == SPLASH_BF16 && kernel_dim == 128 && mi->kind != SPLASH_MASK_DENSE && mi->num_heads == 1 &&
+         Hkv > 0 && (Hq / Hkv) % 2 == 0;
 }
 
 // The library's choice of heads per workgroup: pairs where possible, as long
 // as the pairs still give each CU a workgroup (a pair fills a CU alone).
-int32_t auto_heads_per_wg(const splash_mask_info *mi, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int32_t dtype,
-                          int32_t kv_splits) {
-  if (!head_pairs_possible(mi, Hq, Hkv, D, dtype)) return 1;
+int32_t auto_heads_per_wg(const splash_mask_info *mi, int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
+                          int32_t dtype, int32_t kv_splits) {
+  if (!head_pairs_possible(mi, Hq, Hkv, D, Dv, dtype)) return 1;
   return B * (Hq / 2) * walk_of(mi).nq * kv_splits >= 256 ? 2 : 1;
 }
 
@@ -614,13 +616,9 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
   if (st != SPLASH_OK) return st;
   const bool padded = !native_dims(D, Dv);
   if (heads_per_wg < 0 || heads_per_wg > 2) return fail(SPLASH_EINVAL, "heads_per_workgroup must be 0, 1 or 2");
-  if (padded && heads_per_wg == 2)
-    return fail(SPLASH_EUNSUPPORTED, "head dims other than D == Dv in {64, 128} run one head per workgroup");
-  if (padded && kv_splits > 1)
-    return fail(SPLASH_EUNSUPPORTED, "head dims other than D == Dv in {64, 128} run without key splits");
-  if (heads_per_wg == 2 && !head_pairs_possible(mi, Hq, Hkv, D, dtype))
-    return fail(SPLASH_EUNSUPPORTED, "two heads per workgroup need bf16, D = 128, a computable mask with one "
-                                     "mask head and an even GQA group");
+  if (heads_per_wg == 2 && !head_pairs_possible(mi, Hq, Hkv, D, Dv, dtype))
+    return fail(SPLASH_EUNSUPPORTED, "two heads per workgroup need bf16, the 128-column kernel, a computable mask "
+                                     "with one mask head and an even GQA group");
   if (kv_splits < 1 || kv_splits > DeviceCopy::kMaxSplits)
     return fail(SPLASH_EINVAL, "kv_splits must be in 1..8");
   if (kv_splits > 1 && dtype != SPLASH_BF16)
@@ -660,7 +658,8 @@ splash_status fwd_impl(splash_mask_info *mi, const void *q, const void *k, const
   p.num_sinks = num_sinks;
   p.kv_splits = kv_splits;
   p.items = dc->items[kv_splits];
-  const int32_t hpw = padded ? 1 : heads_per_wg != 0 ? heads_per_wg : auto_heads_per_wg(mi, B, Hq, Hkv, D, dtype, kv_splits);
+  const int32_t hpw =
+      heads_per_wg != 0 ? heads_per_wg : auto_heads_per_wg(mi, B, Hq, Hkv, D, Dv, dtype, kv_splits);
   p.head_pairs = hpw == 2 ? 1 : 0;
   if (padded) {
     p.D = static_cast<int32_t>(padded_kernel_dim(D, Dv));
@@ -775,7 +774,7 @@ extern "C" SPLASH_API splash_status splash_fwd_heads_per_workgroup(const splash_
   if (B < 0 || Hq < 0 || Hkv <= 0) return fail(SPLASH_EINVAL, "bad head counts");
   if (dtype != SPLASH_BF16 && dtype != SPLASH_F32) return fail(SPLASH_EINVAL, "unknown dtype");
   if (kv_splits < 1 || kv_splits > DeviceCopy::kMaxSplits) return fail(SPLASH_EINVAL, "kv_splits must be in 1..8");
-  *heads = auto_heads_per_wg(mi, B, Hq, Hkv, D, dtype, kv_splits);
+  *heads = auto_heads_per_wg(mi, B, Hq, Hkv, D, D, dtype, kv_splits);
   return SPLASH_OK;
 }
 

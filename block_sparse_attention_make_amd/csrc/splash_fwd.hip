@@ -787,7 +787,6 @@ template <int D, bool CAP, bool DENSE, int RU = 1, bool PAD = false>
 __global__ __launch_bounds__(64 * kWWaves * RU, 1)
 void splash_fwd_wide(const FwdParams p) {
   static_assert(RU == 1 || (RU == 2 && D == 128 && !DENSE), "head pairs: D = 128, computable masks");
-  static_assert(!PAD || RU == 1, "padded head dims: one head per workgroup");
   constexpr int kW = kWWaves * RU;          // waves
   constexpr int kThr = 64 * kW;
   using SG = Stage<D, kW>;
@@ -1565,7 +1564,8 @@ void merge_splits(const FwdParams p) {
   const int64_t rows = p.B * p.Hq * p.Sq;
   const int64_t row = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / kTPR;
   const int c0 = (threadIdx.x % kTPR) * 8;
-  if (row >= rows) return;
+  const int dv = p.padded ? p.dv : D;         // row length of the partials and the output
+  if (row >= rows || c0 >= dv) return;
   const int64_t plane = rows;                 // rows per split
   float ls[S];
   union { u32x4 u; __bf16 h[8]; } x[S];
@@ -1573,7 +1573,7 @@ void merge_splits(const FwdParams p) {
   for (int s = 0; s < S; ++s) {
     ls[s] = __builtin_nontemporal_load(&p.part_lse[s * plane + row]);
     x[s].u = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4 *>(static_cast<const __bf16 *>(p.part_o) + (s * plane + row) * D + c0));
+        reinterpret_cast<const u32x4 *>(static_cast<const __bf16 *>(p.part_o) + (s * plane + row) * dv + c0));
   }
   float m = -INFINITY;
 #pragma unroll
@@ -1606,7 +1606,7 @@ void merge_splits(const FwdParams p) {
   union { __bf16 h[8]; u32x4 u; } pk;
 #pragma unroll
   for (int e = 0; e < 8; ++e) pk.h[e] = static_cast<__bf16>(acc[e] * scale);
-  __builtin_nontemporal_store(pk.u, reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(p.out) + row * D + c0));
+  __builtin_nontemporal_store(pk.u, reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(p.out) + row * dv + c0));
   if (p.lse && c0 == 0) __builtin_nontemporal_store(lse2_tot * kLn2, &p.lse[row]);
 }
 
@@ -1617,25 +1617,19 @@ void launch_merge(const FwdParams &p, hipStream_t stream) {
                      p);
 }
 
-template <int D, bool CAP, bool DENSE>
-hipError_t launch_wide(const FwdParams &p, hipStream_t stream) {
+template <int D, bool CAP, bool DENSE, bool PAD>
+hipError_t launch_wide_pad(const FwdParams &p, hipStream_t stream) {
   if constexpr (D == 128 && !DENSE) {
     if (p.head_pairs) {
       const int64_t blocks = p.B * (p.Hq / 2) * p.nq * p.kv_splits;
-      hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE, 2>), dim3(static_cast<unsigned>(blocks)),
+      hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE, 2, PAD>), dim3(static_cast<unsigned>(blocks)),
                          dim3(2 * kWThreads), 0, stream, p);
     }
   }
-  if (p.padded) {   // one split, one head per workgroup (checked by the caller)
-    const int64_t blocks = p.B * p.Hq * p.nq;
-    hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE, 1, true>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kWThreads), 0, stream, p);
-    return hipGetLastError();
-  }
   if (!p.head_pairs || D != 128 || DENSE) {
     const int64_t blocks = p.B * p.Hq * p.nq * p.kv_splits;
-    hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE>), dim3(static_cast<unsigned>(blocks)), dim3(kWThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((splash_fwd_wide<D, CAP, DENSE, 1, PAD>), dim3(static_cast<unsigned>(blocks)), dim3(kWThreads),
+                       0, stream, p);
   }
   switch (p.kv_splits) {   // 1..8, checked by the caller
     case 1: break;
@@ -1648,6 +1642,11 @@ hipError_t launch_wide(const FwdParams &p, hipStream_t stream) {
     default: launch_merge<D, 8>(p, stream); break;
   }
   return hipGetLastError();
+}
+
+template <int D, bool CAP, bool DENSE>
+hipError_t launch_wide(const FwdParams &p, hipStream_t stream) {
+  return p.padded ? launch_wide_pad<D, CAP, DENSE, true>(p, stream) : launch_wide_pad<D, CAP, DENSE, false>(p, stream);
 }
 
 template <int D, bool CAP, bool DENSE>

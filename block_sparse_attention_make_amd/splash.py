@@ -269,8 +269,7 @@ def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
     softmax_aux: optional attention-sink logits, a float32 GPU tensor [ns]
     (shared), [Hkv, ns] (query head h uses row h // (Hq // Hkv)) or [Hq, ns].
     Head dims: D == Dv in {64, 128}, or (bf16) any D and Dv that are multiples
-    of 16 up to 128, which run zero-padded inside the 64- or 128-column kernel
-    with one head per workgroup and no key splits.
+    of 16 up to 128, which run zero-padded inside the 64- or 128-column kernel.
     kv_splits: "auto" (the library's plan: splits only when the grid has
     fewer block rows than the GPU has workgroup slots) or 1..8 -- each block
     row's non-empty blocks divided into that many workgroups, merged by lse;
@@ -313,10 +312,7 @@ def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
         rows, ns = (1, aux.shape[0]) if aux.dim() == 1 else (aux.shape[0], aux.shape[1])
         aux_p = aux.data_ptr() if ns else None
     with torch.cuda.device(q.device):
-        # head dims other than D == Dv in {64, 128} run zero-padded, without key splits
-        native = D == Dv and D in (64, 128)
-        splits = ((plan_kv_splits(mask_info, B, Hq, dt) if native else 1) if kv_splits == "auto"
-                  else int(kv_splits))
+        splits = plan_kv_splits(mask_info, B, Hq, dt) if kv_splits == "auto" else int(kv_splits)
         ws_p, ws_bytes = None, 0
         if splits > 1:
             nbytes = ctypes.c_size_t()

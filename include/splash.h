@@ -185,8 +185,8 @@ SPLASH_API void splash_mask_info_destroy(splash_mask_info *mi);
  * 128 (the EasyDeL BlockSparseAttn page types head_dim and vhead_dim apart
  * and, on GPU, sends only multiples of 16 to its block-sparse kernel, other
  * dims to plain attention).  Those run zero-padded inside the
- * 64-column kernel (both <= 64) or the 128-column one, one head per
- * workgroup and without key splits; rows stay packed at D and Dv elements.
+ * 64-column kernel (both <= 64) or the 128-column one; rows stay packed at
+ * D and Dv elements.
  * The default softmax_scale is D ** -0.5 of the true D.
  * B, Hq or Sq equal to 0 is a no-op.  Validation failures return
  * SPLASH_EINVAL (or SPLASH_EUNSUPPORTED for a head dim / block size the
@@ -237,8 +237,8 @@ SPLASH_API splash_status splash_fwd_sinks(splash_mask_info *mi, const void *q, c
  * machine.
  *
  * kv_splits: 1..8 (1 is exactly splash_fwd_sinks; workspace may then be
- * NULL).  kv_splits > 1 runs bf16 with D == Dv in {64, 128} only (float32
- * or other head dims return SPLASH_EUNSUPPORTED).  workspace: DEVICE scratch of at least
+ * NULL).  kv_splits > 1 runs bf16 only (float32 returns
+ * SPLASH_EUNSUPPORTED).  workspace: DEVICE scratch of at least
  * splash_fwd_workspace_size bytes, 16-byte aligned, overwritten, owned by
  * the caller and valid until the kernels end.  The first call with a given
  * kv_splits on a device uploads that split's table of the MaskInfo (device
@@ -280,9 +280,9 @@ SPLASH_API splash_status splash_fwd_plan(const splash_mask_info *mi, int64_t B, 
  *   2  four waves, the same block row of two heads of one GQA group, which
  *      share their key/value head and their walk, so each K/V stage loaded
  *      into LDS serves 256 query rows; one workgroup per compute unit.
- *      Needs bf16, D == Dv == 128, a computable mask (causal, local,
- *      chunked) with one mask head, and Hq / Hkv even; else
- *      SPLASH_EUNSUPPORTED.
+ *      Needs bf16, the 128-column kernel (D == Dv == 128, or padded dims
+ *      with max(D, Dv) > 64), a computable mask (causal, local, chunked)
+ *      with one mask head, and Hq / Hkv even; else SPLASH_EUNSUPPORTED.
  *   0  the library's choice (splash_fwd_heads_per_workgroup).
  * The result is the same either way, bit for bit (each row's arithmetic is
  * unchanged).  Other arguments, requirements and errors as
@@ -297,8 +297,8 @@ SPLASH_API splash_status splash_fwd_tiled(splash_mask_info *mi, const void *q, c
                                           void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* The heads per workgroup splash_fwd_tiled uses for heads_per_workgroup = 0
- * when Dv == D (other Dv always run 1):
- * 2 where two heads can share a workgroup (see splash_fwd_tiled) and the
+ * with Dv == D: 2 where two heads can share a workgroup (see
+ * splash_fwd_tiled) and the
  * grid of B * Hq / 2 * (block rows) * kv_splits workgroups still gives 256
  * compute units one each, else 1.  Host work only.  Errors: SPLASH_EINVAL
  * (NULL arguments, negative sizes, Hkv <= 0, unknown dtype, kv_splits

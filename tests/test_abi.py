@@ -268,8 +268,7 @@ def test_static_decode_rejects_more_than_its_scratch_before_running():
     (dict(splits=2, ws_bytes=1024), splash.EINVAL),           # too small
     (dict(splits=2, ws=24), splash.EINVAL),                   # misaligned
     (dict(splits=2, Sq=256), splash.EINVAL),                  # MaskInfo mismatch, as splash_fwd
-    (dict(splits=2, D=96, Dv=96), splash.EUNSUPPORTED),       # padded head dims run unsplit
-    (dict(splits=2, D=128, Dv=64), splash.EUNSUPPORTED),
+    (dict(splits=2, D=96, Dv=96, dtype=splash.F32), splash.EUNSUPPORTED),
 ])
 def test_fwd_split_validation_errors_before_launch(over, status):
     lib = splash.load_library()
@@ -304,8 +303,8 @@ def test_fwd_workspace_size_and_plan_on_host():
     ("causal", dict(heads=2, Hq=6, Hkv=2), splash.EUNSUPPORTED),     # odd group
     ("causal", dict(heads=2, D=64, Dv=64), splash.EUNSUPPORTED),     # D = 64
     ("causal", dict(heads=2, dtype=splash.F32), splash.EUNSUPPORTED),
-    ("causal", dict(heads=2, Dv=96), splash.EUNSUPPORTED),           # padded Dv: one head per workgroup
-    ("causal", dict(heads=2, D=96, Dv=96), splash.EUNSUPPORTED),
+    ("causal", dict(heads=2, D=64, Dv=48), splash.EUNSUPPORTED),     # padded dims in the 64-column kernel
+    ("causal", dict(heads=2, D=32, Dv=32), splash.EUNSUPPORTED),
     ("dense", dict(heads=2), splash.EUNSUPPORTED),                   # dense mask
 ])
 def test_fwd_tiled_validation_errors_before_launch(mask, over, status):

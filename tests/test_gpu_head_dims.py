@@ -51,8 +51,7 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_padded_head_dims_parity(case):
-    """kv_splits="auto": these small grids would split with native dims; the
-    binding runs padded dims unsplit."""
+    """kv_splits="auto": the library's split plan (these small grids split)."""
     name, seed, B, Hq, Hkv, Sq, Skv, D, Dv, mk, cap = case
     q, k, v = synthetic.make_qkv(seed, B, Hq, Hkv, Sq, Skv, D, Dv)
     o, l, _ = run_gpu(q, k, v, cap=cap, **mk)
@@ -108,11 +107,56 @@ def test_padded_head_dims_explicit_scale_and_neighbours_untouched():
     compare(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref, TOL[torch.bfloat16], "scale 0.05")
 
 
-def test_padded_head_dims_refuse_splits():
-    q, k, v = synthetic.make_qkv(250, 1, 2, 2, 256, 256, 96, 96)
-    mi = make_mask_info("causal", 256, 256)
-    with pytest.raises(RuntimeError, match="key splits"):
-        splash_fwd(q.to(DEV), k.to(DEV), v.to(DEV), mi, kv_splits=2)
+SHAPE_CASES = [
+    # name, seed, B, Hq, Hkv, Sq, Skv, D, Dv, mask kwargs, cap, splits
+    ("d96_causal_g2_splits4", 250, 1, 4, 2, 640, 640, 96, 96, dict(kind="causal"), None, 4),
+    ("d64_dv112_local_g4", 251, 1, 8, 2, 1024, 1024, 64, 112, dict(kind="local", left=300, right=40), None, 1),
+    ("d80_chunked_cap_g2_splits3", 252, 1, 4, 2, 1536, 1536, 80, 80, dict(kind="chunked", chunk=640), 30.0, 3),
+    ("d128_dv96_rect_g2_splits2", 253, 1, 4, 2, 512, 1664, 128, 96, dict(kind="causal"), None, 2),
+]
+
+
+def _run_shape(q, k, v, mk, cap, splits, heads, aux=None):
+    Sq, Skv = q.shape[2], k.shape[2]
+    mi = make_mask_info(mk["kind"], Sq, Skv, left=mk.get("left"), right=mk.get("right"), chunk=mk.get("chunk"))
+    out = torch.full(q.shape[:3] + (v.shape[3],), float("nan"), dtype=q.dtype, device=DEV)
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    auxd = None if aux is None else torch.as_tensor(aux).to(DEV)
+    splash_fwd(q.to(DEV), k.to(DEV), v.to(DEV), mi, logits_soft_cap=cap, out=out, lse=lse, kv_splits=splits,
+               heads_per_workgroup=heads, softmax_aux=auxd)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("case", SHAPE_CASES, ids=[c[0] for c in SHAPE_CASES])
+def test_padded_head_dims_launch_shapes(case):
+    """Key splits and two heads per workgroup at padded dims (128-column
+    kernel): against the oracle, and one head per workgroup against two bit
+    for bit (each row's arithmetic is the same in both shapes)."""
+    name, seed, B, Hq, Hkv, Sq, Skv, D, Dv, mk, cap, splits = case
+    q, k, v = synthetic.make_qkv(seed, B, Hq, Hkv, Sq, Skv, D, Dv)
+    o2, l2 = _run_shape(q, k, v, mk, cap, splits, heads=2)
+    o_ref, l_ref = oracle_full(q, k, v, cap=cap, **mk)
+    compare(o2.float().numpy(), l2.numpy(), o_ref, l_ref, TOL[torch.bfloat16], f"{name} two heads per workgroup")
+    o1, l1 = _run_shape(q, k, v, mk, cap, splits, heads=1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), f"{name}: one and two heads per workgroup differ"
+
+
+@pytest.mark.parametrize("D,Dv", [(32, 48), (112, 80)])
+def test_padded_head_dims_splits_dense_sinks(D, Dv):
+    """Key splits (1, 2, 5) at padded dims with a dense mask, an empty block
+    row and sinks (the merge adds them once); every split count against the
+    oracle."""
+    q, k, v = synthetic.make_qkv(255 + D, 1, 4, 2, 512, 768, D, Dv)
+    rng = np.random.default_rng(256 + D)
+    dense = synthetic.random_dense_mask(rng, 1, 512, 768, 0.3, force_diagonal=True)
+    dense[0, 128:256, :] = False
+    aux = np.array([[0.25, -0.5], [1.0, -np.inf]], dtype=np.float32)
+    o_ref, l_ref = oracle_full(q, k, v, "dense", dense=dense, aux=aux)
+    for splits in (1, 2, 5):
+        o, l, _ = run_gpu(q, k, v, "dense", dense=dense, aux=aux, kv_splits=splits)
+        compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], f"dense sinks D={D} Dv={Dv} splits={splits}")
+        assert (o[:, :, 128:256] == 0).all()
 
 
 # ---- backward at padded head dims --------------------------------------------
