@@ -857,9 +857,13 @@ extern "C" SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void 
 }
 
 namespace {
+// The decode kernel's head dim: D itself (64 or 128), or the 64- or
+// 128-column kernel that runs D zero-padded.
+int64_t decode_kernel_dim(int64_t D) { return D == 64 || D == 128 ? D : padded_kernel_dim(D, D); }
+
 int64_t decode_ws_floats(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv, int64_t D) {
   const int64_t group = Hkv > 0 ? Hq / Hkv : 0;
-  return B * Hkv * decode_chunks(B * Hkv, group, D, Skv) * group * (D + 2);
+  return B * Hkv * decode_chunks(B * Hkv, group, D, Skv) * group * (decode_kernel_dim(D) + 2);
 }
 }  // namespace
 
@@ -887,7 +891,8 @@ splash_status decode_validate(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv, i
   if (dtype != SPLASH_BF16) return fail(SPLASH_EUNSUPPORTED, "decode runs bf16 only");
   if (Hkv == 0 && Hq > 0) return fail(SPLASH_EINVAL, "Hkv must be positive");
   if (Hkv > 0 && Hq % Hkv) return fail(SPLASH_EINVAL, "Hq must be a multiple of Hkv");
-  if (D != Dv || (D != 64 && D != 128)) return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
+  if (D != Dv || !padded_dims_ok(D, Dv))
+    return fail(SPLASH_EUNSUPPORTED, "decode head dims must satisfy D == Dv, a multiple of 16 up to 128");
   if (!(std::isnan(softmax_scale) || (std::isfinite(softmax_scale) && softmax_scale > 0.f)))
     return fail(SPLASH_EINVAL, "softmax_scale must be NaN (default) or finite and > 0");
   if (B == 0 || Hq == 0) {
@@ -921,7 +926,10 @@ splash_status decode_launch(const void *q, const void *k, const void *v, void *o
   p.Hq = static_cast<int32_t>(Hq);
   p.Hkv = static_cast<int32_t>(Hkv);
   p.group = static_cast<int32_t>(group);
-  p.D = static_cast<int32_t>(D);
+  const int64_t kd = decode_kernel_dim(D);
+  p.D = static_cast<int32_t>(kd);
+  p.dim = static_cast<int32_t>(D);
+  p.padded = kd != D ? 1 : 0;
   p.Skv = Skv;
   p.n_chunks = static_cast<int32_t>(decode_chunks(B * Hkv, group, D, Skv));
   p.split_keys = decode_split_keys(B * Hkv, group, D, Skv);
@@ -933,7 +941,7 @@ splash_status decode_launch(const void *q, const void *k, const void *v, void *o
   p.cap_out = cap ? static_cast<float>(logits_soft_cap * log2e) : 0.f;
   const int64_t n_slot = B * Hkv * p.n_chunks * group;
   p.ws_o = static_cast<float *>(workspace);
-  p.ws_m = p.ws_o + n_slot * D;
+  p.ws_m = p.ws_o + n_slot * kd;
   p.ws_l = p.ws_m + n_slot;
   hipError_t e = launch_decode(p, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(SPLASH_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));

@@ -120,6 +120,33 @@ __device__ __forceinline__ void stream_stage(char *lds, i32x4 res, int64_t row0,
 #pragma clang diagnostic pop
 }
 
+// stream_stage for padded head dims: the arrays' rows hold `mrow` bytes (a
+// multiple of 32, at most the stage's row), so each 1 KiB segment takes its
+// own M0 and per-lane offsets, and a lane whose chunk lies in the padding
+// gets an offset past the resource's end, which reads zeros (the stages'
+// padding columns are zeroed before their first load and stay zero).
+template <int D>
+__device__ __forceinline__ void stream_stage_padded(char *lds, i32x4 res, int64_t row0, int wave, int lane,
+                                                    uint32_t mrow) {
+  using SG = SStage<D>;
+#pragma unroll
+  for (int i = 0; i < SG::kSegsPerWave; ++i) {
+    const int seg = wave * SG::kSegsPerWave + i;
+    const int row = seg * SG::kRowsPerSeg + lane / SG::kChunks;
+    const int c = (lane % SG::kChunks) ^ SG::swz(row);
+    const uint32_t voff = static_cast<uint32_t>(c * 16) < mrow
+        ? static_cast<uint32_t>(row0 + row) * mrow + static_cast<uint32_t>(c * 16)
+        : 0x80000000u;
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) char *)(lds + seg * 1024)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :: "s"(m0), "v"(voff), "s"(res) : "memory", "m0");
+#pragma clang diagnostic pop
+  }
+}
+
 // Wait until at most n of this wave's vector-memory loads are in flight.
 template <int N>
 __device__ __forceinline__ void stream_wait(int n) {
@@ -144,7 +171,10 @@ __device__ __forceinline__ void stream_wait(int n) {
 //    transposing LDS read ds_read_b64_tr_b16 (lane l gets column l % 16 of
 //    a 4 x 16 block of rows 4 (l / 16) + 0..3).
 // Every register of a lane belongs to one head, so a rescale is lane-local.
-template <int D, int G, bool CAP>
+// PAD: head dims other than D (rows of p.dim elements), zero-padded: Q^T and
+// the stages are zero past p.dim, so the scores sum only real columns and
+// the output's padding columns (zero) are dropped by the merge.
+template <int D, int G, bool CAP, bool PAD>
 __global__ __launch_bounds__(kSThreads, 1) void decode_mfma(const DecodeParams p) {
   using SG = SStage<D>;
   constexpr int kKC = D / 32;                  // QK products per stage and wave
@@ -171,13 +201,30 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_mfma(const DecodeParams p
   const int64_t ke = min(kb + p.split_keys, p.Skv);
   const int nst = static_cast<int>((ke - kb + kSKeys - 1) / kSKeys);   // >= 1
 
+  const int md = PAD ? p.dim : D;                // row length in memory
   const int64_t kv_head = (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv;
-  const i32x4 k_res = stream_rsrc(static_cast<const __bf16 *>(p.k) + kv_head * D, p.Skv * SG::kRowBytes);
-  const i32x4 v_res = stream_rsrc(static_cast<const __bf16 *>(p.v) + kv_head * D, p.Skv * SG::kRowBytes);
+  const i32x4 k_res = stream_rsrc(static_cast<const __bf16 *>(p.k) + kv_head * md, p.Skv * md * 2);
+  const i32x4 v_res = stream_rsrc(static_cast<const __bf16 *>(p.v) + kv_head * md, p.Skv * md * 2);
   auto issue = [&](int st) {
-    stream_stage<D>(k_st[st % kSStages], k_res, kb + static_cast<int64_t>(st) * kSKeys, wave, lane);
-    stream_stage<D>(v_st[st % kSStages], v_res, kb + static_cast<int64_t>(st) * kSKeys, wave, lane);
+    const int64_t row0 = kb + static_cast<int64_t>(st) * kSKeys;
+    if constexpr (PAD) {
+      stream_stage_padded<D>(k_st[st % kSStages], k_res, row0, wave, lane, static_cast<uint32_t>(md * 2));
+      stream_stage_padded<D>(v_st[st % kSStages], v_res, row0, wave, lane, static_cast<uint32_t>(md * 2));
+    } else {
+      stream_stage<D>(k_st[st % kSStages], k_res, row0, wave, lane);
+      stream_stage<D>(v_st[st % kSStages], v_res, row0, wave, lane);
+    }
   };
+  if constexpr (PAD) {
+    // the stages' padding columns start (and stay) zero; written and
+    // published before any load into the stages
+    constexpr int kVec = kStBytes / 16;
+    static_assert(kVec % kSThreads == 0, "whole zeroing rounds");
+#pragma unroll
+    for (int i = 0; i < kVec / kSThreads; ++i)
+      reinterpret_cast<u32x4 *>(smem)[tid + kSThreads * i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
 #pragma unroll
   for (int st = 0; st < kSStages - 1; ++st)
     if (st < nst) issue(st);
@@ -185,10 +232,11 @@ __global__ __launch_bounds__(kSThreads, 1) void decode_mfma(const DecodeParams p
   // Q^T operand: head h, dims 32 kk + 8 grp + 0..7
   bf16x8 qb[kKC];
   {
-    const __bf16 *qr = static_cast<const __bf16 *>(p.q) + (static_cast<int64_t>(b) * p.Hq + hkv * G + (hv ? h : 0)) * D;
+    const __bf16 *qr = static_cast<const __bf16 *>(p.q) + (static_cast<int64_t>(b) * p.Hq + hkv * G + (hv ? h : 0)) * md;
 #pragma unroll
     for (int kk = 0; kk < kKC; ++kk) {
-      u32x4 w = *reinterpret_cast<const u32x4 *>(qr + 32 * kk + 8 * grp);
+      u32x4 w = u32x4{0u, 0u, 0u, 0u};
+      if (!PAD || 32 * kk + 8 * grp < md) w = *reinterpret_cast<const u32x4 *>(qr + 32 * kk + 8 * grp);
       if (!hv) w = u32x4{0u, 0u, 0u, 0u};
       __builtin_memcpy(&qb[kk], &w, sizeof(w));
     }
@@ -344,17 +392,24 @@ __global__ __launch_bounds__(64) void decode_merge(const DecodeParams p) {
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  __bf16 *orow = static_cast<__bf16 *>(p.out) + static_cast<int64_t>(bhq) * D;
+  const int md = p.padded ? p.dim : D;   // output row length (padded dims: the caller's)
+  __bf16 *orow = static_cast<__bf16 *>(p.out) + static_cast<int64_t>(bhq) * md;
 #pragma unroll
-  for (int j = 0; j < kCols; ++j) orow[kCols * lane + j] = static_cast<__bf16>(o[j] * inv);
+  for (int j = 0; j < kCols; ++j)
+    if (kCols * lane + j < md) orow[kCols * lane + j] = static_cast<__bf16>(o[j] * inv);
   if (p.lse && lane == 0) p.lse[bhq] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
 }
 
 template <int D, int G>
 hipError_t go(const DecodeParams &p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(p.B * p.Hkv), static_cast<unsigned>(p.n_chunks));
-  if (p.cap) hipLaunchKernelGGL((decode_mfma<D, G, true>), grid, dim3(kSThreads), 0, s, p);
-  else hipLaunchKernelGGL((decode_mfma<D, G, false>), grid, dim3(kSThreads), 0, s, p);
+  if (p.padded) {
+    if (p.cap) hipLaunchKernelGGL((decode_mfma<D, G, true, true>), grid, dim3(kSThreads), 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma<D, G, false, true>), grid, dim3(kSThreads), 0, s, p);
+  } else {
+    if (p.cap) hipLaunchKernelGGL((decode_mfma<D, G, true, false>), grid, dim3(kSThreads), 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma<D, G, false, false>), grid, dim3(kSThreads), 0, s, p);
+  }
   hipLaunchKernelGGL((decode_merge<D, G>), dim3(static_cast<unsigned>(p.B * p.Hq)), dim3(64), 0, s, p);
   return hipGetLastError();
 }

@@ -87,7 +87,10 @@ struct DecodeParams {
   const void *q, *k, *v;   // q [B, Hq, 1, D], k / v [B, Hkv, Skv, D] (bf16)
   void *out;               // [B, Hq, 1, D] bf16
   float *lse;              // [B, Hq] or null
-  int32_t B, Hq, Hkv, group, D;
+  int32_t B, Hq, Hkv, group, D;   // D: the kernel's head dim (64 or 128)
+  // Padded head dims: q, k, v and out rows hold `dim` elements (a multiple
+  // of 16 up to D), run zero-padded to D columns.  padded = 0: dim == D.
+  int32_t dim, padded;
   int64_t Skv;
   int32_t n_chunks;        // partial workgroups per (b, kv head)
   int64_t split_keys;      // keys per partial workgroup (the last one may hold fewer)

@@ -396,7 +396,9 @@ SPLASH_API splash_status splash_bwd(splash_mask_info *mi, const void *q, const v
  * out: DEVICE bf16 [B, Hq, 1, D]; lse: DEVICE float32 [B, Hq] or NULL;
  * workspace: DEVICE scratch of at least splash_decode_workspace_size bytes,
  * overwritten.  All caller-owned, 16-byte aligned, valid until the kernels
- * end.  bf16 only; D == Dv in {64, 128}; Hq / Hkv in {1, 2, 4, 8, 16}; Skv >= 1
+ * end.  bf16 only; D == Dv, in {64, 128} or (run zero-padded inside the
+ * 64- or 128-column kernel) another multiple of 16 up to 128, with rows
+ * packed at D elements; Hq / Hkv in {1, 2, 4, 8, 16}; Skv >= 1
  * and Skv * D * 2 <= 2^31 - 1 bytes per head (else SPLASH_EUNSUPPORTED).
  * Asynchronous on hip_stream; allocates nothing. */
 SPLASH_API splash_status splash_decode_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Skv,

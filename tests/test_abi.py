@@ -160,7 +160,9 @@ def test_lse_merge_zero_rows_is_noop():
     (dict(dtype=splash.F32), splash.EUNSUPPORTED),
     (dict(Hq=3), splash.EINVAL),                     # head ratio
     (dict(Hq=64, Hkv=2), splash.EUNSUPPORTED),       # group of 32
-    (dict(D=96, Dv=96), splash.EUNSUPPORTED),
+    (dict(D=96, Dv=80), splash.EUNSUPPORTED),        # decode pads D == Dv only
+    (dict(D=72, Dv=72), splash.EUNSUPPORTED),        # not a multiple of 16
+    (dict(D=256, Dv=256), splash.EUNSUPPORTED),
     (dict(Skv=0), splash.EUNSUPPORTED),
     (dict(ws=0), splash.EINVAL),
     (dict(ws_bytes=16), splash.EINVAL),              # too small
@@ -226,6 +228,18 @@ def test_bwd_head_dims_validation(D, Dv, dtype, status):
     assert st == status, lib.splash_last_error()
 
 
+def test_decode_workspace_size_padded_dims():
+    """A padded head dim keeps its partials at the kernel's width: D = 96 and
+    D = 112 take the 128-column workspace, D = 48 the 64-column one."""
+    lib = splash.load_library()
+    n = {}
+    for d in (48, 64, 96, 112, 128):
+        v = ctypes.c_size_t()
+        assert lib.splash_decode_workspace_size(8, 32, 8, 32768, d, ctypes.byref(v)) == splash.OK
+        n[d] = v.value
+    assert n[96] == n[112] == n[128] and n[48] == n[64] and n[64] < n[128]
+
+
 def test_binding_checks_caller_buffers():
     """Outputs the caller passes must have the shape and dtype the kernel
     writes; the check runs before any GPU work (CPU tensors are refused too)."""
@@ -254,7 +268,7 @@ def test_static_decode_rejects_more_than_its_scratch_before_running():
     st = lib.splash_decode_static(*a.values())
     assert st == splash.EUNSUPPORTED and "scratch" in lib.splash_last_error().decode()
     for over, status in ((dict(dtype=splash.F32), splash.EUNSUPPORTED), (dict(Hq=3, Hkv=2), splash.EINVAL),
-                         (dict(q=0), splash.EINVAL), (dict(q=8), splash.EINVAL), (dict(D=96, Dv=96), splash.EUNSUPPORTED)):
+                         (dict(q=0), splash.EINVAL), (dict(q=8), splash.EINVAL), (dict(D=72, Dv=72), splash.EUNSUPPORTED)):
         b = dict(a, B=1, **over)
         assert lib.splash_decode_static(*b.values()) == status, (over, lib.splash_last_error())
     assert lib.splash_decode_static(*dict(a, B=0, q=0, k=0, v=0, out=0).values()) == splash.OK

@@ -54,6 +54,38 @@ def test_decode_parity(case):
     compare(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref[..., 0], TOL[torch.bfloat16], name)
 
 
+PADDED = [
+    # name, seed, B, Hq, Hkv, Skv, D, cap: head dims run zero-padded (D == Dv)
+    ("d96_gqa4_ragged", 160, 2, 8, 2, 5001, 96, None),
+    ("d32_mha_cap", 161, 2, 4, 4, 1000, 32, 30.0),
+    ("d80_gqa16_cap", 162, 1, 32, 2, 9000, 80, 30.0),
+    ("d48_gqa8_many_stages", 163, 2, 16, 2, 30001, 48, None),
+    ("d112_one_key", 164, 1, 2, 1, 1, 112, None),
+    ("d16_gqa2_one_range_per_unit", 165, 32, 32, 16, 3000, 16, None),
+]
+
+
+@pytest.mark.parametrize("case", PADDED, ids=[c[0] for c in PADDED])
+def test_decode_padded_head_dims(case):
+    """Decode at head dims other than 64 and 128 (the 64- or 128-column
+    kernel with zero padding), into an output carved from a larger buffer
+    whose tail must stay untouched; the default scale is D ** -0.5 of the
+    caller's D."""
+    name, seed, B, Hq, Hkv, Skv, D, cap = case
+    q, k, v = synthetic.make_qkv(seed, B, Hq, Hkv, 1, Skv, D, D)
+    dev = torch.device("cuda:0")
+    n = B * Hq * D
+    buf = torch.full((n + 1024,), 7.0, dtype=torch.bfloat16, device=dev)
+    out = buf[:n].view(B, Hq, 1, D)
+    out, lse = splash_decode(q.to(dev), k.to(dev), v.to(dev), logits_soft_cap=cap, out=out)
+    torch.cuda.synchronize()
+    assert (buf[n:] == 7.0).all()
+    allowed = np.ones((1, Skv), dtype=bool)
+    o_ref, l_ref = oatt.attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                  lambda h, rows: allowed, soft_cap=cap)
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, l_ref[..., 0], TOL[torch.bfloat16], name)
+
+
 @pytest.mark.parametrize("G,D,cap", [(4, 128, None), (16, 64, None), (8, 128, 30.0)])
 def test_decode_scores_growing_and_shrinking_along_the_cache(G, D, cap):
     """k_j carries b (j / Skv) along one direction and the query heads +-a along it, so
