@@ -484,10 +484,9 @@ splash_status validate_call(const splash_mask_info *mi, int64_t B, int64_t Hq, i
   if (mi->block_q % 128 || mi->block_kv % 128)
     return fail(SPLASH_EUNSUPPORTED, "the kernels run MaskInfo blocks that are multiples of 128 x 128");
   if (!native_dims(D, Dv)) {
-    if (!padded_ok || dtype != SPLASH_BF16)
-      return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
+    if (!padded_ok) return fail(SPLASH_EUNSUPPORTED, "head dims must satisfy D == Dv in {64, 128}");
     if (!padded_dims_ok(D, Dv))
-      return fail(SPLASH_EUNSUPPORTED, "the bf16 forward takes D and Dv that are multiples of 16 up to 128");
+      return fail(SPLASH_EUNSUPPORTED, "head dims must be D == Dv in {64, 128} or multiples of 16 up to 128");
   }
   const int64_t n_wg = B * Hq * (Sq / 128);
   if (n_wg > 0x7fffffffLL || B * Hq > 0x7fffffffLL || B * Hkv * (Skv / 128) > 0x7fffffffLL)

@@ -141,7 +141,7 @@ struct Tile {
 // into a swizzled LDS tile.  Each lane moves 16-byte chunks; 16 lanes cover
 // one 256-byte span of a row, so the global reads are fully coalesced.
 template <int D, bool IS_V>
-__device__ __forceinline__ void stage_tile(char *lds, const float *g, int tid) {
+__device__ __forceinline__ void stage_tile(char *lds, const float *g, int tid, int mrow) {
   using TL = Tile<D>;
   constexpr int kPerThread = kBK * TL::kChunks / kThreads;
   u32x4 buf[kPerThread];
@@ -149,8 +149,10 @@ __device__ __forceinline__ void stage_tile(char *lds, const float *g, int tid) {
   for (int i = 0; i < kPerThread; ++i) {
     const int idx = tid + kThreads * i;
     const int row = idx / TL::kChunks, c = idx % TL::kChunks;
-    buf[i] = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(g) +
-                                              static_cast<size_t>(row) * TL::kRowBytes + c * 16);
+    // padded head dims: rows of mrow bytes in memory, zeros past them
+    buf[i] = c * 16 < mrow ? *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(g) +
+                                                              static_cast<size_t>(row) * mrow + c * 16)
+                           : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
@@ -212,10 +214,14 @@ void splash_fwd_f32(const FwdParams p) {
   const int hkv = hq / p.group;
   const int hm = p.hm == 1 ? 0 : hq;
 
+  // Head dims in memory: D, or (padded) the caller's D and Dv, run
+  // zero-padded to D columns (zeros in Q and the tiles past them; the
+  // output's padding columns are not stored).
+  const int mk = p.padded ? p.dk : D, mv = p.padded ? p.dv : D;
   const int64_t q_row = static_cast<int64_t>(r) * kBQ + lrow;
-  const float *qg = static_cast<const float *>(p.q) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
-  const float *kg = static_cast<const float *>(p.k) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
-  const float *vg = static_cast<const float *>(p.v) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * D;
+  const float *qg = static_cast<const float *>(p.q) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * mk;
+  const float *kg = static_cast<const float *>(p.k) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * mk;
+  const float *vg = static_cast<const float *>(p.v) + (static_cast<int64_t>(b) * p.Hkv + hkv) * p.Skv * mv;
 
   // ---- Q fragment (B operand of S^T = K Q^T), resident for the whole row ----
   // The lane's half owns d in [half D/2, (half+1) D/2) and k-step ks takes one of them.
@@ -223,7 +229,8 @@ void splash_fwd_f32(const FwdParams p) {
   float qf[kQRegs];
 #pragma unroll
   for (int i = 0; i < kQRegs / 4; ++i) {
-    const float4 x = *reinterpret_cast<const float4 *>(qg + half * (D / 2) + 4 * i);
+    const int d0 = half * (D / 2) + 4 * i;
+    const float4 x = d0 < mk ? *reinterpret_cast<const float4 *>(qg + d0) : make_float4(0.f, 0.f, 0.f, 0.f);
     qf[4 * i + 0] = x.x; qf[4 * i + 1] = x.y; qf[4 * i + 2] = x.z; qf[4 * i + 3] = x.w;
   }
 
@@ -287,8 +294,8 @@ void splash_fwd_f32(const FwdParams p) {
 
       // ---- stage K and V of block kvb ----
       __syncthreads();
-      stage_tile<D, false>(lds_k, kg + static_cast<int64_t>(kvb) * kBK * D, tid);
-      stage_tile<D, true>(lds_v, vg + static_cast<int64_t>(kvb) * kBK * D, tid);
+      stage_tile<D, false>(lds_k, kg + static_cast<int64_t>(kvb) * kBK * mk, tid, mk * 4);
+      stage_tile<D, true>(lds_v, vg + static_cast<int64_t>(kvb) * kBK * mv, tid, mv * 4);
       __syncthreads();
 
       // ---- S^T = K Q^T: four 32-key tiles ----
@@ -410,7 +417,7 @@ void splash_fwd_f32(const FwdParams p) {
   const float l_tot = pair_sum(l_run);
   float inv, lse_row;
   row_finish(l_tot, mb_run == -INFINITY ? 0.f : mb_run, sink_lse2(p, hq), inv, lse_row);
-  float *og = static_cast<float *>(p.out) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * D;
+  float *og = static_cast<float *>(p.out) + ((static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row) * mv;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -419,7 +426,7 @@ void splash_fwd_f32(const FwdParams p) {
       float4 x;
       x.x = o[dt][4 * g + 0] * inv; x.y = o[dt][4 * g + 1] * inv;
       x.z = o[dt][4 * g + 2] * inv; x.w = o[dt][4 * g + 3] * inv;
-      *reinterpret_cast<float4 *>(og + col) = x;
+      if (col < mv) *reinterpret_cast<float4 *>(og + col) = x;
     }
   if (p.lse && half == 0) p.lse[(static_cast<int64_t>(b) * p.Hq + hq) * p.Sq + q_row] = lse_row;
 }

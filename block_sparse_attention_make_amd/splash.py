@@ -268,8 +268,8 @@ def splash_fwd(q, k, v, mask_info, softmax_scale=None, logits_soft_cap=None,
 
     softmax_aux: optional attention-sink logits, a float32 GPU tensor [ns]
     (shared), [Hkv, ns] (query head h uses row h // (Hq // Hkv)) or [Hq, ns].
-    Head dims: D == Dv in {64, 128}, or (bf16) any D and Dv that are multiples
-    of 16 up to 128, which run zero-padded inside the 64- or 128-column kernel.
+    Head dims: D == Dv in {64, 128}, or any D and Dv that are multiples of 16
+    up to 128, which run zero-padded inside the 64- or 128-column kernel.
     kv_splits: "auto" (the library's plan: splits only when the grid has
     fewer block rows than the GPU has workgroup slots) or 1..8 -- each block
     row's non-empty blocks divided into that many workgroups, merged by lse;

@@ -181,8 +181,8 @@ SPLASH_API void splash_mask_info_destroy(splash_mask_info *mi);
  *
  * Requirements: mi built with 128 x 128 blocks for q_len == Sq and
  * kv_len == Skv; Hm in {1, Hq}; Hq % Hkv == 0; head dims D == Dv in
- * {64, 128}, or for bf16 any D and Dv that are multiples of 16 from 16 to
- * 128 (the EasyDeL BlockSparseAttn page types head_dim and vhead_dim apart
+ * {64, 128}, or any D and Dv that are multiples of 16 from 16 to 128 (the
+ * EasyDeL BlockSparseAttn page types head_dim and vhead_dim apart
  * and, on GPU, sends only multiples of 16 to its block-sparse kernel, other
  * dims to plain attention).  Those run zero-padded inside the
  * 64-column kernel (both <= 64) or the 128-column one; rows stay packed at

@@ -55,9 +55,8 @@ def _fwd_args(info, **over):
 @pytest.mark.parametrize("over,status", [
     (dict(Sq=256), splash.EINVAL),                 # does not match the MaskInfo
     (dict(Hq=3, Hkv=2), splash.EINVAL),            # head ratio
-    (dict(D=96, Dv=96, dtype=splash.F32), splash.EUNSUPPORTED),   # float32 runs D == Dv in {64, 128}
-    (dict(D=128, Dv=64, dtype=splash.F32), splash.EUNSUPPORTED),
-    (dict(D=72, Dv=72), splash.EUNSUPPORTED),      # bf16 pads multiples of 16 only
+    (dict(D=72, Dv=72), splash.EUNSUPPORTED),      # padding takes multiples of 16 only
+    (dict(D=72, Dv=72, dtype=splash.F32), splash.EUNSUPPORTED),
     (dict(D=128, Dv=120), splash.EUNSUPPORTED),
     (dict(D=144, Dv=144), splash.EUNSUPPORTED),    # above the 128-column kernel
     (dict(D=64, Dv=256), splash.EUNSUPPORTED),

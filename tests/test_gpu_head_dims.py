@@ -1,7 +1,7 @@
-"""GPU parity for head dims other than D == Dv in {64, 128}: the bf16 forward
-runs any D and Dv that are multiples of 16 up to 128 zero-padded inside its
-64- or 128-column kernel (the EasyDeL BlockSparseAttn signature types the
-query/key head dim and the value head dim apart).
+"""GPU parity for head dims other than D == Dv in {64, 128}: the forward
+(bf16 and float32) runs any D and Dv that are multiples of 16 up to 128
+zero-padded inside its 64- or 128-column kernel (the EasyDeL BlockSparseAttn
+signature types the query/key head dim and the value head dim apart).
 
 Each case is compared element by element with the fp64 oracle (whose
 attention is pinned with Dv != D and the default scale of the true D) at the
@@ -58,6 +58,24 @@ def test_padded_head_dims_parity(case):
     assert o.shape == (B, Hq, Sq, Dv)
     o_ref, l_ref = oracle_full(q, k, v, cap=cap, **mk)
     compare(o, l, o_ref, l_ref, TOL[torch.bfloat16], name)
+
+
+F32_CASES = [
+    # name, seed, B, Hq, Hkv, Sq, Skv, D, Dv, mask kwargs, cap
+    ("f32_d96_causal_gqa", 290, 1, 4, 2, 384, 384, 96, 96, dict(kind="causal"), None),
+    ("f32_d32_dv48_local_cap", 291, 1, 2, 1, 512, 512, 32, 48, dict(kind="local", left=130, right=3), 4.0),
+    ("f32_d112_dv80_rect", 292, 1, 2, 2, 256, 640, 112, 80, dict(kind="causal"), None),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_padded_head_dims_f32(case):
+    """The float32 forward at padded dims, at its own bar (1e-5)."""
+    name, seed, B, Hq, Hkv, Sq, Skv, D, Dv, mk, cap = case
+    q, k, v = synthetic.make_qkv(seed, B, Hq, Hkv, Sq, Skv, D, Dv, dtype=torch.float32)
+    o, l, _ = run_gpu(q, k, v, cap=cap, **mk)
+    o_ref, l_ref = oracle_full(q, k, v, cap=cap, **mk)
+    compare(o, l, o_ref, l_ref, TOL[torch.float32], name)
 
 
 @pytest.mark.parametrize("D,Dv,cap", [(48, 64, None), (96, 80, 3.0)], ids=["kernel64", "kernel128_cap"])
