@@ -785,8 +785,7 @@ extern "C" SPLASH_API splash_status splash_lse_merge(const void *out_a, const fl
   auto ok_dt = [](int32_t d) { return d == SPLASH_BF16 || d == SPLASH_F32; };
   if (!ok_dt(dtype_a) || !ok_dt(dtype_b) || !ok_dt(dtype_out)) return fail(SPLASH_EINVAL, "unknown dtype");
   if (rows < 0) return fail(SPLASH_EINVAL, "rows must be >= 0");
-  if (Dv <= 0 || Dv % 8 != 0 || 64 % (Dv / 8) != 0)
-    return fail(SPLASH_EUNSUPPORTED, "Dv must be one of 8, 16, 32, 64, 128, 256, 512");
+  if (Dv <= 0 || Dv % 8 != 0 || Dv > 512) return fail(SPLASH_EUNSUPPORTED, "Dv must be a multiple of 8 up to 512");
   if (rows == 0) return SPLASH_OK;
   if (!out_a || !lse_a || !out_b || !lse_b || !out || !lse) return fail(SPLASH_EINVAL, "NULL pointer");
   if ((reinterpret_cast<uintptr_t>(out_a) | reinterpret_cast<uintptr_t>(out_b) | reinterpret_cast<uintptr_t>(out)) % 16)

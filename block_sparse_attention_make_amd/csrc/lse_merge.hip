@@ -54,15 +54,20 @@ __device__ __forceinline__ void store8(__bf16 *p, const Eight &v) {
   __builtin_nontemporal_store(pk.u, reinterpret_cast<u32x4 *>(p));
 }
 
+// A row's dv / 8 chunks go to tpr threads (dv / 8 rounded up to a power of
+// two, at most 64), so a row never straddles two wavefronts: in an in-place
+// merge every thread of a row reads its lse before any of them writes it.
 template <typename TA, typename TB, typename TO>
 __global__ void __launch_bounds__(256) lse_merge_kernel(const TA *oa, const float *la, const TB *ob,
                                                         const float *lb, TO *oo, float *lo, int64_t rows,
-                                                        int dv) {
-  const int64_t n_chunks = rows * (dv / 8);
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n_chunks;
+                                                        int dv, int tpr) {
+  const int64_t n_threads = rows * tpr;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n_threads;
        t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t e0 = t * 8;
-    const int64_t row = e0 / dv;
+    const int64_t row = t / tpr;
+    const int c = static_cast<int>(t % tpr);
+    if (c * 8 >= dv) continue;   // a padding thread of the row
+    const int64_t e0 = row * dv + c * 8;
     const float a = la[row], b = lb[row];
     const bool ha = a > -INFINITY, hb = b > -INFINITY;
     float l;
@@ -80,19 +85,21 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(const TA *oa, const floa
 #pragma unroll
     for (int i = 0; i < 8; ++i) r.x[i] = (ha ? wa * va.x[i] : 0.f) + (hb ? wb * vb.x[i] : 0.f);
     store8(oo + e0, r);
-    if (e0 % dv == 0) lo[row] = l;
+    if (c == 0) lo[row] = l;
   }
 }
 
 template <typename TA, typename TB, typename TO>
 hipError_t go(const void *oa, const float *la, const void *ob, const float *lb, void *oo, float *lo,
               int64_t rows, int dv, hipStream_t stream) {
-  const int64_t n_chunks = rows * (dv / 8);
-  const int64_t want = (n_chunks + 255) / 256;
+  int tpr = 1;
+  while (tpr * 8 < dv) tpr *= 2;   // threads per row, a power of two (dv <= 512: at most 64)
+  const int64_t n_threads = rows * tpr;
+  const int64_t want = (n_threads + 255) / 256;
   const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
   hipLaunchKernelGGL((lse_merge_kernel<TA, TB, TO>), dim3(grid), dim3(256), 0, stream,
                      static_cast<const TA *>(oa), la, static_cast<const TB *>(ob), lb, static_cast<TO *>(oo), lo,
-                     rows, dv);
+                     rows, dv, tpr);
   return hipGetLastError();
 }
 

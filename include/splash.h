@@ -339,8 +339,8 @@ SPLASH_API splash_status splash_make_mask_info_kv_slice(const splash_mask_desc *
  * from rounding at every step), 16-byte aligned.  lse_a, lse_b, lse: DEVICE
  * float32 [rows].  out may be out_a (or out_b) and lse may be lse_a (or
  * lse_b) -- an in-place accumulation -- when the dtypes agree; any other
- * overlap is not allowed.  Dv in {8, 16, 32, 64, 128, 256, 512}
- * (else SPLASH_EUNSUPPORTED).  Asynchronous on hip_stream; allocates
+ * overlap is not allowed.  Dv a multiple of 8 up to 512 (else
+ * SPLASH_EUNSUPPORTED).  Asynchronous on hip_stream; allocates
  * nothing.  Errors as for splash_fwd. */
 SPLASH_API splash_status splash_lse_merge(const void *out_a, const float *lse_a, int32_t dtype_a,
                                           const void *out_b, const float *lse_b, int32_t dtype_b,

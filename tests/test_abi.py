@@ -135,7 +135,8 @@ def test_fwd_sinks_empty_batch_is_noop():
 @pytest.mark.parametrize("over,status", [
     (dict(dta=5), splash.EINVAL),
     (dict(rows=-1), splash.EINVAL),
-    (dict(dv=96), splash.EUNSUPPORTED),
+    (dict(dv=100), splash.EUNSUPPORTED),           # not a multiple of 8
+    (dict(dv=520), splash.EUNSUPPORTED),
     (dict(dv=1024), splash.EUNSUPPORTED),
     (dict(oa=0), splash.EINVAL),
     (dict(oa=8), splash.EINVAL),

@@ -92,6 +92,9 @@ def test_sharded_forward_equals_full_attention(kind, mk, sizes, cap):
     (torch.float32, torch.bfloat16, torch.bfloat16, 64),
     (torch.bfloat16, torch.float32, torch.bfloat16, 256),
     (torch.float32, torch.float32, torch.float32, 8),
+    (torch.bfloat16, torch.bfloat16, torch.float32, 96),     # 12 chunks a row: 16 threads, 4 idle
+    (torch.float32, torch.bfloat16, torch.bfloat16, 40),
+    (torch.float32, torch.float32, torch.float32, 512),
 ])
 def test_merge_kernel_parity(dta, dtb, dto, dv):
     """Random parts with rows empty in one part, in the other, in both; the
@@ -116,9 +119,12 @@ def test_merge_kernel_parity(dta, dtb, dto, dv):
     compare(o.float().cpu().numpy(), l.cpu().numpy(), ref_o, ref_l, tol, "merge")
 
 
-def test_merge_in_place():
+@pytest.mark.parametrize("dv", [128, 96, 24])
+def test_merge_in_place(dv):
+    """Out and lse written over part a; a row's threads must all read its
+    lse before any writes it (also where Dv / 8 is not a power of two)."""
     rng = np.random.default_rng(95)
-    rows, dv = 1000, 128
+    rows = 1000
     a = torch.from_numpy(rng.standard_normal((rows, dv)).astype(np.float32)).to(DEV)
     b = torch.from_numpy(rng.standard_normal((rows, dv)).astype(np.float32)).to(DEV)
     la = torch.from_numpy(rng.standard_normal(rows).astype(np.float32)).to(DEV)
@@ -127,4 +133,23 @@ def test_merge_in_place():
     o, l = lse_merge(a, la, b, lb, out=a, lse=la)
     torch.cuda.synchronize()
     assert o.data_ptr() == a.data_ptr() and l.data_ptr() == la.data_ptr()
-    compare(a.cpu().numpy(), la.cpu().numpy(), ref_o, ref_l, 1e-5, "merge_in_place")
+    compare(a.cpu().numpy(), la.cpu().numpy(), ref_o, ref_l, 1e-5, f"merge_in_place dv={dv}")
+
+
+@pytest.mark.parametrize("D,Dv", [(96, 80), (32, 48)])
+def test_sharded_forward_padded_head_dims(D, Dv):
+    """The key/value-sharded path at head dims run zero-padded: each shard's
+    forward, then the merge over rows of Dv elements."""
+    sizes = [384, 256, 384]
+    S = sum(sizes)
+    q, k, v = synthetic.make_qkv(96 + D, 1, 4, 2, S, S, D, Dv)
+    mis, ks, vs = [], [], []
+    for k0, kn in _shards(S, sizes):
+        mis.append(make_mask_info("causal", S, S, kv_slice=(k0, kn)))
+        ks.append(k[:, :, k0:k0 + kn].contiguous().to(DEV))
+        vs.append(v[:, :, k0:k0 + kn].contiguous().to(DEV))
+    o, l = splash_fwd_kv_sharded(q.to(DEV), ks, vs, mis)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 4, S, Dv)
+    o_ref, l_ref = oracle_full(q, k, v, "causal")
+    compare(o.float().cpu().numpy(), l.cpu().numpy(), o_ref, l_ref, TOL[torch.bfloat16], f"sharded D={D} Dv={Dv}")
