@@ -90,6 +90,9 @@ WORKLOADS["causal_d96_8k"] = Workload("causal_d96_8k", 1, 16, 16, 8192, 8192, 96
 DECODE_WORKLOADS = {
     "decode_gqa_32k": Workload("decode_gqa_32k", 8, 32, 8, 1, 32768, 128, 128, "bf16",
                                MaskSpec("dense"), seed=6),
+    # the same cache at a head dim the decode runs zero-padded (96 of 128 columns)
+    "decode_gqa_32k_d96": Workload("decode_gqa_32k_d96", 8, 32, 8, 1, 32768, 96, 96, "bf16",
+                                   MaskSpec("dense"), seed=10),
 }
 
 

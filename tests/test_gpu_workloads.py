@@ -77,12 +77,13 @@ def test_device_mask_info_bit_exact(name):
         assert d.dtype == r.dtype and d.shape == r.shape and d.tobytes() == r.tobytes(), nm
 
 
-def test_decode_full_size_whole_output():
-    """decode_gqa_32k (B = 8, Hq = 32, Hkv = 8, 32,768 cached keys, D = 128), called as the
-    decode benchmark calls it: every (b, query head) row against the fp64 oracle with every
-    key allowed."""
+@pytest.mark.parametrize("name", sorted(synthetic.DECODE_WORKLOADS))
+def test_decode_full_size_whole_output(name):
+    """decode_gqa_32k (B = 8, Hq = 32, Hkv = 8, 32,768 cached keys, D = 128, and the same at
+    D = 96), called as the decode benchmark calls it: every (b, query head) row against the
+    fp64 oracle with every key allowed."""
     from block_sparse_attention_make_amd import splash_decode
-    w = synthetic.DECODE_WORKLOADS["decode_gqa_32k"]
+    w = synthetic.DECODE_WORKLOADS[name]
     q, k, v = synthetic.make_qkv(w.seed, w.B, w.Hq, w.Hkv, 1, w.Skv, w.D, w.Dv)
     dev = torch.device("cuda:0")
     out, lse = splash_decode(q.to(dev), k.to(dev), v.to(dev))
