@@ -1,7 +1,8 @@
 """The forward captured into a HIP graph: every replay, with the program's own
 eager launches and synchronisations between replays, gives the eager result
-bit for bit.  Covers a causal GQA forward (two heads per workgroup) and a
-dense forward with split keys (forward kernel plus merge in one graph)."""
+bit for bit.  Covers a causal GQA forward (two heads per workgroup), a
+dense forward with split keys (forward kernel plus merge in one graph) and
+padded head dims with both launch shapes."""
 import pytest
 import torch
 
@@ -23,6 +24,10 @@ def _case(name):
         q, k, v = synthetic.make_qkv(601, 1, 8, 2, 1024, 1024, 128, 128)
         mi = make_mask_info("causal", 1024, 1024)
         return q, k, v, mi, dict(heads_per_workgroup=2, kv_splits=1)
+    if name == "padded_pairs_splits":   # head dims run zero-padded: D = 96, Dv = 80
+        q, k, v = synthetic.make_qkv(604, 1, 8, 2, 1024, 1024, 96, 80)
+        mi = make_mask_info("causal", 1024, 1024)
+        return q, k, v, mi, dict(heads_per_workgroup=2, kv_splits=2)
     rng = __import__("numpy").random.default_rng(602)
     q, k, v = synthetic.make_qkv(603, 1, 4, 4, 768, 768, 128, 128)
     dense = synthetic.random_dense_mask(rng, 1, 768, 768, 0.2)
@@ -30,15 +35,16 @@ def _case(name):
     return q, k, v, mi, dict(kv_splits=3)
 
 
-@pytest.mark.parametrize("name", ["causal_pairs", "dense_splits"])
+@pytest.mark.parametrize("name", ["causal_pairs", "dense_splits", "padded_pairs_splits"])
 def test_graph_replays_match_eager(name):
     q, k, v, mi, kw = _case(name)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    out = torch.empty(q.shape, dtype=q.dtype, device=DEV)
+    Dv = v.shape[3]
+    out = torch.empty(q.shape[:3] + (Dv,), dtype=q.dtype, device=DEV)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
     ws = None
     if kw["kv_splits"] > 1:
-        ws = torch.empty(kw["kv_splits"] * q.shape[0] * q.shape[1] * q.shape[2] * (2 * 128 + 4) // 4,
+        ws = torch.empty(kw["kv_splits"] * q.shape[0] * q.shape[1] * q.shape[2] * (2 * Dv + 4) // 4,
                          dtype=torch.float32, device=DEV)
     # eager reference (also uploads the MaskInfo and its split table: no
     # allocation happens inside the capture)
